@@ -1,0 +1,129 @@
+"""GEMM oracle: D = A·B (+C) in float64 (test infrastructure).
+
+Definitions followed, all from [SYNC-GEMM]:
+
+* 一 (positioning): the primitive computes D = alpha·A·B + beta·C.
+* 二 (What it accepts): M % 16 == 0, N % 8 == 0, K % 8 == 0; A and B are both
+  float16 or both bfloat16; C and D are float32; alpha must be 1.0 and beta is
+  0.0 (D = A·B) or 1.0 (D = A·B + C).  transpose_A / transpose_B only describe
+  the stored orientation: A is stored (M, K) or (K, M), B is stored (K, N) or
+  (N, K), and both are normalised to A[M, K], B[K, N] before the product;
+  C and D are always (M, N).
+* 三 (demo): with beta = 0 the value of C does not matter.
+
+Readings where the page is silent (each also listed in the design notes):
+
+* Zero extents satisfy the divisibility rules; an empty product is zero, so
+  K = 0 gives D = beta·C and M = 0 or N = 0 gives an empty D.
+* With beta = 0 the oracle never reads C, so NaN or garbage in C cannot reach D.
+* The error bound is |D - D_ref| <= 1e-4 · sum_k |A_ik B_kj| + 1e-6 per element,
+  with D_ref the float64 result; the pages only say "within fp16 tolerance".
+
+Pins (tests/test_oracle_gemm.py): exact rational brute force with
+fractions.Fraction on small shapes (the 16x8x16 atom included), beta = 0 vs 1
+semantics with NaN-filled C, transposition equivalence over all four
+(transA, transB) pairs and both formats, identity and zero matrices, and the
+acceptance table against the page's listed rejections.
+"""
+
+import numpy as np
+
+from .numerics import decode
+
+FORMATS = ("f16", "bf16")
+
+
+def accepts(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+    """Acceptance table of [SYNC-GEMM] 二.  Returns (ok, category).
+
+    category is one of None, "shape", "dtype", "alpha", "beta"; checks run in
+    that order so a call with several faults reports the first one.
+    """
+    if min(M, N, K) < 0 or M % 16 or N % 8 or K % 8:
+        return False, "shape"
+    if a_dtype not in FORMATS or b_dtype != a_dtype or c_dtype != "f32" or d_dtype != "f32":
+        return False, "dtype"
+    if alpha != 1.0:
+        return False, "alpha"
+    if beta not in (0.0, 1.0):
+        return False, "beta"
+    return True, None
+
+
+def logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, dtype):
+    """Decode A and B and normalise them to A[M, K], B[K, N] (float64)."""
+    a = decode(a_bits, dtype)
+    b = decode(b_bits, dtype)
+    a = a.reshape((K, M) if trans_a else (M, K))
+    b = b.reshape((N, K) if trans_b else (K, N))
+    a_l = a.T if trans_a else a
+    b_l = b.T if trans_b else b
+    return a_l, b_l
+
+
+def gemm_ref(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, dtype):
+    """Full float64 D_ref = A·B (+ C when beta == 1).  C is not read when beta == 0."""
+    ok, why = accepts(M, N, K, dtype, dtype, beta=beta)
+    if not ok:
+        raise ValueError(f"oracle: call rejected ({why})")
+    a_l, b_l = logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, dtype)
+    d = np.matmul(a_l, b_l) if K else np.zeros((M, N))
+    if beta == 1.0:
+        d = d + np.asarray(c, dtype=np.float32).reshape(M, N).astype(np.float64)
+    return d
+
+
+def abs_bound(a_bits, b_bits, M, N, K, trans_a, trans_b, dtype):
+    """sum_k |A_ik · B_kj| for every (i, j), float64."""
+    a_l, b_l = logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, dtype)
+    return np.matmul(np.abs(a_l), np.abs(b_l)) if K else np.zeros((M, N))
+
+
+def _row_of_a(a_bits, M, K, trans_a, rows):
+    a = a_bits.reshape((K, M) if trans_a else (M, K))
+    return a[:, rows].T if trans_a else a[rows, :]
+
+
+def _col_of_b(b_bits, N, K, trans_b, cols):
+    b = b_bits.reshape((N, K) if trans_b else (K, N))
+    return b[cols, :] if trans_b else b[:, cols].T
+
+
+def gemm_ref_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, dtype, rows, cols, chunk=512):
+    """D_ref and the bound at sampled outputs (rows[s], cols[s]), one float64 dot each."""
+    ok, why = accepts(M, N, K, dtype, dtype, beta=beta)
+    if not ok:
+        raise ValueError(f"oracle: call rejected ({why})")
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    d = np.empty(rows.size)
+    bound = np.empty(rows.size)
+    for s0 in range(0, rows.size, chunk):
+        r = rows[s0:s0 + chunk]
+        q = cols[s0:s0 + chunk]
+        a = decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, r)), dtype)
+        b = decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, q)), dtype)
+        prod = a * b
+        d[s0:s0 + chunk] = prod.sum(axis=1)
+        bound[s0:s0 + chunk] = np.abs(prod).sum(axis=1)
+    if beta == 1.0:
+        cc = np.asarray(c, dtype=np.float32).reshape(M, N)
+        d = d + cc[rows, cols].astype(np.float64)
+    return d, bound
+
+
+def tolerance(bound):
+    """Allowed |D - D_ref| per element: 1e-4 · sum_k |A_ik B_kj| + 1e-6."""
+    return 1e-4 * np.asarray(bound, dtype=np.float64) + 1e-6
+
+
+def check(d_gpu, d_ref, bound):
+    """Returns (ok, worst_ratio) where ratio = |D - D_ref| / tolerance; D must be finite."""
+    d_gpu = np.asarray(d_gpu, dtype=np.float64)
+    if d_gpu.size == 0:
+        return True, 0.0
+    if not np.all(np.isfinite(d_gpu)):
+        return False, float("inf")
+    ratio = np.abs(d_gpu - d_ref) / tolerance(bound)
+    worst = float(ratio.max())
+    return worst <= 1.0, worst

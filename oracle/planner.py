@@ -1,0 +1,181 @@
+"""vec_auto copy partition planner (oracle; test infrastructure).
+
+Restates [VEC-AUTO]:
+
+* 接受什么输入 (the gate, _divides_thread_cnt): the thread count must be positive
+  and must divide the element count of the region; otherwise the copy is
+  rejected rather than masked by a slow scalar path.
+* 算法核心 step 1: the region is split into a three-level iteration
+  [outer, threads, vec]; the global side fixes the canonical (stride-descending)
+  order, the vec iteration is its contiguous innermost part and each thread owns
+  consecutive fused-index slots.  The generated IR of the demo shows the fused
+  index of round f, thread t as f·(threads·vec) + t·vec (生成的 TIRx IR).
+* step 2: vector widths of 128, 64, 32, 16 and 8 bits are tried widest first; a
+  width is taken when (a) the contiguous tail divides by it and (b) every
+  non-vector stride on both sides, the thread iteration included, and both base
+  offsets are multiples of it.
+* 输入如何改变算法 / swizzled shared 布局: with a swizzled shared side the vector
+  may not leave one 16-byte swizzle chunk.
+* 对齐约束的兜底: misaligned strides or a region starting at an odd column narrow
+  the width, down to one element.
+
+Readings (the page is silent; each also listed in the design notes):
+
+* widths narrower than the element, or not a multiple of it, are skipped;
+* the width must also divide elements/threads, so that elements = outer·threads·vec;
+* a vector is contiguous on a side when that side stores the fused order's inner
+  dimension contiguously and the vector does not cross a row, or when the whole
+  region is packed on that side; a side stored in the other order only admits
+  one-element vectors;
+* "misaligned" is measured in elements from the side's base: base offset (pointer
+  address / element size plus region offset) and leading dimension.
+
+Pinned by tests/test_oracle_planner.py: the page's worked example (32 threads,
+32x32 float32 -> vec 4 = 128 bits, outer 8, fused index f·128 + t·4), the
+per-dtype rounds of the same tile, the 64-elements-on-1024-threads rejection,
+and the two narrowing examples (fp16 row stride 20; a region starting at
+column 3); plus brute force that every planned chunk is contiguous and aligned
+on both sides.
+"""
+
+from .layout import ROW, COL, XOR, CHUNK_BYTES, xor_defined
+
+WIDTHS_BITS = (128, 64, 32, 16, 8)
+
+
+class Plan:
+    def __init__(self, outer, threads, vec, vec_bits):
+        self.outer, self.threads, self.vec, self.vec_bits = outer, threads, vec, vec_bits
+
+    def __repr__(self):
+        return f"Plan(outer={self.outer}, threads={self.threads}, vec={self.vec}, bits={self.vec_bits})"
+
+    def __eq__(self, other):
+        return isinstance(other, Plan) and (self.outer, self.threads, self.vec, self.vec_bits) == (
+            other.outer, other.threads, other.vec, other.vec_bits)
+
+
+class Reject:
+    """category is "threads" (count <= 0 or not dividing the elements) or "layout"."""
+
+    def __init__(self, category, reason):
+        self.category, self.reason = category, reason
+
+    def __repr__(self):
+        return f"Reject({self.category!r}: {self.reason})"
+
+
+def fused_order(drive):
+    """Canonical order of the driving (global) side: "row" or "col"."""
+    return COL if drive.kind == COL else ROW
+
+
+def _strides(side, rows, cols):
+    """(row stride, column stride) of a side, in elements."""
+    ld = side.eff_ld(rows, cols)
+    if side.kind == COL:
+        return 1, ld
+    return ld, 1
+
+
+def _side_ok(side, rows, cols, order, v, elem_bytes):
+    """Is every v-element chunk of the fused order contiguous and v-aligned on this side?
+
+    A chunk is the run of fused positions [x, x+v) with x a multiple of v; the
+    fused position x is (outer, inner) = divmod(x, inner extent) in `order`.
+    """
+    if side.kind == XOR:
+        if side.ld not in (0, cols) or not xor_defined(cols, elem_bytes):
+            return False
+        if v * elem_bytes > CHUNK_BYTES:
+            return False
+    if v == 1:
+        return True
+    s_r, s_c = _strides(side, rows, cols)
+    inner, outer_ext = (cols, rows) if order == ROW else (rows, cols)
+    s_in, s_out = (s_c, s_r) if order == ROW else (s_r, s_c)
+    if side.kind == XOR and order != ROW:
+        return False
+    if inner % v == 0:
+        # chunks stay inside one row of the fused order
+        if s_in != 1:
+            return False
+        if outer_ext > 1 and s_out % v:
+            return False
+    else:
+        # chunks cross rows: the region must be one contiguous run on this side
+        if side.kind == XOR:
+            return False
+        if inner > 1 and s_in != 1:
+            return False
+        if s_out != inner:
+            return False
+    return side.base % v == 0
+
+
+def plan_region(rows, cols, elem_bits, threads, drive, other):
+    """Partition one rows x cols region copied between `drive` (global side) and `other`."""
+    if threads <= 0:
+        return Reject("threads", "thread count must be positive")
+    n = rows * cols
+    if n % threads:
+        return Reject("threads", f"{n} elements do not divide over {threads} threads")
+    eb = elem_bits // 8
+    for side in (drive, other):
+        if side.kind == XOR and not xor_defined(cols, eb):
+            return Reject("layout", "xor layout needs rows of a power-of-two count of 16-byte chunks")
+    order = fused_order(drive)
+    if n == 0:
+        return Plan(0, threads, 1, elem_bits)
+    for bits in WIDTHS_BITS:
+        if bits < elem_bits or bits % elem_bits:
+            continue
+        v = bits // elem_bits
+        if (n // threads) % v:
+            continue
+        if all(_side_ok(s, rows, cols, order, v, eb) for s in (drive, other)):
+            return Plan(n // (threads * v), threads, v, bits)
+    return Reject("layout", "no vector width keeps every transfer contiguous")
+
+
+def chunk_coords(plan, rows, cols, order, f, t):
+    """Logical (r, c) pairs of the elements thread t moves in round f (fused order)."""
+    inner = cols if order == ROW else rows
+    x0 = f * plan.threads * plan.vec + t * plan.vec
+    out = []
+    for j in range(plan.vec):
+        o, i = divmod(x0 + j, inner)
+        out.append((o, i) if order == ROW else (i, o))
+    return out
+
+
+def plan_tiles(rows, cols, tile_rows, tile_cols, elem_bits, threads, tensor_side, lds_side):
+    """Plan of a rows x cols tensor copied tile by tile: every tile must accept the vector.
+
+    Brute force over every tile: the tensor side of tile (i, j) is the tensor
+    layout with its base moved to (i·tile_rows, j·tile_cols).  The chosen width
+    is the widest that every tile accepts (acceptance is closed under halving,
+    so this is the minimum of the per-tile widths).
+    """
+    from .layout import Layout
+    if threads <= 0:
+        return Reject("threads", "thread count must be positive")
+    if rows == 0 or cols == 0:
+        return Plan(0, threads, 1, elem_bits)
+    if tile_rows <= 0 or tile_cols <= 0 or rows % tile_rows or cols % tile_cols:
+        return Reject("layout", "tensor is not a whole number of tiles")
+    full_ld = tensor_side.ld or (rows if tensor_side.kind == COL else cols)
+    best = None
+    for i in range(rows // tile_rows):
+        for j in range(cols // tile_cols):
+            r0, c0 = i * tile_rows, j * tile_cols
+            if tensor_side.kind == ROW:
+                view = Layout(ROW, full_ld, tensor_side.base + r0 * full_ld + c0)
+            else:
+                view = Layout(COL, full_ld, tensor_side.base + c0 * full_ld + r0)
+            p = plan_region(tile_rows, tile_cols, elem_bits, threads, view, lds_side)
+            if isinstance(p, Reject):
+                return p
+            if best is None or p.vec < best.vec:
+                best = p
+    return best

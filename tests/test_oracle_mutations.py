@@ -1,0 +1,172 @@
+"""Planted mistakes in copies of the oracle must be caught by the pins.
+
+Each mutant is a plausible slip (a transposed operand, a wrong sign, a dropped
+term, an ignored flag or alignment rule).  The test passes when at least one pin
+check fails on the mutant; the real oracle is never modified.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import gemm as G
+from oracle import layout as L
+from oracle import planner as P
+from oracle.numerics import decode
+from tests import pins
+
+
+def _mut_gemm(kind):
+    def fn(a_bits, b_bits, c, M, N, K, ta, tb, beta, dtype):
+        a = decode(a_bits, dtype).reshape((K, M) if ta else (M, K))
+        b = decode(b_bits, dtype).reshape((N, K) if tb else (K, N))
+        a_l = a.T if ta else a
+        b_l = b.T if tb else b
+        if kind == "ignore_trans_a":
+            a_l = decode(a_bits, dtype).reshape(M, K)
+        if kind == "ignore_trans_b":
+            b_l = decode(b_bits, dtype).reshape(K, N)
+        if kind == "abs_a":
+            a_l = np.abs(a_l)
+        if kind == "drop_last_k" and K:
+            a_l = a_l[:, :-1]
+            b_l = b_l[:-1, :]
+        d = a_l @ b_l if a_l.shape[1] else np.zeros((M, N))
+        if kind == "beta_ignored":
+            return d
+        if kind == "subtract_c" and beta == 1.0:
+            return d - np.asarray(c, np.float32).reshape(M, N).astype(np.float64)
+        if kind == "read_c_when_beta0" and c is not None:
+            return d + beta * np.asarray(c, np.float32).reshape(M, N).astype(np.float64)
+        if kind == "c_shifted" and beta == 1.0:
+            return d + np.roll(np.asarray(c, np.float32).reshape(M, N), 1, axis=0).astype(np.float64)
+        if beta == 1.0:
+            d = d + np.asarray(c, np.float32).reshape(M, N).astype(np.float64)
+        return d
+    return fn
+
+
+def _caught(check, fn):
+    try:
+        check(fn)
+    except Exception:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("kind", ["ignore_trans_a", "ignore_trans_b", "abs_a", "drop_last_k",
+                                  "beta_ignored", "subtract_c", "read_c_when_beta0", "c_shifted"])
+def test_gemm_mutant_is_caught(kind):
+    fn = _mut_gemm(kind)
+    shapes = pins.SMALL_SHAPES[:4]
+    assert (_caught(lambda f: pins.pin_gemm_brute_force(f, shapes), fn)
+            or any(_caught(p, fn) for p in pins.GEMM_PINS[1:]))
+
+
+def test_acceptance_mutants_are_caught():
+    from tests.test_oracle_gemm import test_acceptance_table as t
+    import inspect
+    params = [m for m in t.pytestmark if m.name == "parametrize"][0].args[1]
+
+    def run(accepts_fn):
+        for args, cat in params:
+            ok, why = accepts_fn(**args)
+            assert ok == (cat is None) and why == cat
+
+    def no_alpha(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+        return G.accepts(M, N, K, a_dtype, b_dtype, c_dtype, d_dtype, 1.0, beta)
+
+    def loose_k(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+        return G.accepts(M, N, K - K % 8, a_dtype, b_dtype, c_dtype, d_dtype, alpha, beta)
+
+    def mixed_ok(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+        return G.accepts(M, N, K, a_dtype, a_dtype, c_dtype, d_dtype, alpha, beta)
+
+    for m in (no_alpha, loose_k, mixed_ok):
+        assert _caught(run, m)
+    assert inspect.isfunction(t)
+
+
+def _planner_pins():
+    from tests import test_oracle_planner as T
+    checks = [T.test_worked_example_32x32_f32_one_warp, T.test_dtype_rounds_table,
+              T.test_rejections_and_narrowing, T.test_swizzled_side_caps_vector_at_one_chunk,
+              T.test_tiled_plan_is_min_over_tiles]
+    cases = list(T._cases())
+
+    def brute(_):
+        for case in cases:
+            T.test_plan_is_valid_and_widest(case)
+    return [lambda _, c=c: c() for c in checks] + [brute]
+
+
+@pytest.mark.parametrize("kind", ["no_base", "no_ld", "narrow_first", "no_thread_check",
+                                  "no_vec_divides"])
+def test_planner_mutant_is_caught(kind, monkeypatch):
+    orig_side_ok = P._side_ok
+    orig_plan = P.plan_region
+
+    def side_ok(side, rows, cols, order, v, eb):
+        if kind == "no_base":
+            side = L.Layout(side.kind, side.ld, 0)
+        if kind == "no_ld" and side.kind != L.XOR:
+            ld = side.eff_ld(rows, cols)
+            side = L.Layout(side.kind, ld - ld % v if ld % v and ld > v else ld, side.base)
+        return orig_side_ok(side, rows, cols, order, v, eb)
+
+    def plan_region(rows, cols, elem_bits, threads, drive, other):
+        if kind == "no_thread_check":
+            if threads <= 0:
+                threads = 1
+            if (rows * cols) % threads:
+                return P.Plan((rows * cols) // threads, threads, 1, elem_bits)
+        if kind == "narrow_first":
+            monkeypatch.setattr(P, "WIDTHS_BITS", (8, 16, 32, 64, 128))
+        if kind == "no_vec_divides":
+            n = rows * cols
+            for bits in (128, 64, 32, 16, 8):
+                if bits < elem_bits:
+                    continue
+                v = bits // elem_bits
+                if all(orig_side_ok(s, rows, cols, P.fused_order(drive), v, elem_bits // 8) for s in (drive, other)) \
+                        and threads > 0 and n % threads == 0:
+                    return P.Plan(max(1, n // (threads * v)), threads, v, bits)
+        return orig_plan(rows, cols, elem_bits, threads, drive, other)
+
+    monkeypatch.setattr(P, "_side_ok", side_ok)
+    monkeypatch.setattr(P, "plan_region", plan_region)
+    import tests.test_oracle_planner as T
+    monkeypatch.setattr(T, "plan_region", plan_region)
+    assert any(_caught(p, None) for p in _planner_pins())
+
+
+@pytest.mark.parametrize("kind", ["period4", "col_as_row", "xor_whole_row"])
+def test_layout_mutant_is_caught(kind, monkeypatch):
+    import tests.test_oracle_copy as T
+    orig_offsets = L.offsets
+
+    def xor_offset(r, c, cols, eb):
+        ce = 16 // eb
+        chunks = cols // ce
+        r = np.asarray(r, dtype=np.int64)
+        c = np.asarray(c, dtype=np.int64)
+        if kind == "period4":
+            return r * cols + ((c // ce) ^ (r % min(4, chunks))) * ce + c % ce
+        if kind == "xor_whole_row":
+            return r * cols + (c ^ (r % min(8, cols)))
+        return r * cols + ((c // ce) ^ (r % min(8, chunks))) * ce + c % ce
+
+    def offsets(layout, rows, cols, eb):
+        if kind == "col_as_row" and layout.kind == L.COL:
+            layout = L.Layout(L.ROW, 0, layout.base)
+        return orig_offsets(layout, rows, cols, eb)
+
+    monkeypatch.setattr(L, "xor_offset", xor_offset)
+    monkeypatch.setattr(L, "offsets", offsets)
+    monkeypatch.setattr(T, "offsets", offsets)
+    monkeypatch.setattr(T, "xor_offset", xor_offset)
+    import oracle.copy as C
+    monkeypatch.setattr(C, "offsets", offsets)
+    checks = [T.test_xor_matches_byte_address_form_for_128_byte_rows, T.test_copy_row_to_col_is_transpose]
+    checks += [lambda a=a: T.test_xor_layout_is_a_bijection_with_whole_chunks(*a) for a in T.TILES]
+    checks += [lambda a=a: T.test_xor_layout_is_an_involution(*a) for a in T.TILES]
+    assert any(_caught(lambda _: c(), None) for c in checks)
