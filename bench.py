@@ -1,0 +1,228 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * tile GEMM  D = A·B, M = N = K = 8192, bf16 A/B normal(0,1)/sqrt(K), fp32 D, beta = 0
+  * streaming tile copy of 2^28 fp16 values viewed as 16384 x 16384, 128x64 tiles staged
+    through XOR-swizzled LDS by 256-thread workgroups, out of place.
+Inputs are resident in HBM before the timed region.  Each kernel is bracketed by HIP
+events on the stream it is launched on (torch's current stream, which the binding
+passes to the library); `value` is the GEMM's TFLOP/s over the timed steps, the copy's
+GB/s is reported beside it.  The fp16 transA beta=1 variant of the same GEMM is timed
+after the steps and reported as an extra field.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2516.6   # dense fp16/bf16: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0       # HBM3E
+M = N = K = 8192
+ROWS = COLS = 16384
+METRIC = "GEMM TFLOP/s + % MFMA peak (bf16 8192³); tile-copy GB/s + % HBM peak"
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tile_level_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(kernel)
+    if not rec or rec.get("sources_sha") != kernel_sources_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(gemm_inputs, copy_src, budget_s=12.0):
+    """Time the oracle as it stands on bounded samples of the same workload (host cores)."""
+    from oracle import gemm as og
+    from oracle.copy import copy_ref
+    from oracle.layout import Layout
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = os.cpu_count() or 1
+    a_bits, b_bits, _ = gemm_inputs
+    # GEMM: oracle.gemm.gemm_ref (float64 matmul) on a slab of rows of A
+    rows = 64
+    while True:
+        t0 = time.perf_counter()
+        og.gemm_ref(a_bits[:rows], b_bits, None, rows, N, K, False, False, 0.0, "bf16")
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or rows >= M:
+            break
+        rows = min(M, rows * max(2, int(budget_s / 4 / max(dt, 1e-3))))
+        rows -= rows % 16
+    gemm_tflops = 2.0 * rows * N * K / dt / 1e12
+    # copy: oracle.copy.copy_ref on a slab of rows of the 16384 x 16384 f16 tensor
+    slab = 1024
+    src = copy_src[:slab * COLS]
+    t0 = time.perf_counter()
+    copy_ref(src, np.zeros_like(src), slab, COLS, Layout("row"), Layout("row"))
+    cdt = time.perf_counter() - t0
+    copy_gbs = 2.0 * src.nbytes / cdt / 1e9
+    return {
+        "value": round(gemm_tflops, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": (f"gemm: oracle.gemm.gemm_ref (float64 matmul after exact bf16 decode) on rows "
+                   f"0..{rows} of the 8192^3 bf16 GEMM ({dt:.2f} s); copy: oracle.copy.copy_ref on "
+                   f"{slab} of 16384 rows ({cdt:.2f} s, single thread) = {copy_gbs:.3f} GB/s"),
+        "copy_value": round(copy_gbs, 4), "copy_unit": "GB/s", "copy_cores": 1,
+        "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the tile GEMM and tile copy "
+              "run on a single MI355X and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import tile_level_gemm_amd as tg
+
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    gin = synth.gemm8k_bf16_inputs()
+    A, B = up(gin[0]), up(gin[1])
+    D = torch.empty((M, N), dtype=torch.float32, device=dev)
+    copy_src_bits = synth.stream_input(ROWS, COLS)
+    S = up(copy_src_bits)
+    T = torch.empty_like(S)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        tg.tile_gemm(A, B, None, D, M, N, K, 0, 0, 0.0, tg.TG_BF16)
+        if ev is not None:
+            ev[1].record()
+        tg.tile_copy(S, T, (ROWS, COLS), tg.TG_F16)
+        if ev is not None:
+            ev[2].record()
+
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print("bench: timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gemm_ms = [e[0].elapsed_time(e[1]) for e in events]
+    copy_ms = [e[1].elapsed_time(e[2]) for e in events]
+    g_avg = float(np.mean(gemm_ms))
+    c_avg = float(np.mean(copy_ms))
+    flops = 2.0 * M * N * K
+    tflops = flops / (g_avg * 1e-3) / 1e12
+    copy_bytes = 2.0 * ROWS * COLS * 2
+    gbs = copy_bytes / (c_avg * 1e-3) / 1e9
+
+    # parity spot check of the timed outputs (sampled GEMM outputs, full copy identity)
+    from oracle import gemm as og
+    rows, cols = synth.sample_points(M, N, 53, count=256)
+    ref, bound = og.gemm_ref_at(gin[0], gin[1], None, M, N, K, False, False, 0.0, "bf16", rows, cols)
+    g_ok, g_worst = og.check(D.cpu().numpy()[rows, cols], ref, bound)
+    c_ok = bool(torch.equal(S, T))
+
+    # fp16 transA beta=1 variant of the same GEMM
+    hin = synth.gemm8k_f16_inputs()
+    Ah, Bh = up(hin[0]), up(hin[1])
+    Ch = torch.from_numpy(hin[2]).to(dev)
+    for _ in range(2):
+        tg.tile_gemm(Ah, Bh, Ch, D, M, N, K, 1, 0, 1.0, tg.TG_F16)
+    hev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    hev[0].record()
+    reps = max(3, args.steps // 2)
+    for _ in range(reps):
+        tg.tile_gemm(Ah, Bh, Ch, D, M, N, K, 1, 0, 1.0, tg.TG_F16)
+    hev[1].record()
+    torch.cuda.synchronize()
+    h_ms = hev[0].elapsed_time(hev[1]) / reps
+
+    base = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        base = cpu_baseline(gin, copy_src_bits)
+
+    gemm_traffic = traffic_for("gemm_tiled_256x256_bf16_nn")
+    copy_traffic = traffic_for("tile_copy_16384x16384_f16")
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("tile GEMM 8192x8192x8192 bf16 A,B normal(0,1)/sqrt(K), fp32 D, beta=0 + "
+                         "streaming tile copy 2^28 fp16 (16384x16384, 128x64 tiles, 256 threads, "
+                         "XOR-swizzled LDS)"),
+            "M": M, "N": N, "K": K, "copy_rows": ROWS, "copy_cols": COLS,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": gemm_traffic,
+            "kernel": "gemm_tiled 256x256x64 bf16 (transA=0, transB=0)", "avg_ms": round(g_avg, 5),
+        },
+        "copy": {
+            "value": round(gbs, 2), "unit": "GB/s", "avg_ms": round(c_avg, 5),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": copy_traffic},
+        },
+        "gemm_f16_transA_beta1": {"value": round(flops / (h_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+                                   "avg_ms": round(h_ms, 5),
+                                   "frac": round(flops / (h_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+        "parity": {"gemm_sampled_ok": bool(g_ok), "gemm_worst_err_over_tol": round(g_worst, 5),
+                   "copy_bit_exact": c_ok},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

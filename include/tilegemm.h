@@ -1,0 +1,227 @@
+/*
+ * tilegemm.h — C ABI of the MI355X (gfx950) tile GEMM and tile copy library.
+ *
+ * Sources (cited by page title and section):
+ *   [SYNC-GEMM]  "TVM TIRx 同步 GEMM 深度解析：warp 级 mma.sync 的寄存器碎片排布与完整下放链路"
+ *                (trdm.cn/news/580350), sections 一 … 八 and the closing test-coverage part.
+ *   [VEC-AUTO]   "TVM TIRx CUDA 向量化内存拷贝实战：vec_auto 变体的 global↔shared 实现路径（gmem_smem）
+ *                深度解析" (0539edu.com/news/4886382).
+ *   [TCGEN05-CP] "TVM Blackwell tcgen05.cp 全解析：shared→tmem 异步拷贝的形状选择、矩阵描述符与调度算法"
+ *                (pnsm.cn/news/1939927).
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     allocates no device memory and keeps no pointer after a call returns.
+ *   - Device pointers: A, B, C, D, src and dst are device (HBM) pointers of the
+ *     current HIP device.  Host-only entry points (the *_plan functions and
+ *     tile_copy_partition) take addresses only to test alignment and never
+ *     dereference them; they need no GPU.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream).  Launches are asynchronous on that stream; the library creates
+ *     no stream and never synchronises.
+ *   - Errors: every argument is validated before anything is launched, so a
+ *     rejected call writes nothing.  The return value is a tg_status; the
+ *     reason of the last failure on the calling thread is tile_last_error().
+ *     A HIP launch failure returns TG_E_HIP with the HIP error text.
+ *   - Rejection, never masking: a call the kernels cannot serve exactly is
+ *     refused with a reason rather than run on a slow scalar path
+ *     ([VEC-AUTO] 接受什么输入; [SYNC-GEMM] 测试覆盖, rejection tests).
+ */
+#ifndef TILEGEMM_H
+#define TILEGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats.  GEMM operands A and B take TG_F16 or TG_BF16; copies move
+ * any of them as raw bits. */
+typedef enum tg_dtype {
+  TG_F16 = 1,       /* IEEE binary16 */
+  TG_BF16 = 2,      /* bfloat16 */
+  TG_F32 = 3,       /* IEEE binary32 */
+  TG_U8 = 4,        /* uint8 */
+  TG_I8 = 5,        /* int8 */
+  TG_FP8_E4M3 = 6,  /* float8 e4m3fn */
+  TG_FP8_E5M2 = 7   /* float8 e5m2 */
+} tg_dtype;
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_E_NULL = -1,     /* a required pointer is NULL */
+  TG_E_SHAPE = -2,    /* extents: negative, M%16, N%8, K%8, or not a whole number of tiles */
+  TG_E_DTYPE = -3,    /* unsupported element format */
+  TG_E_BETA = -4,     /* beta not exactly 0.0 or 1.0 */
+  TG_E_ALIAS = -5,    /* an output overlaps an input other than the allowed C == D */
+  TG_E_ALIGN = -6,    /* a GEMM operand cannot be read with 128-bit vectors */
+  TG_E_THREADS = -7,  /* thread count <= 0, > 1024, or not dividing the tile's elements */
+  TG_E_LAYOUT = -8,   /* layout kind / leading dimension not usable */
+  TG_E_HIP = -9,      /* HIP runtime or launch error */
+  TG_E_ARG = -10      /* any other invalid argument (flags, transpose values, NULL out-params) */
+} tg_status;
+
+/* Layout of a rows x cols matrix in memory ([VEC-AUTO] 算法核心 step 1: a
+ * copy is described by the layouts of its two sides). */
+typedef enum tg_layout_kind {
+  TG_ROW_MAJOR = 0,    /* element (r, c) at r*ld + c; ld >= cols, 0 = packed (cols) */
+  TG_COL_MAJOR = 1,    /* element (r, c) at c*ld + r; ld >= rows, 0 = packed (rows) */
+  TG_XOR_SWIZZLE = 2   /* packed row-major tile, each row cut into 16-byte chunks whose
+                          index is XOR-ed with (r mod min(8, chunks per row)); rows must be a
+                          power-of-two number of chunks.  For 128-byte rows this is
+                          x ^ ((x & 0x380) >> 3) on the byte offset x — the swizzle family
+                          of [TCGEN05-CP] 调度算法 step 2 with 16-byte atoms. */
+} tg_layout_kind;
+
+typedef struct tg_layout {
+  int32_t kind;      /* tg_layout_kind */
+  int32_t reserved;  /* must be 0 */
+  int64_t ld;        /* leading dimension in elements; 0 = packed */
+} tg_layout;
+
+/* How tile_copy_ex stages a tensor: it is cut into tile_rows x tile_cols
+ * tiles; a workgroup of `threads` threads moves one tile global -> LDS
+ * (laid out as lds_kind: TG_ROW_MAJOR or TG_XOR_SWIZZLE), synchronises, then
+ * LDS -> global. */
+typedef struct tg_copy_opts {
+  int32_t tile_rows;
+  int32_t tile_cols;
+  int32_t threads;   /* 1 .. 1024 */
+  int32_t lds_kind;  /* TG_ROW_MAJOR or TG_XOR_SWIZZLE */
+  int32_t flags;     /* must be 0 */
+} tg_copy_opts;
+
+/* One direction of a tile copy as the vec_auto partition [outer, threads,
+ * vec]: round f of thread t moves the fused elements
+ * [(f*threads + t)*vec, +vec) of the tile in the driving (global) side's order
+ * ([VEC-AUTO] 算法核心 steps 1–2 and 生成的 TIRx IR). */
+typedef struct tg_copy_phase {
+  int32_t outer;     /* rounds per thread */
+  int32_t threads;
+  int32_t vec;       /* elements per vector transfer */
+  int32_t vec_bits;  /* vec * element bits: 128, 64, 32, 16 or 8 */
+} tg_copy_phase;
+
+typedef struct tg_copy_plan {
+  tg_copy_phase load;   /* global (src) -> LDS, driven by the src layout's order */
+  tg_copy_phase store;  /* LDS -> global (dst), driven by the dst layout's order */
+  int32_t tile_rows, tile_cols, lds_kind, lds_bytes;
+  int64_t tiles;        /* number of tiles = workgroup-iterations */
+} tg_copy_plan;
+
+/* Kernel choice of tile_gemm, reported by tile_gemm_plan. */
+typedef enum tg_gemm_kernel {
+  TG_GEMM_NONE = 0,     /* nothing to launch (M == 0 or N == 0) */
+  TG_GEMM_ATOM = 1,     /* register kernel: one wave per 16x16 output tile, v_mfma_f32_16x16x32 */
+  TG_GEMM_TILED = 2,    /* LDS double-buffered kernel, v_mfma_f32_32x32x16 */
+  TG_GEMM_FILL = 3      /* K == 0: D = beta*C without a product */
+} tg_gemm_kernel;
+
+typedef struct tg_gemm_plan {
+  int32_t kernel;                 /* tg_gemm_kernel */
+  int32_t block_m, block_n, block_k;
+  int32_t wave_m, wave_n;         /* output tile of one wavefront */
+  int32_t threads;                /* per workgroup */
+  int32_t bounds_checked;         /* 1 when some tile is ragged (masked loads and stores) */
+  int32_t lds_bytes;
+  int64_t grid;                   /* workgroups */
+} tg_gemm_plan;
+
+/*
+ * tile_gemm — D = A·B + beta·C   ([SYNC-GEMM] 一, 二, 四 step 3).
+ *
+ *   A      device, dtype (TG_F16 or TG_BF16).  Stored row-major [M,K] when transA == 0,
+ *          [K,M] when transA == 1.  Packed (leading dimension K or M).
+ *   B      device, same dtype.  Stored row-major [K,N] when transB == 0, [N,K] when transB == 1.
+ *   C      device fp32 [M,N] row-major packed; read only when beta == 1 (may be NULL when
+ *          beta == 0).  C may be exactly D (in-place D += A·B); any other overlap with D is
+ *          rejected.
+ *   D      device fp32 [M,N] row-major packed; written.  Must not overlap A or B.
+ *   M,N,K  M % 16 == 0, N % 8 == 0, K % 8 == 0, all >= 0 ([SYNC-GEMM] 二).  M == 0 or N == 0 is
+ *          a no-op; K == 0 gives D = beta·C.
+ *   transA, transB   0 or 1; they only describe the stored orientation, the product is
+ *          always A[M,K]·B[K,N] ([SYNC-GEMM] 二 and 四 step 1).
+ *   beta   exactly 0.0 (D = A·B, C never read) or 1.0 (D = A·B + C).  alpha is fixed at 1
+ *          ([SYNC-GEMM] 二: alpha = 1.0, beta ∈ {0.0, 1.0}).
+ *   dtype  TG_F16 or TG_BF16 for both A and B; C and D are fp32.  Products are formed
+ *          exactly and accumulated in fp32 in place over K by MFMA.
+ *   Alignment: A and B 16-byte aligned (128-bit loads), C and D 4-byte aligned; otherwise
+ *          TG_E_ALIGN.
+ * Returns TG_OK or a tg_status; asynchronous on `stream`.
+ */
+int tile_gemm(const void* A, const void* B, const float* C, float* D,
+              int64_t M, int64_t N, int64_t K, int transA, int transB,
+              float beta, int dtype, void* stream);
+
+/*
+ * tile_gemm_plan — host-only validation and kernel choice of tile_gemm for the same
+ * arguments (pointers are only tested for NULL, alignment and overlap).  Returns what
+ * tile_gemm would return before launching, and fills *out on TG_OK.  Needs no GPU.
+ */
+int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D,
+                   int64_t M, int64_t N, int64_t K, int transA, int transB,
+                   float beta, int dtype, tg_gemm_plan* out);
+
+/*
+ * tile_copy — bit-exact copy of a shape[0] x shape[1] matrix from src to dst, staged
+ * global -> LDS -> global by workgroups with the default options below
+ * ([VEC-AUTO]: copy is a synchronous element copy; the gmem_smem path).
+ *
+ *   src, dst    device buffers of dtype elements; dst must not overlap src.
+ *   shape       {rows, cols}, both >= 0; an empty shape is a no-op.
+ *   dtype       any tg_dtype (moved as bits; both sides have the same dtype).
+ *   src_layout, dst_layout   TG_ROW_MAJOR or TG_COL_MAJOR with ld (0 = packed); a global side
+ *               may be TG_XOR_SWIZZLE only when the whole matrix is one tile (it then
+ *               exposes the LDS image: the tile written in LDS physical order).
+ * Default options: tile_cols = min(cols, 128 bytes / element size), tile_rows =
+ * min(rows, 128); threads = 256 when the tile holds a multiple of 256 elements, else 64,
+ * else the largest power of two dividing the tile's elements; lds_kind = TG_XOR_SWIZZLE
+ * when the tile's rows are a power-of-two number of 16-byte chunks, else TG_ROW_MAJOR.
+ * The vector width of each direction is the widest of 128/64/32/16/8 bits that keeps every
+ * transfer contiguous and aligned on both of its sides, for every tile ([VEC-AUTO] 算法核心
+ * step 2; 对齐约束的兜底: misalignment narrows the width, down to one element).
+ * Rejections: the thread count must divide the tile's elements ([VEC-AUTO] 接受什么输入,
+ * _divides_thread_cnt) -> TG_E_THREADS; the tensor must be a whole number of tiles ->
+ * TG_E_SHAPE.
+ */
+int tile_copy(const void* src, void* dst, const int64_t shape[2], int dtype,
+              const tg_layout* src_layout, const tg_layout* dst_layout, void* stream);
+
+/* tile_copy_ex — tile_copy with explicit staging options (opts != NULL). */
+int tile_copy_ex(const void* src, void* dst, const int64_t shape[2], int dtype,
+                 const tg_layout* src_layout, const tg_layout* dst_layout,
+                 const tg_copy_opts* opts, void* stream);
+
+/*
+ * tile_copy_plan — host-only: the plan tile_copy_ex would run (opts may be NULL for the
+ * defaults).  src and dst are used only for their alignment.  Returns the same status the
+ * copy would return before launching.  Needs no GPU.
+ */
+int tile_copy_plan(const void* src, const void* dst, const int64_t shape[2], int dtype,
+                   const tg_layout* src_layout, const tg_layout* dst_layout,
+                   const tg_copy_opts* opts, tg_copy_plan* out);
+
+/*
+ * tile_copy_partition — host-only: the vec_auto partition of ONE rows x cols region copied
+ * between a driving (global) side and another side ([VEC-AUTO] 接受什么输入 and 算法核心
+ * steps 1–2).  Bases are element offsets of the region's first element on each side
+ * (pointer address / element size plus region offset).  threads <= 0 or not dividing
+ * rows*cols -> TG_E_THREADS.  elem_bits is 8, 16, 32 or 64.  Needs no GPU.
+ */
+int tile_copy_partition(int64_t rows, int64_t cols, int elem_bits, int threads,
+                        const tg_layout* drive, int64_t drive_base,
+                        const tg_layout* other, int64_t other_base,
+                        tg_copy_phase* out);
+
+/* Reason for the last failure on the calling thread ("" after a success). */
+const char* tile_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int tile_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEGEMM_H */

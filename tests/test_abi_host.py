@@ -1,0 +1,249 @@
+"""Host-only checks of libtilegemm.so (no GPU): exported symbols, planner and
+validation decisions against the oracle, kernel choice.  Integer decisions must
+match exactly."""
+
+import itertools
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tile_level_gemm_amd as tg
+from oracle import gemm as ogemm
+from oracle.layout import COL, ROW, XOR, Layout
+from oracle.planner import Plan, Reject, plan_region, plan_tiles
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KIND = {ROW: tg.TG_ROW_MAJOR, COL: tg.TG_COL_MAJOR, XOR: tg.TG_XOR_SWIZZLE}
+CATEGORY = {tg.TG_E_THREADS: "threads", tg.TG_E_LAYOUT: "layout", tg.TG_E_SHAPE: "shape",
+            tg.TG_E_DTYPE: "dtype", tg.TG_E_BETA: "beta"}
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "tilegemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tile_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"tile_gemm", "tile_copy", "tile_copy_ex", "tile_copy_plan", "tile_gemm_plan",
+            "tile_copy_partition", "tile_last_error", "tile_abi_version"} <= set(names)
+    lib = tg.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert tg.tile_abi_version() == 1
+
+
+# ------------------------------------------------------------- planner ----
+
+def c_partition(rows, cols, eb, threads, drive, other):
+    try:
+        p = tg.tile_copy_partition(rows, cols, 8 * eb, threads, (KIND[drive.kind], drive.ld), drive.base,
+                                   (KIND[other.kind], other.ld), other.base)
+        return Plan(p.outer, p.threads, p.vec, p.vec_bits)
+    except tg.TileError as e:
+        return Reject(CATEGORY[e.status], e.reason)
+
+
+def same(a, b):
+    if isinstance(a, Reject) or isinstance(b, Reject):
+        return isinstance(a, Reject) and isinstance(b, Reject) and a.category == b.category
+    return a == b
+
+
+def _partition_cases():
+    rs = np.random.default_rng(77)
+    shapes = [(8, 16), (16, 16), (4, 24), (32, 32), (16, 8), (6, 40), (1, 64), (8, 64), (3, 5),
+              (128, 64), (64, 32), (2, 128), (12, 12)]
+    for (rows, cols), eb, threads in itertools.product(shapes, (1, 2, 4, 8), (0, 1, 3, 4, 8, 32, 64, 256)):
+        kind = rs.choice([ROW, ROW, COL])
+        full = cols if kind == ROW else rows
+        ld = int(full + rs.choice([0, 0, 1, 2, 4, 8, 16, 20]))
+        base = int(rs.choice([0, 0, 1, 2, 4, 8, 16, 3, 6]))
+        okind = rs.choice([ROW, ROW, XOR, COL])
+        oful = cols if okind != COL else rows
+        old = 0 if okind == XOR else int(oful + rs.choice([0, 0, 8]))
+        obase = 0 if okind == XOR else int(rs.choice([0, 0, 4, 2]))
+        yield rows, cols, eb, threads, Layout(kind, ld, base), Layout(okind, old, obase)
+
+
+@pytest.mark.parametrize("case", list(_partition_cases()))
+def test_partition_matches_oracle(case):
+    rows, cols, eb, threads, drive, other = case
+    want = plan_region(rows, cols, 8 * eb, threads, drive, other)
+    got = c_partition(rows, cols, eb, threads, drive, other)
+    assert same(got, want), (case, got, want)
+
+
+def _golden(name):
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        return json.load(f)
+
+
+def test_golden_fixtures_through_the_library():
+    g = _golden("planner_worked_example.json")
+    p = c_partition(g["rows"], g["cols"], g["elem_bits"] // 8, g["threads"],
+                    Layout(ROW, 32, 0), Layout(ROW, 32, 0))
+    assert p == Plan(8, 32, 4, 128)
+    g = _golden("planner_dtype_rounds.json")
+    for case in g["cases"]:
+        p = c_partition(32, 32, case["elem_bits"] // 8, 32, Layout(ROW), Layout(ROW))
+        assert (p.vec, p.outer) == (case["vec"], case["outer"])
+    g = _golden("planner_rejections_and_narrowing.json")
+    for case in g["reject"]:
+        p = c_partition(case["rows"], case["cols"], case["elem_bits"] // 8, case["threads"],
+                        Layout(ROW), Layout(ROW))
+        assert isinstance(p, Reject) and p.category == case["category"]
+    for case in g["narrow"]:
+        s, d = case["src"], case["dst"]
+        p = c_partition(case["rows"], case["cols"], case["elem_bits"] // 8, case["threads"],
+                        Layout(s["kind"], s["ld"], s["base"]), Layout(d["kind"], d["ld"], d["base"]))
+        assert (p.vec, p.outer) == (case["vec"], case["outer"])
+
+
+def _tiled_cases():
+    rs = np.random.default_rng(99)
+    for _ in range(300):
+        eb = int(rs.choice([1, 2, 4]))
+        tr, tc = int(rs.choice([1, 2, 4, 8, 16])), int(rs.choice([2, 4, 8, 16, 32, 64]))
+        nr, nc = int(rs.integers(1, 4)), int(rs.integers(1, 4))
+        rows, cols = tr * nr, tc * nc
+        threads = int(rs.choice([1, 2, 4, 8, 16, 32, 64]))
+        skind = rs.choice([ROW, ROW, COL])
+        dkind = rs.choice([ROW, COL])
+        sld = (cols if skind == ROW else rows) + int(rs.choice([0, 0, 2, 4, 8, 3]))
+        dld = (cols if dkind == ROW else rows) + int(rs.choice([0, 0, 8, 1]))
+        soff, doff = int(rs.choice([0, 0, 1, 2, 8])), int(rs.choice([0, 0, 4]))
+        lds = rs.choice([ROW, XOR])
+        yield rows, cols, tr, tc, eb, threads, (skind, sld, soff), (dkind, dld, doff), lds
+
+
+@pytest.mark.parametrize("case", list(_tiled_cases()))
+def test_tiled_copy_plan_matches_oracle(case):
+    rows, cols, tr, tc, eb, threads, s, d, lds = case
+    base_addr = 1 << 20
+    src_addr = base_addr + s[2] * eb
+    dst_addr = (1 << 28) + d[2] * eb
+    lds_side = Layout(lds, tc if lds == ROW else 0, 0)
+    want_l = plan_tiles(rows, cols, tr, tc, 8 * eb, threads, Layout(s[0], s[1], src_addr // eb), lds_side)
+    want_s = plan_tiles(rows, cols, tr, tc, 8 * eb, threads, Layout(d[0], d[1], dst_addr // eb), lds_side)
+    dtype = {1: tg.TG_U8, 2: tg.TG_F16, 4: tg.TG_F32}[eb]
+    opts = dict(tile_rows=tr, tile_cols=tc, threads=threads, lds_kind=KIND[lds])
+    try:
+        p = tg.tile_copy_plan(src_addr, dst_addr, (rows, cols), dtype, (KIND[s[0]], s[1]),
+                              (KIND[d[0]], d[1]), opts)
+        got_l = Plan(*[getattr(p.load, f) for f in ("outer", "threads", "vec", "vec_bits")])
+        got_s = Plan(*[getattr(p.store, f) for f in ("outer", "threads", "vec", "vec_bits")])
+        assert p.tiles == (rows // tr) * (cols // tc)
+    except tg.TileError as e:
+        got_l = got_s = Reject(CATEGORY.get(e.status, "other"), e.reason)
+    assert same(got_l, want_l), (case, got_l, want_l)
+    if not isinstance(got_l, Reject):
+        assert same(got_s, want_s), (case, got_s, want_s)
+
+
+def test_copy_plan_configs_and_rejections():
+    # 32x32 f32 by one wavefront, row-major LDS
+    p = tg.tile_copy_plan(1 << 20, 1 << 24, (32, 32), tg.TG_F32, None, None,
+                          dict(tile_rows=32, tile_cols=32, threads=64, lds_kind=tg.TG_ROW_MAJOR))
+    assert p.load.as_tuple() == (4, 64, 4, 128) and p.store.as_tuple() == (4, 64, 4, 128)
+    # 128x64 f16, 256 threads, XOR LDS; defaults pick the same
+    p = tg.tile_copy_plan(1 << 20, 1 << 24, (128, 64), tg.TG_F16)
+    assert (p.tile_rows, p.tile_cols, p.lds_kind, p.tiles) == (128, 64, tg.TG_XOR_SWIZZLE, 1)
+    assert p.load.as_tuple() == (4, 256, 8, 128)
+    # the streaming copy: 16384^2 f16 in 128x64 tiles
+    p = tg.tile_copy_plan(1 << 30, 1 << 31, (16384, 16384), tg.TG_F16)
+    assert p.tiles == 32768 and p.load.as_tuple() == (4, 256, 8, 128) and p.lds_bytes == 16384
+    # thread count must divide the tile: 64-element tile on 1024 threads
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_copy_plan(1 << 20, 1 << 24, (1, 64), tg.TG_F16, None, None,
+                          dict(tile_rows=1, tile_cols=64, threads=1024, lds_kind=tg.TG_ROW_MAJOR))
+    assert e.value.status == tg.TG_E_THREADS
+    # ragged tensor (not a whole number of tiles)
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_copy_plan(1 << 20, 1 << 24, (100, 64), tg.TG_F16, None, None,
+                          dict(tile_rows=128, tile_cols=64, threads=256, lds_kind=tg.TG_XOR_SWIZZLE))
+    assert e.value.status == tg.TG_E_SHAPE
+    # overlapping src/dst
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_copy_plan(1 << 20, (1 << 20) + 64, (32, 32), tg.TG_F32)
+    assert e.value.status == tg.TG_E_ALIAS
+    # misaligned source narrows the load width, the store keeps 128 bits
+    p = tg.tile_copy_plan((1 << 20) + 2, 1 << 24, (128, 64), tg.TG_F16)
+    assert p.load.vec == 1 and p.store.vec == 8
+    # empty tensor is a no-op plan
+    p = tg.tile_copy_plan(None, None, (0, 64), tg.TG_F16)
+    assert p.tiles == 0
+    # bad dtype and layout
+    for bad in (dict(dtype=99), dict(src=(7, 0))):
+        with pytest.raises(tg.TileError):
+            tg.tile_copy_plan(1 << 20, 1 << 24, (32, 32), bad.get("dtype", tg.TG_F32), bad.get("src"))
+
+
+# ---------------------------------------------------------------- GEMM ----
+
+A_ADDR, B_ADDR, C_ADDR, D_ADDR = 1 << 32, 1 << 33, 1 << 34, 1 << 35
+ODT = {tg.TG_F16: "f16", tg.TG_BF16: "bf16"}
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 8, 16), (8, 8, 16), (16, 4, 16), (16, 8, 12), (32, 24, 40),
+                                   (0, 8, 16), (16, 8, 0), (-16, 8, 8), (64, 64, 24), (512, 512, 256)])
+@pytest.mark.parametrize("dtype", [tg.TG_F16, tg.TG_BF16, tg.TG_F32, tg.TG_I8])
+@pytest.mark.parametrize("beta", [0.0, 1.0, 0.5, 2.0])
+def test_gemm_validation_matches_oracle(M, N, K, dtype, beta):
+    want_ok, want_cat = ogemm.accepts(M, N, K, ODT.get(dtype, "other"), ODT.get(dtype, "other"), beta=beta)
+    try:
+        tg.tile_gemm_plan(A_ADDR, B_ADDR, C_ADDR, D_ADDR, M, N, K, 0, 0, beta, dtype)
+        got_ok, got_cat = True, None
+    except tg.TileError as e:
+        got_ok, got_cat = False, CATEGORY.get(e.status, "other")
+    assert (got_ok, got_cat) == (want_ok, want_cat)
+
+
+def test_gemm_rejections_need_no_gpu():
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm(A_ADDR, B_ADDR, C_ADDR, D_ADDR, 16, 8, 16, 0, 0, 0.5, tg.TG_F16)
+    assert e.value.status == tg.TG_E_BETA
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm(A_ADDR, B_ADDR, None, D_ADDR, 16, 8, 16, 0, 0, 1.0, tg.TG_F16)
+    assert e.value.status == tg.TG_E_NULL
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm(A_ADDR + 8, B_ADDR, None, D_ADDR, 16, 8, 16, 0, 0, 0.0, tg.TG_F16)
+    assert e.value.status == tg.TG_E_ALIGN
+    with pytest.raises(tg.TileError) as e:  # D overlaps A
+        tg.tile_gemm(A_ADDR, B_ADDR, None, A_ADDR + 64, 16, 8, 16, 0, 0, 0.0, tg.TG_F16)
+    assert e.value.status == tg.TG_E_ALIAS
+    with pytest.raises(tg.TileError) as e:  # C partially overlaps D
+        tg.tile_gemm(A_ADDR, B_ADDR, D_ADDR + 4, D_ADDR, 16, 8, 16, 0, 0, 1.0, tg.TG_F16)
+    assert e.value.status == tg.TG_E_ALIAS
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm(A_ADDR, B_ADDR, None, D_ADDR, 16, 8, 16, 2, 0, 0.0, tg.TG_F16)
+    assert e.value.status == tg.TG_E_ARG
+    # C == D exactly is the allowed in-place form
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, D_ADDR, D_ADDR, 16, 8, 16, 0, 0, 1.0, tg.TG_F16)
+    assert p.kernel == tg.TG_GEMM_ATOM
+
+
+def test_binding_rejects_alpha():
+    import torch
+    a = torch.zeros(16, 16, dtype=torch.float16)
+    with pytest.raises(tg.TileError):
+        tg.gemm(a, a, alpha=2.0)
+
+
+def test_gemm_kernel_choice():
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 16, 8, 16, 0, 0, 0.0, tg.TG_F16)
+    assert (p.kernel, p.grid, p.threads) == (tg.TG_GEMM_ATOM, 1, 64)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, C_ADDR, D_ADDR, 512, 512, 256, 0, 1, 1.0, tg.TG_BF16)
+    assert p.kernel == tg.TG_GEMM_TILED and p.grid >= 64 and not p.bounds_checked
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 8192, 8192, 8192, 0, 0, 0.0, tg.TG_BF16)
+    assert (p.kernel, p.block_m, p.block_n, p.grid, p.bounds_checked) == (tg.TG_GEMM_TILED, 256, 256, 1024, 0)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 528, 520, 264, 1, 0, 0.0, tg.TG_F16)
+    assert p.kernel == tg.TG_GEMM_TILED and p.bounds_checked
+    p = tg.tile_gemm_plan(None, None, None, D_ADDR, 16, 8, 0, 0, 0, 0.0, tg.TG_F16)
+    assert p.kernel == tg.TG_GEMM_FILL
+    p = tg.tile_gemm_plan(None, None, None, None, 0, 8, 16, 0, 0, 0.0, tg.TG_F16)
+    assert p.kernel == tg.TG_GEMM_NONE

@@ -1,0 +1,150 @@
+"""GPU parity of tile_gemm against the oracle: |D - D_ref| <= 1e-4·sum|a·b| + 1e-6 per element."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import tile_level_gemm_amd as tg
+from oracle import gemm as og
+from tests.gpu_util import Guarded, say, upload_bits, upload_f32
+
+pytestmark = pytest.mark.gpu
+
+FMT = {"f16": tg.TG_F16, "bf16": tg.TG_BF16}
+
+
+def run_gemm(a_bits, b_bits, c, M, N, K, ta, tb, beta, fmt, c_is_d=False):
+    A = upload_bits(a_bits)
+    B = upload_bits(b_bits)
+    D = Guarded(M * N * 4, fill=(c if c_is_d else np.full((M, N), np.nan, np.float32)))
+    Cd = None
+    if beta == 1.0 and not c_is_d:
+        Cd = upload_f32(c)
+    cptr = D.ptr if c_is_d else Cd
+    tg.tile_gemm(A, B, cptr, D.ptr, M, N, K, ta, tb, beta, FMT[fmt])
+    torch.cuda.synchronize()
+    return D.host(np.float32).reshape(M, N), D.guards_intact()
+
+
+def full_check(M, N, K, fmt, ta, tb, beta, seeds, dist="normal", c_is_d=False, scale=1.0):
+    a_bits, b_bits, c = synth.gemm_inputs(M, N, K, fmt, ta, tb, beta, seeds, a_scale=scale,
+                                          b_scale=scale, dist=dist, c_dist=dist)
+    d, guards = run_gemm(a_bits, b_bits, c, M, N, K, ta, tb, beta, fmt, c_is_d=c_is_d)
+    ref = og.gemm_ref(a_bits, b_bits, c, M, N, K, ta, tb, beta, fmt)
+    bound = og.abs_bound(a_bits, b_bits, M, N, K, ta, tb, fmt)
+    ok, worst = og.check(d, ref, bound)
+    assert guards, "guard band written"
+    assert ok, f"worst |D-D_ref|/tol = {worst}"
+    return worst
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_atom_16x8x16(beta):
+    say(f"gemm atom 16x8x16 f16 beta={beta}")
+    a_bits, b_bits, c = synth.atom_inputs(beta)
+    d, guards = run_gemm(a_bits, b_bits, c, 16, 8, 16, False, False, beta, "f16")
+    ref = og.gemm_ref(a_bits, b_bits, c, 16, 8, 16, False, False, beta, "f16")
+    bound = og.abs_bound(a_bits, b_bits, 16, 8, 16, False, False, "f16")
+    ok, worst = og.check(d, ref, bound)
+    assert guards and ok, worst
+
+
+def test_gemm_512x512x256_bf16_transb_beta1():
+    say("gemm 512x512x256 bf16 transB beta=1")
+    a_bits, b_bits, c = synth.gemm512_inputs()
+    d, guards = run_gemm(a_bits, b_bits, c, 512, 512, 256, False, True, 1.0, "bf16")
+    ref = og.gemm_ref(a_bits, b_bits, c, 512, 512, 256, False, True, 1.0, "bf16")
+    bound = og.abs_bound(a_bits, b_bits, 512, 512, 256, False, True, "bf16")
+    ok, worst = og.check(d, ref, bound)
+    assert guards and ok, worst
+
+
+# The page's tiled categories (single tile, one dim multi-tile, all dims, M = 64, K = 8,
+# K = 24) plus ragged edges of every kernel configuration.
+SHAPES = [(16, 8, 16), (16, 8, 8), (16, 8, 24), (32, 8, 16), (16, 24, 16), (64, 8, 16),
+          (64, 64, 24), (80, 72, 40), (128, 128, 64), (192, 136, 72), (320, 264, 200),
+          (528, 520, 264), (1536, 1536, 128), (1552, 1544, 136), (4096, 4096, 128),
+          (4112, 4104, 72)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("fmt,beta", [("f16", 0.0), ("f16", 1.0), ("bf16", 0.0), ("bf16", 1.0)])
+def test_tiled_shapes(M, N, K, fmt, beta):
+    say(f"gemm {M}x{N}x{K} {fmt} beta={beta}")
+    full_check(M, N, K, fmt, False, False, beta, (M + 1, N + 2, K + 3))
+
+
+@pytest.mark.parametrize("M,N,K", [(48, 24, 40), (320, 192, 128), (1552, 1544, 136), (4096, 4096, 128),
+                                   (4112, 4104, 72)])
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_transposes(M, N, K, fmt, ta, tb):
+    say(f"gemm {M}x{N}x{K} {fmt} transA={ta} transB={tb}")
+    full_check(M, N, K, fmt, ta, tb, 1.0, (7, 8, 9))
+
+
+def test_k_zero_and_empty():
+    say("gemm K=0 / M=0")
+    c = synth.uniform(5, 32 * 16).reshape(32, 16)
+    D = Guarded(32 * 16 * 4, fill=np.full((32, 16), np.nan, np.float32))
+    tg.tile_gemm(None, None, upload_f32(c), D.ptr, 32, 16, 0, 0, 0, 1.0, tg.TG_F16)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.host(np.float32).reshape(32, 16), c) and D.guards_intact()
+    tg.tile_gemm(None, None, None, D.ptr, 32, 16, 0, 0, 0, 0.0, tg.TG_BF16)
+    torch.cuda.synchronize()
+    assert not D.host(np.float32).any() and D.guards_intact()
+    E = Guarded(64, fill=np.full(16, 7.0, np.float32))
+    tg.tile_gemm(None, None, None, E.ptr, 0, 16, 16, 0, 0, 0.0, tg.TG_F16)
+    torch.cuda.synchronize()
+    assert np.all(E.host(np.float32) == 7.0) and E.guards_intact()
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 8, 16), (256, 192, 96), (1552, 1544, 136)])
+def test_in_place_c_is_d(M, N, K):
+    say(f"gemm in-place C==D {M}x{N}x{K}")
+    full_check(M, N, K, "bf16", False, False, 1.0, (11, 12, 13), c_is_d=True)
+
+
+def test_beta0_ignores_nan_c():
+    say("gemm beta=0 with NaN C")
+    M, N, K = 320, 264, 200
+    a_bits, b_bits, _ = synth.gemm_inputs(M, N, K, "f16", False, False, 0.0, (1, 2, 3))
+    A, B = upload_bits(a_bits), upload_bits(b_bits)
+    Cn = torch.full((M, N), float("nan"), device="cuda:0")
+    D1 = torch.empty((M, N), device="cuda:0")
+    D2 = torch.empty((M, N), device="cuda:0")
+    tg.tile_gemm(A, B, Cn, D1, M, N, K, 0, 0, 0.0, tg.TG_F16)
+    tg.tile_gemm(A, B, None, D2, M, N, K, 0, 0, 0.0, tg.TG_F16)
+    torch.cuda.synchronize()
+    assert torch.isfinite(D1).all() and torch.equal(D1, D2)
+
+
+def _sampled(M, N, K, fmt, ta, tb, beta, inputs, sample_seed, tag):
+    a_bits, b_bits, c = inputs
+    say(f"gemm {tag}: {M}x{N}x{K} {fmt} transA={ta} transB={tb} beta={beta}")
+    A, B = upload_bits(a_bits), upload_bits(b_bits)
+    Cd = upload_f32(c) if beta == 1.0 else None
+    D = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    plan = tg.tile_gemm_plan(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
+    assert (plan.block_m, plan.block_n, plan.bounds_checked) == (256, 256, 0)
+    tg.tile_gemm(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
+    D2 = torch.empty_like(D)
+    tg.tile_gemm(A, B, Cd, D2, M, N, K, ta, tb, beta, FMT[fmt])
+    torch.cuda.synchronize()
+    assert torch.equal(D, D2), "two runs differ (no atomics: results must be bitwise repeatable)"
+    rows, cols = synth.sample_points(M, N, sample_seed)
+    d_gpu = D.cpu().numpy()[rows, cols]
+    ref, bound = og.gemm_ref_at(a_bits, b_bits, c, M, N, K, ta, tb, beta, fmt, rows, cols)
+    ok, worst = og.check(d_gpu, ref, bound)
+    say(f"{tag}: worst |D-D_ref|/tol = {worst:.3g} over {rows.size} samples")
+    assert ok, worst
+    assert torch.isfinite(D).all()
+
+
+def test_gemm_8192_bf16_beta0_sampled():
+    _sampled(8192, 8192, 8192, "bf16", False, False, 0.0, synth.gemm8k_bf16_inputs(), 53, "8192 bf16")
+
+
+def test_gemm_8192_f16_transa_beta1_sampled():
+    _sampled(8192, 8192, 8192, "f16", True, False, 1.0, synth.gemm8k_f16_inputs(), 57, "8192 f16")

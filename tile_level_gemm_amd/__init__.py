@@ -1,0 +1,228 @@
+"""Python binding of libtilegemm.so (argument marshalling only).
+
+Every function of include/tilegemm.h is exposed under the same name and takes the
+same arguments; device buffers may be given as torch tensors or raw addresses.
+All compute runs in the library's HIP kernels; PyTorch only provides device
+memory and the current stream.  There is no fallback: if the library is not built
+every call raises.
+
+`torch` is imported before the library is loaded so that the library binds to the
+HIP runtime torch already loaded (one runtime per process).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtilegemm.so")
+
+# enums of include/tilegemm.h
+TG_F16, TG_BF16, TG_F32, TG_U8, TG_I8, TG_FP8_E4M3, TG_FP8_E5M2 = 1, 2, 3, 4, 5, 6, 7
+TG_OK, TG_E_NULL, TG_E_SHAPE, TG_E_DTYPE, TG_E_BETA, TG_E_ALIAS = 0, -1, -2, -3, -4, -5
+TG_E_ALIGN, TG_E_THREADS, TG_E_LAYOUT, TG_E_HIP, TG_E_ARG = -6, -7, -8, -9, -10
+TG_ROW_MAJOR, TG_COL_MAJOR, TG_XOR_SWIZZLE = 0, 1, 2
+TG_GEMM_NONE, TG_GEMM_ATOM, TG_GEMM_TILED, TG_GEMM_FILL = 0, 1, 2, 3
+
+STATUS_NAMES = {0: "TG_OK", -1: "TG_E_NULL", -2: "TG_E_SHAPE", -3: "TG_E_DTYPE", -4: "TG_E_BETA",
+                -5: "TG_E_ALIAS", -6: "TG_E_ALIGN", -7: "TG_E_THREADS", -8: "TG_E_LAYOUT",
+                -9: "TG_E_HIP", -10: "TG_E_ARG"}
+
+TORCH_DTYPES = {torch.float16: TG_F16, torch.bfloat16: TG_BF16, torch.float32: TG_F32,
+                torch.uint8: TG_U8, torch.int8: TG_I8}
+for _name, _code in (("float8_e4m3fn", TG_FP8_E4M3), ("float8_e5m2", TG_FP8_E5M2)):
+    if hasattr(torch, _name):
+        TORCH_DTYPES[getattr(torch, _name)] = _code
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("ld", ctypes.c_int64)]
+
+
+class CopyOpts(ctypes.Structure):
+    _fields_ = [("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("lds_kind", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class CopyPhase(ctypes.Structure):
+    _fields_ = [("outer", ctypes.c_int32), ("threads", ctypes.c_int32), ("vec", ctypes.c_int32),
+                ("vec_bits", ctypes.c_int32)]
+
+    def as_tuple(self):
+        return (self.outer, self.threads, self.vec, self.vec_bits)
+
+
+class CopyPlan(ctypes.Structure):
+    _fields_ = [("load", CopyPhase), ("store", CopyPhase), ("tile_rows", ctypes.c_int32),
+                ("tile_cols", ctypes.c_int32), ("lds_kind", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("tiles", ctypes.c_int64)]
+
+
+class GemmPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("bounds_checked", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int64)]
+
+
+class TileError(RuntimeError):
+    """A non-TG_OK status; .status holds the code, str() the library's reason."""
+
+    def __init__(self, status, reason):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+_lib = None
+
+_I64, _INT, _VP, _F = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+_SIGS = {
+    "tile_gemm": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT, _VP]),
+    "tile_gemm_plan": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT,
+                              ctypes.POINTER(GemmPlan)]),
+    "tile_copy": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
+                         ctypes.POINTER(Layout), _VP]),
+    "tile_copy_ex": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
+                            ctypes.POINTER(Layout), ctypes.POINTER(CopyOpts), _VP]),
+    "tile_copy_plan": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
+                              ctypes.POINTER(Layout), ctypes.POINTER(CopyOpts),
+                              ctypes.POINTER(CopyPlan)]),
+    "tile_copy_partition": (_INT, [_I64, _I64, _INT, _INT, ctypes.POINTER(Layout), _I64,
+                                   ctypes.POINTER(Layout), _I64, ctypes.POINTER(CopyPhase)]),
+    "tile_last_error": (ctypes.c_char_p, []),
+    "tile_abi_version": (_INT, []),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m tile_level_gemm_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def tile_last_error():
+    return lib().tile_last_error().decode()
+
+
+def tile_abi_version():
+    return lib().tile_abi_version()
+
+
+def _check(status):
+    if status != TG_OK:
+        raise TileError(status, tile_last_error())
+
+
+def _addr(x):
+    """Device address of a tensor (or an int address, or None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, torch.Tensor):
+        if x.numel() and not x.is_contiguous():
+            raise ValueError("tensors passed to the library must be contiguous")
+        return x.data_ptr() if x.numel() else (x.data_ptr() or None)
+    raise TypeError(f"expected a tensor, an int address or None, got {type(x)}")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _layout(x):
+    if x is None:
+        return Layout(TG_ROW_MAJOR, 0, 0)
+    if isinstance(x, Layout):
+        return x
+    kind, ld = (x, 0) if isinstance(x, int) else x
+    return Layout(kind, 0, ld)
+
+
+def _shape(shape):
+    return (ctypes.c_int64 * 2)(int(shape[0]), int(shape[1]))
+
+
+# ------------------------------------------------------------------ GEMM ----
+
+def tile_gemm(A, B, C, D, M, N, K, transA, transB, beta, dtype, stream=None):
+    """D = A·B + beta·C through the library (see include/tilegemm.h)."""
+    _check(lib().tile_gemm(_addr(A), _addr(B), _addr(C), _addr(D), M, N, K, int(transA),
+                           int(transB), float(beta), int(dtype), _stream(stream)))
+
+
+def tile_gemm_plan(A, B, C, D, M, N, K, transA, transB, beta, dtype):
+    out = GemmPlan()
+    _check(lib().tile_gemm_plan(_addr(A), _addr(B), _addr(C), _addr(D), M, N, K, int(transA),
+                                int(transB), float(beta), int(dtype), ctypes.byref(out)))
+    return out
+
+
+def gemm(A, B, C=None, beta=0.0, trans_a=False, trans_b=False, alpha=1.0, out=None, stream=None):
+    """Tensor convenience: returns D (fp32) = A·B (+C).  alpha must be 1 (the primitive has none)."""
+    if alpha != 1.0:
+        raise TileError(TG_E_ARG, "alpha must be 1.0")
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+        raise TileError(TG_E_DTYPE, "A and B must both be float16 or both bfloat16")
+    M = A.shape[1] if trans_a else A.shape[0]
+    K = A.shape[0] if trans_a else A.shape[1]
+    N = B.shape[0] if trans_b else B.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    tile_gemm(A, B, C, out, M, N, K, trans_a, trans_b, beta, TORCH_DTYPES[A.dtype], stream)
+    return out
+
+
+# ------------------------------------------------------------------ copy ----
+
+def _opts(opts):
+    if opts is None or isinstance(opts, CopyOpts):
+        return opts
+    return CopyOpts(int(opts.get("tile_rows", 0)), int(opts.get("tile_cols", 0)),
+                    int(opts.get("threads", 0)), int(opts.get("lds_kind", TG_XOR_SWIZZLE)),
+                    int(opts.get("flags", 0)))
+
+
+def tile_copy(src, dst, shape, dtype, src_layout=None, dst_layout=None, stream=None):
+    sl, dl = _layout(src_layout), _layout(dst_layout)
+    _check(lib().tile_copy(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
+                           ctypes.byref(dl), _stream(stream)))
+
+
+def tile_copy_ex(src, dst, shape, dtype, src_layout, dst_layout, opts, stream=None):
+    sl, dl, o = _layout(src_layout), _layout(dst_layout), _opts(opts)
+    _check(lib().tile_copy_ex(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
+                              ctypes.byref(dl), ctypes.byref(o) if o is not None else None,
+                              _stream(stream)))
+
+
+def tile_copy_plan(src, dst, shape, dtype, src_layout=None, dst_layout=None, opts=None):
+    sl, dl, o = _layout(src_layout), _layout(dst_layout), _opts(opts)
+    out = CopyPlan()
+    _check(lib().tile_copy_plan(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
+                                ctypes.byref(dl), ctypes.byref(o) if o is not None else None,
+                                ctypes.byref(out)))
+    return out
+
+
+def tile_copy_partition(rows, cols, elem_bits, threads, drive, drive_base, other, other_base):
+    d, o = _layout(drive), _layout(other)
+    out = CopyPhase()
+    _check(lib().tile_copy_partition(rows, cols, elem_bits, threads, ctypes.byref(d), drive_base,
+                                     ctypes.byref(o), other_base, ctypes.byref(out)))
+    return out

@@ -1,0 +1,344 @@
+// C-ABI entry points: argument validation, planning and launch.
+//
+// Validation follows [SYNC-GEMM] 二 ("What it accepts": M%16, N%8, K%8; A and B
+// both f16 or both bf16; C and D fp32; alpha = 1; beta in {0, 1}; transposes
+// normalised to A[M,K], B[K,N]) and [VEC-AUTO] 接受什么输入 (the copy's element
+// count must divide over its threads; equal dtype on both sides).  Every check
+// runs before any HIP call, so a rejected call writes nothing and the host-only
+// entry points need no GPU.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "tg_internal.h"
+
+namespace tg {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const std::string& why) {
+  g_last_error = why;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace tg
+
+using namespace tg;
+
+namespace {
+
+const int64_t kMaxDim = (int64_t)1 << 30;
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, f, a, b, c);
+  return buf;
+}
+
+int validate_gemm(const void* A, const void* B, const float* C, const float* D, int64_t M,
+                  int64_t N, int64_t K, int transA, int transB, float beta, int dtype) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(TG_E_SHAPE, fmt("negative extent (M=%lld, N=%lld, K=%lld)", M, N, K));
+  if (M % 16 || N % 8 || K % 8)
+    return fail(TG_E_SHAPE,
+                fmt("gemm needs M %% 16 == 0, N %% 8 == 0, K %% 8 == 0 (got M=%lld, N=%lld, K=%lld)",
+                    M, N, K));
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(TG_E_SHAPE, "extent above 2^30");
+  if (dtype != TG_F16 && dtype != TG_BF16)
+    return fail(TG_E_DTYPE, fmt("gemm operands must be TG_F16 or TG_BF16 (got dtype %lld); C and D "
+                                "are fp32", dtype));
+  if (transA != 0 && transA != 1) return fail(TG_E_ARG, "transA must be 0 or 1");
+  if (transB != 0 && transB != 1) return fail(TG_E_ARG, "transB must be 0 or 1");
+  if (!(beta == 0.0f || beta == 1.0f))
+    return fail(TG_E_BETA, "beta must be exactly 0.0 or 1.0 (alpha is fixed at 1)");
+  if (M == 0 || N == 0) return TG_OK;
+  if (!D) return fail(TG_E_NULL, "D is NULL");
+  if (beta == 1.0f && !C) return fail(TG_E_NULL, "beta == 1 needs C");
+  if (K > 0 && (!A || !B)) return fail(TG_E_NULL, "A or B is NULL");
+  const int64_t dbytes = M * N * 4;
+  if (K > 0) {
+    if (overlaps(D, dbytes, A, M * K * 2) || overlaps(D, dbytes, B, K * N * 2))
+      return fail(TG_E_ALIAS, "D overlaps A or B");
+    if ((uintptr_t)A % 16 || (uintptr_t)B % 16)
+      return fail(TG_E_ALIGN, "A and B must be 16-byte aligned for 128-bit operand loads");
+  }
+  if (beta == 1.0f && C != D && overlaps(D, dbytes, C, dbytes))
+    return fail(TG_E_ALIAS, "C overlaps D without being exactly D");
+  if ((uintptr_t)D % 4 || (beta == 1.0f && (uintptr_t)C % 4))
+    return fail(TG_E_ALIGN, "C and D must be 4-byte aligned");
+  return TG_OK;
+}
+
+bool valid_kind(int k) { return k == TG_ROW_MAJOR || k == TG_COL_MAJOR || k == TG_XOR_SWIZZLE; }
+
+// Validates a copy and fills the plan and launch arguments.
+int plan_copy(const void* src, const void* dst, const int64_t shape[2], int dtype,
+              const tg_layout* sl, const tg_layout* dl, const tg_copy_opts* opts,
+              tg_copy_plan* plan, CopyArgs* args) {
+  if (!shape) return fail(TG_E_NULL, "shape is NULL");
+  if (!sl || !dl) return fail(TG_E_NULL, "src_layout or dst_layout is NULL");
+  const int64_t rows = shape[0], cols = shape[1];
+  if (rows < 0 || cols < 0) return fail(TG_E_SHAPE, "negative extent");
+  if (rows > kMaxDim || cols > kMaxDim) return fail(TG_E_SHAPE, "extent above 2^30");
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(TG_E_DTYPE, fmt("unknown dtype %lld", dtype));
+  if (!valid_kind(sl->kind) || !valid_kind(dl->kind) || sl->reserved || dl->reserved)
+    return fail(TG_E_LAYOUT, "unknown layout kind or nonzero reserved field");
+  if (sl->ld < 0 || dl->ld < 0) return fail(TG_E_LAYOUT, "negative leading dimension");
+  if (opts && opts->flags) return fail(TG_E_ARG, "opts->flags must be 0");
+
+  std::memset(plan, 0, sizeof *plan);
+  std::memset(args, 0, sizeof *args);
+  if (rows == 0 || cols == 0) {
+    const int t = opts ? opts->threads : 256;
+    if (t <= 0 || t > 1024) return fail(TG_E_THREADS, "threads must be in 1..1024");
+    plan->load = plan->store = tg_copy_phase{0, t, 1, 8 * eb};
+    return TG_OK;
+  }
+  if (!src || !dst) return fail(TG_E_NULL, "src or dst is NULL");
+
+  // Tile and workgroup choice.
+  tg_copy_opts o{};
+  if (opts) {
+    o = *opts;
+  } else {
+    o.tile_cols = (int32_t)std::min<int64_t>(cols, 128 / eb);
+    o.tile_rows = (int32_t)std::min<int64_t>(rows, 128);
+    const int64_t te = (int64_t)o.tile_rows * o.tile_cols;
+    if (te % 256 == 0) o.threads = 256;
+    else if (te % 64 == 0) o.threads = 64;
+    else { o.threads = 1; while (o.threads < 64 && te % (2 * o.threads) == 0) o.threads *= 2; }
+    const int64_t rb = (int64_t)o.tile_cols * eb;
+    o.lds_kind = (rb % 16 == 0 && ((rb / 16) & (rb / 16 - 1)) == 0) ? TG_XOR_SWIZZLE : TG_ROW_MAJOR;
+  }
+  if (o.threads <= 0 || o.threads > 1024) return fail(TG_E_THREADS, "threads must be in 1..1024");
+  if (o.tile_rows <= 0 || o.tile_cols <= 0) return fail(TG_E_SHAPE, "tile extents must be positive");
+  if (o.lds_kind != TG_ROW_MAJOR && o.lds_kind != TG_XOR_SWIZZLE)
+    return fail(TG_E_LAYOUT, "the LDS layout must be TG_ROW_MAJOR or TG_XOR_SWIZZLE");
+  if (rows % o.tile_rows || cols % o.tile_cols)
+    return fail(TG_E_SHAPE, fmt("a %lld x %lld tensor is not a whole number of %lld-row tiles", rows,
+                                cols, o.tile_rows) + fmt(" x %lld-col tiles", o.tile_cols));
+  const int64_t lds_bytes = (int64_t)o.tile_rows * o.tile_cols * eb;
+  if (lds_bytes > 65536) return fail(TG_E_SHAPE, "a tile may hold at most 64 KiB of LDS");
+  const int64_t tiles_r = rows / o.tile_rows, tiles_c = cols / o.tile_cols;
+
+  // Global sides, with leading dimensions resolved.
+  auto resolve = [&](const tg_layout* l, const void* p, Side* s, const char* name) -> int {
+    s->kind = l->kind;
+    if (l->kind == TG_ROW_MAJOR) {
+      s->ld = l->ld ? l->ld : cols;
+      if (s->ld < cols) return fail(TG_E_LAYOUT, std::string(name) + ": row-major ld < cols");
+    } else if (l->kind == TG_COL_MAJOR) {
+      s->ld = l->ld ? l->ld : rows;
+      if (s->ld < rows) return fail(TG_E_LAYOUT, std::string(name) + ": column-major ld < rows");
+    } else {
+      if (tiles_r != 1 || tiles_c != 1)
+        return fail(TG_E_LAYOUT, std::string(name) + ": an XOR-swizzled global side must be one tile");
+      if (l->ld != 0 && l->ld != cols)
+        return fail(TG_E_LAYOUT, std::string(name) + ": an XOR-swizzled side is packed");
+      s->ld = cols;
+    }
+    if ((uintptr_t)p % eb) return fail(TG_E_ALIGN, std::string(name) + ": not element aligned");
+    s->base = (int64_t)((uintptr_t)p / eb);
+    return TG_OK;
+  };
+  Side ss, ds;
+  int st = resolve(sl, src, &ss, "src");
+  if (st) return st;
+  st = resolve(dl, dst, &ds, "dst");
+  if (st) return st;
+  const int64_t extent_s = (ss.kind == TG_COL_MAJOR ? (cols - 1) * ss.ld + rows
+                                                    : (rows - 1) * ss.ld + cols) * eb;
+  const int64_t extent_d = (ds.kind == TG_COL_MAJOR ? (cols - 1) * ds.ld + rows
+                                                    : (rows - 1) * ds.ld + cols) * eb;
+  if (overlaps(src, extent_s, dst, extent_d)) return fail(TG_E_ALIAS, "dst overlaps src");
+
+  const Side lds{o.lds_kind, o.tile_cols, 0};
+  std::string why;
+  tg_copy_phase lp, sp;
+  // Per direction: the widest width that the region and every tile step accept.
+  auto phase = [&](const Side& g, tg_copy_phase* out, const char* dir) -> int {
+    int r = partition(o.tile_rows, o.tile_cols, eb, o.threads, g, lds, out, &why);
+    if (r) return fail(r, std::string(dir) + ": " + why);
+    // Every width below an accepted one is accepted too (all conditions are
+    // divisibilities by a power of two), so halving finds the widest width
+    // that also keeps every tile's base aligned.
+    while (out->vec > 1 && !tile_steps_aligned(g, o.tile_rows, o.tile_cols, tiles_r, tiles_c, out->vec)) {
+      out->vec /= 2;
+      out->vec_bits /= 2;
+      out->outer *= 2;
+    }
+    return TG_OK;
+  };
+  st = phase(ss, &lp, "load");
+  if (st) return st;
+  st = phase(ds, &sp, "store");
+  if (st) return st;
+
+  plan->load = lp;
+  plan->store = sp;
+  plan->tile_rows = o.tile_rows;
+  plan->tile_cols = o.tile_cols;
+  plan->lds_kind = o.lds_kind;
+  plan->lds_bytes = (int32_t)lds_bytes;
+  plan->tiles = tiles_r * tiles_c;
+
+  args->src = (const uint8_t*)src;
+  args->dst = (uint8_t*)dst;
+  args->src_ld = ss.ld;
+  args->dst_ld = ds.ld;
+  args->src_kind = ss.kind;
+  args->dst_kind = ds.kind;
+  args->tile_rows = o.tile_rows;
+  args->tile_cols = o.tile_cols;
+  args->tiles_c = tiles_c;
+  args->ntiles = plan->tiles;
+  args->eb = eb;
+  args->lds_xor = o.lds_kind == TG_XOR_SWIZZLE;
+  {
+    const int64_t chunks = (int64_t)o.tile_cols * eb / 16;
+    args->xor_mask = (int32_t)(std::min<int64_t>(8, std::max<int64_t>(chunks, 1)) - 1);
+  }
+  args->threads = o.threads;
+  auto fill = [&](const Side& g, const tg_copy_phase& p, CopyPhase* c) {
+    c->outer = p.outer;
+    c->vec = p.vec;
+    c->row_order = g.kind != TG_COL_MAJOR;
+    c->inner = c->row_order ? o.tile_cols : o.tile_rows;
+    c->inner_log2 = -1;
+    for (int s = 0; s < 31; ++s)
+      if ((1 << s) == c->inner) c->inner_log2 = s;
+  };
+  fill(ss, lp, &args->load);
+  fill(ds, sp, &args->store);
+  return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tile_last_error(void) { return g_last_error.c_str(); }
+
+int tile_abi_version(void) { return 1; }
+
+int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D, int64_t M,
+                   int64_t N, int64_t K, int transA, int transB, float beta, int dtype,
+                   tg_gemm_plan* out) {
+  clear_error();
+  if (!out) return fail(TG_E_ARG, "out is NULL");
+  int st = validate_gemm(A, B, C, D, M, N, K, transA, transB, beta, dtype);
+  if (st) return st;
+  const GemmConfig c = choose_gemm(M, N, K);
+  out->kernel = c.kernel;
+  out->block_m = c.bm;
+  out->block_n = c.bn;
+  out->block_k = c.bk;
+  out->wave_m = c.wm;
+  out->wave_n = c.wn;
+  out->threads = c.threads;
+  out->bounds_checked = c.bounds;
+  out->lds_bytes = c.lds_bytes;
+  out->grid = c.grid;
+  return TG_OK;
+}
+
+int tile_gemm(const void* A, const void* B, const float* C, float* D, int64_t M, int64_t N,
+              int64_t K, int transA, int transB, float beta, int dtype, void* stream) {
+  clear_error();
+  int st = validate_gemm(A, B, C, D, M, N, K, transA, transB, beta, dtype);
+  if (st) return st;
+  const GemmConfig cfg = choose_gemm(M, N, K);
+  if (cfg.kernel == TG_GEMM_NONE) return TG_OK;
+  if (cfg.kernel == TG_GEMM_FILL && beta == 1.0f && C == D) return TG_OK;
+  GemmArgs g{};
+  g.A = (const uint16_t*)A;
+  g.B = (const uint16_t*)B;
+  g.C = beta == 1.0f ? C : nullptr;
+  g.D = D;
+  g.M = (int32_t)M;
+  g.N = (int32_t)N;
+  g.K = (int32_t)K;
+  g.use_c = beta == 1.0f;
+  if (cfg.bm) {
+    g.tiles_m = (int32_t)((M + cfg.bm - 1) / cfg.bm);
+    g.tiles_n = (int32_t)((N + cfg.bn - 1) / cfg.bn);
+  }
+  return launch_gemm(g, cfg, transA, transB, dtype, stream);
+}
+
+int tile_copy_plan(const void* src, const void* dst, const int64_t shape[2], int dtype,
+                   const tg_layout* src_layout, const tg_layout* dst_layout,
+                   const tg_copy_opts* opts, tg_copy_plan* out) {
+  clear_error();
+  if (!out) return fail(TG_E_ARG, "out is NULL");
+  CopyArgs args;
+  return plan_copy(src, dst, shape, dtype, src_layout, dst_layout, opts, out, &args);
+}
+
+int tile_copy_ex(const void* src, void* dst, const int64_t shape[2], int dtype,
+                 const tg_layout* src_layout, const tg_layout* dst_layout,
+                 const tg_copy_opts* opts, void* stream) {
+  clear_error();
+  if (!opts) return fail(TG_E_ARG, "opts is NULL (use tile_copy for the defaults)");
+  tg_copy_plan plan;
+  CopyArgs args;
+  int st = plan_copy(src, dst, shape, dtype, src_layout, dst_layout, opts, &plan, &args);
+  if (st) return st;
+  if (plan.tiles == 0) return TG_OK;
+  return launch_tile_copy(args, plan.load.vec * args.eb, plan.store.vec * args.eb, plan.lds_bytes,
+                          stream);
+}
+
+int tile_copy(const void* src, void* dst, const int64_t shape[2], int dtype,
+              const tg_layout* src_layout, const tg_layout* dst_layout, void* stream) {
+  clear_error();
+  tg_copy_plan plan;
+  CopyArgs args;
+  int st = plan_copy(src, dst, shape, dtype, src_layout, dst_layout, nullptr, &plan, &args);
+  if (st) return st;
+  if (plan.tiles == 0) return TG_OK;
+  return launch_tile_copy(args, plan.load.vec * args.eb, plan.store.vec * args.eb, plan.lds_bytes,
+                          stream);
+}
+
+int tile_copy_partition(int64_t rows, int64_t cols, int elem_bits, int threads,
+                        const tg_layout* drive, int64_t drive_base, const tg_layout* other,
+                        int64_t other_base, tg_copy_phase* out) {
+  clear_error();
+  if (!drive || !other || !out) return fail(TG_E_NULL, "NULL argument");
+  if (elem_bits != 8 && elem_bits != 16 && elem_bits != 32 && elem_bits != 64)
+    return fail(TG_E_DTYPE, "elem_bits must be 8, 16, 32 or 64");
+  if (!valid_kind(drive->kind) || !valid_kind(other->kind))
+    return fail(TG_E_LAYOUT, "unknown layout kind");
+  if (drive->kind == TG_XOR_SWIZZLE)
+    return fail(TG_E_LAYOUT, "the driving (global) side cannot be XOR-swizzled");
+  auto side = [&](const tg_layout* l, int64_t base) {
+    Side s{l->kind, l->ld, base};
+    if (!s.ld) s.ld = l->kind == TG_COL_MAJOR ? rows : cols;
+    if (l->kind == TG_XOR_SWIZZLE) s.ld = cols;
+    return s;
+  };
+  const Side d = side(drive, drive_base), o = side(other, other_base);
+  if ((d.kind == TG_ROW_MAJOR && d.ld < cols) || (d.kind == TG_COL_MAJOR && d.ld < rows) ||
+      (o.kind == TG_ROW_MAJOR && o.ld < cols) || (o.kind == TG_COL_MAJOR && o.ld < rows))
+    return fail(TG_E_LAYOUT, "leading dimension smaller than the region");
+  if (other->kind == TG_XOR_SWIZZLE && other->ld != 0 && other->ld != cols)
+    return fail(TG_E_LAYOUT, "an XOR-swizzled side is packed");
+  std::string why;
+  int st = partition(rows, cols, elem_bits / 8, threads, d, o, out, &why);
+  if (st) return fail(st, why);
+  return TG_OK;
+}
+
+}  // extern "C"

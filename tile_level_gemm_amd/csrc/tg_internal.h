@@ -1,0 +1,90 @@
+// Internal declarations shared by the C-ABI layer (abi.cpp), the host planner
+// (plan.cpp) and the HIP kernels (copy_kernels.hip, gemm_kernels.hip).
+// Not part of the public ABI: include/tilegemm.h is.
+#pragma once
+
+#include <stdint.h>
+#include <string>
+
+#include "../../include/tilegemm.h"
+
+namespace tg {
+
+// ---------------------------------------------------------------- errors ---
+// Sets the thread-local reason string and returns `code`.
+int fail(int code, const std::string& why);
+void clear_error();
+
+// --------------------------------------------------------------- planner ---
+// One side of a copy region: layout kind, resolved leading dimension (never 0)
+// and the element offset of the region's first element.
+struct Side {
+  int kind;
+  int64_t ld;
+  int64_t base;
+};
+
+int elem_bytes(int dtype);  // 0 for an unknown dtype
+
+// The vec_auto partition of one rows x cols region (see tile_copy_partition).
+// Returns TG_OK or a status with *why set.
+int partition(int64_t rows, int64_t cols, int eb, int threads, const Side& drive,
+              const Side& other, tg_copy_phase* out, std::string* why);
+
+// Extra alignment rule of a tiled tensor side: every tile's base must stay
+// aligned to `vec` (tile steps tile_rows*row_stride and tile_cols*col_stride).
+bool tile_steps_aligned(const Side& s, int64_t tile_rows, int64_t tile_cols, int64_t tiles_r,
+                        int64_t tiles_c, int64_t vec);
+
+// --------------------------------------------------------- launch structs ---
+struct CopyPhase {
+  int32_t outer;       // rounds per thread
+  int32_t vec;         // elements per transfer
+  int32_t row_order;   // 1: fused order is row-major over the tile, 0: column-major
+  int32_t inner;       // extent of the fused order's inner dimension
+  int32_t inner_log2;  // log2(inner) when a power of two, else -1
+};
+
+struct CopyArgs {
+  const uint8_t* src;
+  uint8_t* dst;
+  int64_t src_ld, dst_ld;     // elements
+  int32_t src_kind, dst_kind; // tg_layout_kind (XOR only for one-tile tensors)
+  int32_t tile_rows, tile_cols;
+  int64_t tiles_c;            // tiles along the column dimension
+  int64_t ntiles;
+  int32_t eb;                 // element bytes
+  int32_t lds_xor;            // LDS tile layout: 1 = XOR swizzle, 0 = packed row-major
+  int32_t xor_mask;           // (min(8, 16-byte chunks per tile row) - 1) for XOR layouts
+  int32_t threads;
+  CopyPhase load, store;
+};
+
+int launch_tile_copy(const CopyArgs& a, int vec_bytes_load, int vec_bytes_store, int lds_bytes,
+                     void* stream);
+
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  const float* C;
+  float* D;
+  int32_t M, N, K;
+  int32_t use_c;
+  int32_t tiles_m, tiles_n;
+};
+
+struct GemmConfig {
+  int kernel;          // tg_gemm_kernel
+  int bm, bn, bk, wm, wn, threads;
+  int bounds;          // ragged tiles present
+  int lds_bytes;
+  int64_t grid;
+};
+
+// Host-side kernel choice for a validated problem.
+GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K);
+
+int launch_gemm(const GemmArgs& g, const GemmConfig& cfg, int trans_a, int trans_b, int dtype,
+                void* stream);
+
+}  // namespace tg
