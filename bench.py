@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="before warmup, run one plain device-to-device copy of the 512 MiB copy "
+                         "source (torch copy_) as the known-size kernel that scales HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the tile GEMM and tile copy "
@@ -123,6 +126,9 @@ def main():
     S = up(copy_src_bits)
     T = torch.empty_like(S)
     torch.cuda.synchronize()
+    if args.calib_copy:
+        T.copy_(S)
+        torch.cuda.synchronize()
 
     def step(ev=None):
         if ev is not None:
