@@ -32,16 +32,24 @@ ROWS = COLS = 16384
 METRIC = "GEMM TFLOP/s + % MFMA peak (bf16 8192³); tile-copy GB/s + % HBM peak"
 
 
-def kernel_sources_sha():
+KERNEL_SOURCES = {
+    "gemm": ("gemm_kernels.hip", "lds_layout.h", "tg_internal.h"),
+    "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
+}
+
+
+def kernel_sources_sha(which):
+    """Hash of the sources a kernel is built from (counters go stale when it changes)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tile_level_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[which]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 def traffic_for(kernel):
+    # profiles/traffic.json: {kernel: {"sources": "gemm"|"copy", "sources_sha": ..., "bytes_per_launch": ...}}
     """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -49,7 +57,7 @@ def traffic_for(kernel):
     with open(path) as f:
         data = json.load(f)
     rec = data.get(kernel)
-    if not rec or rec.get("sources_sha") != kernel_sources_sha():
+    if not rec or rec.get("sources_sha") != kernel_sources_sha(rec.get("sources", "")):
         return None
     return rec.get("bytes_per_launch")
 
