@@ -126,6 +126,8 @@ typedef struct tg_gemm_plan {
   int32_t bounds_checked;         /* 1 when some tile is ragged (masked loads and stores) */
   int32_t lds_bytes;
   int64_t grid;                   /* workgroups */
+  int32_t loader;                 /* 0: operands staged through VGPRs, 1: direct global -> LDS */
+  int32_t reserved;
 } tg_gemm_plan;
 
 /*

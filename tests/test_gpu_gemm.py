@@ -75,7 +75,7 @@ def test_tiled_shapes(M, N, K, fmt, beta):
     full_check(M, N, K, fmt, False, False, beta, (M + 1, N + 2, K + 3))
 
 
-@pytest.mark.parametrize("M,N,K", [(48, 24, 40), (320, 192, 128), (1552, 1544, 136), (4096, 4096, 128),
+@pytest.mark.parametrize("M,N,K", [(48, 24, 40), (320, 192, 128), (1552, 1544, 136), (4096, 4096, 640),
                                    (4112, 4104, 72)])
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
@@ -127,7 +127,7 @@ def _sampled(M, N, K, fmt, ta, tb, beta, inputs, sample_seed, tag):
     Cd = upload_f32(c) if beta == 1.0 else None
     D = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
     plan = tg.tile_gemm_plan(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
-    assert (plan.block_m, plan.block_n, plan.bounds_checked) == (256, 256, 0)
+    assert (plan.block_m, plan.block_n, plan.bounds_checked, plan.loader) == (256, 256, 0, 1)
     tg.tile_gemm(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
     D2 = torch.empty_like(D)
     tg.tile_gemm(A, B, Cd, D2, M, N, K, ta, tb, beta, FMT[fmt])

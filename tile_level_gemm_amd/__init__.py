@@ -63,7 +63,8 @@ class GemmPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("block_k", ctypes.c_int32), ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("bounds_checked", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int64)]
+                ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int64), ("loader", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class TileError(RuntimeError):

@@ -250,6 +250,8 @@ int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D,
   out->bounds_checked = c.bounds;
   out->lds_bytes = c.lds_bytes;
   out->grid = c.grid;
+  out->loader = c.direct;
+  out->reserved = 0;
   return TG_OK;
 }
 

@@ -36,6 +36,8 @@
 //     in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "lds_layout.h"
 #include "tg_internal.h"
 
@@ -245,23 +247,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled(GemmArg
   }
 
   // epilogue: lane holds column n = lane%32 of each tile, rows 8(r/4) + 4(lane/32) + r%4
+  auto epilogue = [&](auto use_c) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn + 32 * j + (int)lrow;
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn + 32 * j + (int)lrow;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (int)khalf + (r & 3);
-        if (!BOUNDS || (m < g.M && n < g.N)) {
-          const int64_t o = (int64_t)m * g.N + n;
-          float d = acc[i][j][r];
-          if (g.use_c) d += g.C[o];
-          g.D[o] = d;
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (int)khalf + (r & 3);
+          if (!BOUNDS || (m < g.M && n < g.N)) {
+            const int64_t o = (int64_t)m * g.N + n;
+            float d = acc[i][j][r];
+            if constexpr (decltype(use_c)::value) d += g.C[o];
+            g.D[o] = d;
+          }
         }
       }
     }
-  }
+  };
+  if (g.use_c) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // --------------------------------------------------------- atom kernel ----
@@ -359,7 +365,9 @@ int launch_gemm(const GemmArgs& g, const GemmConfig& c, int trans_a, int trans_b
                 void* stream) {
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (c.kernel == TG_GEMM_FILL) {
+  if (c.kernel == TG_GEMM_TILED && c.direct) {
+    e = launch_gemm_direct(g, c.grid, trans_a, trans_b, dtype, s);
+  } else if (c.kernel == TG_GEMM_FILL) {
     hipLaunchKernelGGL(gemm_fill, dim3((unsigned)c.grid), dim3(256), 0, s, g);
     e = hipGetLastError();
   } else if (dtype == TG_F16) {

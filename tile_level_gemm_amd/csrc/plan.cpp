@@ -191,6 +191,7 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   c.bounds = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
   c.lds_bytes = 2 * (c.bm + c.bn) * 128;
   c.grid = blocks(c.bm, c.bn);
+  c.direct = c.bm == 256 && direct_gemm_fits(M, N, K);
   return c;
 }
 

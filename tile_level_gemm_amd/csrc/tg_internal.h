@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string>
 
+#include <hip/hip_runtime.h>
+
 #include "../../include/tilegemm.h"
 
 namespace tg {
@@ -79,6 +81,7 @@ struct GemmConfig {
   int bounds;          // ragged tiles present
   int lds_bytes;
   int64_t grid;
+  int direct;          // 1: gemm_direct (global -> LDS loads, whole 256x256 tiles, K % 128 == 0)
 };
 
 // Host-side kernel choice for a validated problem.
@@ -86,5 +89,9 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K);
 
 int launch_gemm(const GemmArgs& g, const GemmConfig& cfg, int trans_a, int trans_b, int dtype,
                 void* stream);
+
+bool direct_gemm_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
+                              hipStream_t s);
 
 }  // namespace tg
