@@ -21,6 +21,8 @@
 //    fragments are read while the current step's 16 MFMAs run.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tg_internal.h"
 
 namespace tg {
@@ -231,7 +233,8 @@ __global__ __launch_bounds__(256) void gemm_direct(GemmArgs g) {
   //   wave reads `cur` any more;
   //   then step 3's MFMAs (operands already in registers) overlap the reads of stage kt+1's
   //   first fragments and the DMA of stage kt+2 into `cur`.
-  const int KT = g.K / BK;   // even: K % 128 == 0
+  // The last two stages are peeled off the loop so the steady-state body is branch free.
+  const int KT = g.K / BK;   // even and >= 2: K % 128 == 0, K > 0
   oa.load(pa, lda, sa0, wave);
   ob.load(pb, ldb, sb0, wave);
   __builtin_amdgcn_s_waitcnt(0);
@@ -244,29 +247,57 @@ __global__ __launch_bounds__(256) void gemm_direct(GemmArgs g) {
     ob.load(pb + adv_b, ldb, sb1, wave);
   }
 
-  auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, int kt) {
+  // Instruction interleave of one K step: each LDS read (and, after the barrier, each DMA
+  // instruction) is paired with one MFMA so the matrix core never waits behind a burst of
+  // memory instructions.  kReads = LDS read instructions per K step for this operand mix.
+  constexpr int kReads = (A_MN ? 8 : 4) + (B_MN ? 8 : 4);
+  auto interleave_reads = [&]() {
+#pragma unroll
+    for (int q = 0; q < kReads; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
+  };
+  auto interleave_reads_dma = [&]() {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      if (q < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 DMA (VMEM read)
+    }
+  };
+
+  // One K stage.  DMA: also load stage kt+2 into the buffer this stage frees; NEXT: read
+  // the next stage's first fragments (false only for the last stage).
+  auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, int kt,
+                   auto dma, auto next) {
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       oa.frags(ca, s + 1, an);
       ob.frags(cb, s + 1, bn);
       mfmas(a, b);
+      interleave_reads();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         a[i] = an[i];
         b[i] = bn[i];
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep step 2's MFMAs ahead of the wait
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < KT) {
+    if constexpr (decltype(next)::value) {
       oa.frags(na, 0, an);
       ob.frags(nb_, 0, bn);
     }
-    if (kt + 2 < KT) {
+    if constexpr (decltype(dma)::value) {
       oa.load(pa + (int64_t)(kt + 2) * adv_a, lda, ca, wave);
       ob.load(pb + (int64_t)(kt + 2) * adv_b, ldb, cb, wave);
     }
     mfmas(a, b);
+    if constexpr (decltype(dma)::value) interleave_reads_dma();
+    else if constexpr (decltype(next)::value) interleave_reads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       a[i] = an[i];
@@ -274,25 +305,50 @@ __global__ __launch_bounds__(256) void gemm_direct(GemmArgs g) {
     }
   };
 
-  for (int kt = 0; kt < KT; kt += 2) {
-    stage(sa0, sb0, sa1, sb1, kt);
-    stage(sa1, sb1, sa0, sb0, kt + 1);
+  // Steady state: stages kt, kt+1 with kt + 3 < KT (both issue DMA); then the last two.
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    stage(sa0, sb0, sa1, sb1, kt, T_{}, T_{});
+    stage(sa1, sb1, sa0, sb0, kt + 1, T_{}, T_{});
   }
+  stage(sa0, sb0, sa1, sb1, kt, F_{}, T_{});
+  stage(sa1, sb1, sa0, sb0, kt + 1, F_{}, F_{});
 
   // epilogue: lane holds column n = lane%32 of each tile, rows 8(r/4) + 4(lane/32) + r%4
   const int lrow = lane & 31, khalf = lane >> 5;
   float* dbase = g.D + (int64_t)(m0 + wm + 4 * khalf) * g.N + (n0 + wn + lrow);
   if (g.use_c) {
+    // C may be exactly D, so the compiler may not move a C load above an earlier D store.
+    // Loads are therefore issued in program order one batch (one 32-row band, 64 values)
+    // ahead of the stores: every element is still read before it is written, and each
+    // batch costs one memory round trip instead of one per element.
     const float* cbase = g.C + (int64_t)(m0 + wm + 4 * khalf) * g.N + (n0 + wn + lrow);
+    float cv[2][4][16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        cv[0][j][r] = cbase[(int64_t)(8 * (r >> 2) + (r & 3)) * g.N + 32 * j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i + 1 < 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            cv[(i + 1) & 1][j][r] =
+                cbase[(int64_t)(32 * (i + 1) + 8 * (r >> 2) + (r & 3)) * g.N + 32 * j];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t o = (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * g.N + 32 * j;
-          dbase[o] = acc[i][j][r] + cbase[o];
+          dbase[o] = acc[i][j][r] + cv[i & 1][j][r];
         }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)

@@ -246,21 +246,31 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled(GemmArg
     __syncthreads();
   }
 
-  // epilogue: lane holds column n = lane%32 of each tile, rows 8(r/4) + 4(lane/32) + r%4
+  // epilogue: lane holds column n = lane%32 of each tile, rows 8(r/4) + 4(lane/32) + r%4.
+  // With beta = 1 the C values of a tile are loaded before any of its D stores: C may be
+  // exactly D, so program order must already put every load ahead of the store that could
+  // overwrite it; batching per tile turns 16 round trips into one.
   auto epilogue = [&](auto use_c) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn + 32 * j + (int)lrow;
+        float cv[16];
+        if constexpr (decltype(use_c)::value) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (int)khalf + (r & 3);
+            cv[r] = (!BOUNDS || (m < g.M && n < g.N)) ? g.C[(int64_t)m * g.N + n] : 0.0f;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (int)khalf + (r & 3);
           if (!BOUNDS || (m < g.M && n < g.N)) {
-            const int64_t o = (int64_t)m * g.N + n;
             float d = acc[i][j][r];
-            if constexpr (decltype(use_c)::value) d += g.C[o];
-            g.D[o] = d;
+            if constexpr (decltype(use_c)::value) d += cv[r];
+            g.D[(int64_t)m * g.N + n] = d;
           }
         }
       }
