@@ -33,7 +33,7 @@ METRIC = "GEMM TFLOP/s + % MFMA peak (bf16 8192³); tile-copy GB/s + % HBM peak"
 
 
 KERNEL_SOURCES = {
-    "gemm": ("gemm_kernels.hip", "lds_layout.h", "tg_internal.h"),
+    "gemm": ("gemm_direct.hip", "gemm_kernels.hip", "lds_layout.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
 }
 
@@ -60,6 +60,58 @@ def traffic_for(kernel):
     if not rec or rec.get("sources_sha") != kernel_sources_sha(rec.get("sources", "")):
         return None
     return rec.get("bytes_per_launch")
+
+
+TRAFFIC_KERNELS = {
+    # traffic.json key: (kernel-name substring in the rocprofv3 csv, sources, algorithmic bytes)
+    "gemm_direct_256x256_bf16_nn": ("gemm_direct<false, true, 1, 1, 2>", "gemm",
+                                    2 * M * K * 2 + M * N * 4),
+    "tile_copy_16384x16384_f16": ("tile_copy_rows<16>", "copy", 2 * ROWS * COLS * 2),
+}
+
+
+def summarize_counters(fetch_dir, write_dir, out_path):
+    """Write profiles/traffic.json from two rocprofv3 --pmc runs of `bench.py --calib-copy`.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the factors that make the
+    calibration copy (torch copy_ of the 512 MiB copy source: grid 131072 x 512) read and
+    write exactly 512 MiB; bytes_per_launch = scaled fetch + scaled write, averaged.
+    """
+    import csv
+
+    def load(d, counter):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        return [r for r in rows if r["Counter_Name"] == counter]
+
+    known = ROWS * COLS * 2
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+
+    def calib(rows):
+        cands = [float(r["Counter_Value"]) for r in rows
+                 if "copyBuffer" in r["Kernel_Name"] and r["Grid_Size"] == "131072"]
+        return max(cands)
+
+    ff = known / 1024.0 / calib(fetch)
+    wf = known / 1024.0 / calib(write)
+    out = {"_calibration": {"kernel": "__amd_rocclr_copyBuffer, 512 MiB device-to-device",
+                            "fetch_factor": ff, "write_factor": wf,
+                            "FETCH_SIZE_KiB": calib(fetch), "WRITE_SIZE_KiB": calib(write),
+                            "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- "
+                                         "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy"
+                                         for c in ("FETCH_SIZE", "WRITE_SIZE")]}}
+    for key, (sub, src, algo) in TRAFFIC_KERNELS.items():
+        fv = [float(r["Counter_Value"]) for r in fetch if sub in r["Kernel_Name"]]
+        wv = [float(r["Counter_Value"]) for r in write if sub in r["Kernel_Name"]]
+        if not fv or not wv:
+            continue
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        out[key] = {"kernel": sub, "sources": src, "sources_sha": kernel_sources_sha(src),
+                    "FETCH_SIZE_KiB": f_kib, "WRITE_SIZE_KiB": w_kib,
+                    "bytes_per_launch": round((f_kib * ff + w_kib * wf) * 1024),
+                    "algorithmic_bytes": algo}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def cpu_baseline(gemm_inputs, copy_src, budget_s=12.0):
@@ -105,12 +157,18 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="before warmup, run one plain device-to-device copy of the 512 MiB copy "
                          "source (torch copy_) as the known-size kernel that scales HBM counters")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc csv directories and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        res = summarize_counters(*args.summarize_counters, os.path.join(ROOT, "profiles", "traffic.json"))
+        print(json.dumps(res, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the tile GEMM and tile copy "
               "run on a single MI355X and this build has no multi-GPU path.", file=sys.stderr)
@@ -180,7 +238,7 @@ def main():
     hin = synth.gemm8k_f16_inputs()
     Ah, Bh = up(hin[0]), up(hin[1])
     Ch = torch.from_numpy(hin[2]).to(dev)
-    for _ in range(2):
+    for _ in range(args.warmup):
         tg.tile_gemm(Ah, Bh, Ch, D, M, N, K, 1, 0, 1.0, tg.TG_F16)
     hev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
@@ -197,7 +255,7 @@ def main():
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         base = cpu_baseline(gin, copy_src_bits)
 
-    gemm_traffic = traffic_for("gemm_tiled_256x256_bf16_nn")
+    gemm_traffic = traffic_for("gemm_direct_256x256_bf16_nn")
     copy_traffic = traffic_for("tile_copy_16384x16384_f16")
     out = {
         "metric": METRIC,
@@ -221,7 +279,7 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": gemm_traffic,
-            "kernel": "gemm_tiled 256x256x64 bf16 (transA=0, transB=0)", "avg_ms": round(g_avg, 5),
+            "kernel": "gemm_direct 256x256x64 bf16 (transA=0, transB=0)", "avg_ms": round(g_avg, 5),
         },
         "copy": {
             "value": round(gbs, 2), "unit": "GB/s", "avg_ms": round(c_avg, 5),

@@ -124,6 +124,57 @@ __global__ __launch_bounds__(1024) void tile_copy_kernel(CopyArgs a) {
   }
 }
 
+// Row-major fast path: both global sides row-major, one vector width VB for both directions,
+// and each round covers whole tile rows (threads·VB is a multiple of the tile's row bytes).
+// Then the element a thread moves in round f sits at row r_t + f·rpr, byte column cb_t,
+// where (r_t, cb_t) come from the thread index once; with rpr a multiple of the XOR period
+// the swizzled LDS offset only advances by rpr rows per round.  Same partition and result
+// as tile_copy_kernel, with the per-round divisions and layout switches folded away.
+template <int VB, int ROUNDS>
+__global__ __launch_bounds__(1024) void tile_copy_rows(CopyArgs a, int32_t rpr) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  using TV = typename VecT<VB>::T;
+  const uint32_t rowb = (uint32_t)(a.tile_cols * a.eb);
+  const uint32_t xb = (uint32_t)threadIdx.x * VB;
+  const uint32_t r_t = xb / rowb, cb_t = xb - r_t * rowb;
+  const uint32_t lds_t = a.lds_xor ? xor_swizzle_bytes(r_t, cb_t, rowb, (uint32_t)a.xor_mask)
+                                   : r_t * rowb + cb_t;
+  const uint32_t lds_step = (uint32_t)rpr * rowb;
+  const int64_t src_step = (int64_t)rpr * a.src_ld * a.eb;
+  const int64_t dst_step = (int64_t)rpr * a.dst_ld * a.eb;
+  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int64_t r0 = (tile / a.tiles_c) * a.tile_rows + r_t;
+    const int64_t c0 = (tile % a.tiles_c) * a.tile_cols;
+    const uint8_t* sp = a.src + (r0 * a.src_ld + c0) * a.eb + cb_t;
+    uint8_t* dp = a.dst + (r0 * a.dst_ld + c0) * a.eb + cb_t;
+    // all ROUNDS loads are in flight before the first LDS write
+    TV v[ROUNDS];
+#pragma unroll
+    for (int f = 0; f < ROUNDS; ++f) v[f] = __builtin_nontemporal_load((const TV*)(sp + f * src_step));
+#pragma unroll
+    for (int f = 0; f < ROUNDS; ++f) *(TV*)(lds + lds_t + (uint32_t)f * lds_step) = v[f];
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < ROUNDS; ++f)
+      __builtin_nontemporal_store(*(const TV*)(lds + lds_t + (uint32_t)f * lds_step),
+                                  (TV*)(dp + f * dst_step));
+    __syncthreads();
+  }
+}
+
+template <int VB>
+hipError_t launch_rows(const CopyArgs& a, int32_t rpr, int rounds, dim3 g, dim3 b, int lds,
+                       hipStream_t s) {
+  switch (rounds) {
+    case 1: hipLaunchKernelGGL((tile_copy_rows<VB, 1>), g, b, lds, s, a, rpr); break;
+    case 2: hipLaunchKernelGGL((tile_copy_rows<VB, 2>), g, b, lds, s, a, rpr); break;
+    case 4: hipLaunchKernelGGL((tile_copy_rows<VB, 4>), g, b, lds, s, a, rpr); break;
+    case 8: hipLaunchKernelGGL((tile_copy_rows<VB, 8>), g, b, lds, s, a, rpr); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int VL>
 hipError_t launch_vs(const CopyArgs& a, int vs, dim3 grid, dim3 block, int lds, hipStream_t s) {
   switch (vs) {
@@ -145,6 +196,22 @@ int launch_tile_copy(const CopyArgs& a, int vl, int vs, int lds_bytes, void* str
   const dim3 g((unsigned)grid), b((unsigned)a.threads);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
+  const int64_t rowb = (int64_t)a.tile_cols * a.eb;
+  const int64_t round_bytes = (int64_t)a.threads * vl;
+  const int rounds = a.load.outer;
+  const bool rows_fast = a.src_kind == TG_ROW_MAJOR && a.dst_kind == TG_ROW_MAJOR && vl == vs &&
+                         (vl == 16 || vl == 8 || vl == 4) && round_bytes % rowb == 0 &&
+                         (!a.lds_xor || ((round_bytes / rowb) % (a.xor_mask + 1)) == 0) &&
+                         a.load.outer == a.store.outer && a.load.row_order && a.store.row_order &&
+                         (rounds == 1 || rounds == 2 || rounds == 4 || rounds == 8);
+  if (rows_fast) {
+    const int32_t rpr = (int32_t)(round_bytes / rowb);
+    if (vl == 16) e = launch_rows<16>(a, rpr, rounds, g, b, lds_bytes, s);
+    else if (vl == 8) e = launch_rows<8>(a, rpr, rounds, g, b, lds_bytes, s);
+    else e = launch_rows<4>(a, rpr, rounds, g, b, lds_bytes, s);
+    if (e != hipSuccess) return fail(TG_E_HIP, std::string("tile_copy launch: ") + hipGetErrorString(e));
+    return TG_OK;
+  }
   switch (vl) {
     case 16: e = launch_vs<16>(a, vs, g, b, lds_bytes, s); break;
     case 8: e = launch_vs<8>(a, vs, g, b, lds_bytes, s); break;

@@ -34,10 +34,11 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const uint8_t gbl_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 8;   // tile-rows per scheduling group (measured: 8 beats 2, 4, 16)
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -149,14 +150,15 @@ struct Operand {
   // `wave` is wave-uniform (from readfirstlane) so the LDS block address is scalar.
   __device__ __forceinline__ void load(const uint16_t* panel, int64_t ld, uint8_t* stage,
                                        int wave) const {
-    const uint8_t* base = (const uint8_t*)panel;
+    // scalar base (panel + per-pair step) plus a 32-bit per-lane offset: saddr addressing
+    gbl_u8* base = (gbl_u8*)panel;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // K-major: +8 rows per instruction pair; M/N-major: +2 k-rows per instruction pair
       const int64_t step = MN ? (int64_t)(2 * (i & ~1)) * ld * 2 : (int64_t)(8 * (i & ~1)) * ld * 2;
-      const uint8_t* src = base + step + dma[i & 1];
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + (wave * 8 + i) * 1024),
-                                       16, 0, 0);
+      gbl_u8* src = base + step + dma[i & 1];
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (lds_void*)(stage + (wave * 8 + i) * 1024), 16, 0, 0);
     }
   }
   __device__ __forceinline__ void frags(const uint8_t* stage, int s, u32x4 (&f)[4]) const {

@@ -51,7 +51,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kBK = 64;      // K extent of one LDS stage (128-byte rows)
-constexpr int kGroupM = 4;   // tile-rows per scheduling group
+constexpr int kGroupM = 8;   // tile-rows per scheduling group
 
 template <int DT>
 struct Mfma;
