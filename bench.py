@@ -64,9 +64,9 @@ def traffic_for(kernel):
 
 TRAFFIC_KERNELS = {
     # traffic.json key: (kernel-name substring in the rocprofv3 csv, sources, algorithmic bytes)
-    "gemm_direct_256x256_bf16_nn": ("gemm_direct<false, true, 1, 1, 2>", "gemm",
+    "gemm_direct_256x256_bf16_nn": ("gemm_direct<false, true, 2, 2, 4>", "gemm",
                                     2 * M * K * 2 + M * N * 4),
-    "tile_copy_16384x16384_f16": ("tile_copy_rows<16>", "copy", 2 * ROWS * COLS * 2),
+    "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4>", "copy", 2 * ROWS * COLS * 2),
 }
 
 
@@ -279,7 +279,7 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": gemm_traffic,
-            "kernel": "gemm_direct 256x256x64 bf16 (transA=0, transB=0)", "avg_ms": round(g_avg, 5),
+            "kernel": "gemm_direct<A K-major, B N-major, bf16, 2x4 waves> 256x256x64", "avg_ms": round(g_avg, 5),
         },
         "copy": {
             "value": round(gbs, 2), "unit": "GB/s", "avg_ms": round(c_avg, 5),

@@ -192,6 +192,11 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   c.lds_bytes = 2 * (c.bm + c.bn) * 128;
   c.grid = blocks(c.bm, c.bn);
   c.direct = c.bm == 256 && direct_gemm_fits(M, N, K);
+  if (c.direct) {   // gemm_direct: 8 waves of 128 x 64
+    c.wm = 128;
+    c.wn = 64;
+    c.threads = 512;
+  }
   return c;
 }
 
