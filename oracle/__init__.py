@@ -18,8 +18,9 @@ The oracle is written from these pages (cited by title and section):
              矩阵描述符与调度算法" (pnsm.cn/news/1939927).
 
 Modules:
-  numerics  exact decoding of fp16 / bf16 bit patterns to float64
-  gemm      D = A·B (+C) in float64, the acceptance table, the error bound
+  numerics  exact decoding of fp16 / bf16 / fp8 (e4m3, e5m2) / e8m0 bit patterns to float64
+  gemm      D = A·B (+C) in float64 (16-bit operands, and the fp8 operands of the
+            asynchronous GEMM's precision family), the acceptance tables, the error bound
   layout    logical (row, col) -> element offset for row-major, column-major and
             the XOR-swizzled tile layout
   copy      element-by-element copy between two layouts (bit patterns)

@@ -24,6 +24,12 @@ fractions.Fraction on small shapes (the 16x8x16 atom included), beta = 0 vs 1
 semantics with NaN-filled C, transposition equivalence over all four
 (transA, transB) pairs and both formats, identity and zero matrices, and the
 acceptance table against the page's listed rejections.
+
+The fp8 entry points (accepts_fp8, gemm_fp8_ref, gemm_fp8_ref_at, abs_bound_fp8)
+are pinned by tests/test_oracle_gemm_fp8.py: exact int64 products of operands
+decoded by torch's own float8 types (all four format pairs, all transposes,
+both betas), beta semantics, transposition equivalence, identity / empty
+products, and their acceptance table.
 """
 
 import numpy as np
@@ -50,10 +56,12 @@ def accepts(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, 
     return True, None
 
 
-def logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, dtype):
-    """Decode A and B and normalise them to A[M, K], B[K, N] (float64)."""
+def logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, dtype, b_dtype=None):
+    """Decode A and B and normalise them to A[M, K], B[K, N] (float64).
+
+    b_dtype defaults to dtype (the synchronous GEMM takes one format for both)."""
     a = decode(a_bits, dtype)
-    b = decode(b_bits, dtype)
+    b = decode(b_bits, dtype if b_dtype is None else b_dtype)
     a = a.reshape((K, M) if trans_a else (M, K))
     b = b.reshape((N, K) if trans_b else (K, N))
     a_l = a.T if trans_a else a
@@ -94,6 +102,12 @@ def gemm_ref_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, dtype, rows,
     ok, why = accepts(M, N, K, dtype, dtype, beta=beta)
     if not ok:
         raise ValueError(f"oracle: call rejected ({why})")
+    return _dots_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, dtype, dtype, rows, cols,
+                    chunk)
+
+
+def _dots_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype, b_dtype, rows, cols,
+             chunk):
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     d = np.empty(rows.size)
@@ -101,8 +115,8 @@ def gemm_ref_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, dtype, rows,
     for s0 in range(0, rows.size, chunk):
         r = rows[s0:s0 + chunk]
         q = cols[s0:s0 + chunk]
-        a = decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, r)), dtype)
-        b = decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, q)), dtype)
+        a = decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, r)), a_dtype)
+        b = decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, q)), b_dtype)
         prod = a * b
         d[s0:s0 + chunk] = prod.sum(axis=1)
         bound[s0:s0 + chunk] = np.abs(prod).sum(axis=1)
@@ -110,6 +124,62 @@ def gemm_ref_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, dtype, rows,
         cc = np.asarray(c, dtype=np.float32).reshape(M, N)
         d = d + cc[rows, cols].astype(np.float64)
     return d, bound
+
+
+# ---- fp8 operands: the asynchronous GEMM's precision family -----------------------------
+# [SYNC-GEMM] 七: besides f16/bf16, the asynchronous GEMM takes fp8 operands (and fp4, and
+# block-scaled variants).  The product is the same D = A·B (+C) with fp32 C and D; the page
+# gives no shape table for these precisions.  Readings (also in the design notes):
+#
+# * A and B may each be e4m3 or e5m2, independently (mixed pairs included);
+# * M and N multiples of 16, K a multiple of 128: one 128-byte operand row of K per step of
+#   the kernel that serves it, in place of the synchronous GEMM's k16 / k8 atom rule;
+# * alpha = 1, beta in {0, 1}, and the transpose flags mean what they mean for the
+#   synchronous GEMM (stored orientation, normalised to A[M, K], B[K, N]).
+
+FP8_FORMATS = ("e4m3", "e5m2")
+
+
+def accepts_fp8(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+    """Acceptance of the fp8 GEMM.  Returns (ok, category) like accepts()."""
+    if min(M, N, K) < 0 or M % 16 or N % 16 or K % 128:
+        return False, "shape"
+    if (a_dtype not in FP8_FORMATS or b_dtype not in FP8_FORMATS or c_dtype != "f32"
+            or d_dtype != "f32"):
+        return False, "dtype"
+    if alpha != 1.0:
+        return False, "alpha"
+    if beta not in (0.0, 1.0):
+        return False, "beta"
+    return True, None
+
+
+def gemm_fp8_ref(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype, b_dtype):
+    """Full float64 D_ref = A·B (+ C when beta == 1) for fp8 operands (uint8 bit patterns)."""
+    ok, why = accepts_fp8(M, N, K, a_dtype, b_dtype, beta=beta)
+    if not ok:
+        raise ValueError(f"oracle: call rejected ({why})")
+    a_l, b_l = logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype)
+    d = np.matmul(a_l, b_l) if K else np.zeros((M, N))
+    if beta == 1.0:
+        d = d + np.asarray(c, dtype=np.float32).reshape(M, N).astype(np.float64)
+    return d
+
+
+def abs_bound_fp8(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype):
+    """sum_k |A_ik · B_kj| for every (i, j), float64, fp8 operands."""
+    a_l, b_l = logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype)
+    return np.matmul(np.abs(a_l), np.abs(b_l)) if K else np.zeros((M, N))
+
+
+def gemm_fp8_ref_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype, b_dtype, rows,
+                    cols, chunk=512):
+    """D_ref and the bound at sampled outputs for fp8 operands, one float64 dot each."""
+    ok, why = accepts_fp8(M, N, K, a_dtype, b_dtype, beta=beta)
+    if not ok:
+        raise ValueError(f"oracle: call rejected ({why})")
+    return _dots_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype, b_dtype, rows,
+                    cols, chunk)
 
 
 def tolerance(bound):

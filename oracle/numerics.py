@@ -1,4 +1,4 @@
-"""Exact decoding of 16-bit floating-point bit patterns (oracle; test infrastructure).
+"""Exact decoding of 16- and 8-bit floating-point bit patterns (oracle; test infrastructure).
 
 [SYNC-GEMM] 二 (What it accepts): A and B are both float16 or both bfloat16,
 C and D are float32.  The oracle receives A and B as the raw uint16 bit patterns
@@ -6,8 +6,10 @@ the GPU receives, and decodes them to float64.  Both formats embed exactly in
 float64, so the decode is exact (subnormals included).
 
 Pinned by tests/test_oracle_numerics.py: exhaustive comparison of all 65 536
-patterns of each format with a sign/exponent/mantissa formula written in the
-test from the IEEE-754 binary16 and the bfloat16 definitions.
+patterns of each 16-bit format with a sign/exponent/mantissa formula written in
+the test from the IEEE-754 binary16 and the bfloat16 definitions, and of all 256
+patterns of each 8-bit format with torch's own float8_e4m3fn / float8_e5m2 /
+float8_e8m0fnu conversions plus the formats' closed-form extremes.
 """
 
 import numpy as np
@@ -29,9 +31,54 @@ def bf16_bits_to_f64(bits):
 
 
 def decode(bits, dtype):
-    """Decode by format name: 'f16' or 'bf16'."""
+    """Decode by format name: 'f16', 'bf16', 'e4m3' or 'e5m2'."""
     if dtype == "f16":
         return f16_bits_to_f64(bits)
     if dtype == "bf16":
         return bf16_bits_to_f64(bits)
-    raise ValueError(f"oracle: unknown 16-bit format {dtype!r}")
+    if dtype in _FP8:
+        return fp8_bits_to_f64(bits, dtype)
+    raise ValueError(f"oracle: unknown format {dtype!r}")
+
+
+# ---- 8-bit formats of the asynchronous GEMM's precision family ------------------------
+# [SYNC-GEMM] 七 lists fp8 (and block-scaled variants with per-block scale factors) among
+# the asynchronous GEMM's operand precisions.  The formats are the OCP 8-bit floats:
+#
+#   e4m3 ("E4M3FN"): sign, 4 exponent bits (bias 7), 3 fraction bits.  No infinities; the
+#                    single pattern S.1111.111 is NaN, so the largest finite value is 448.
+#   e5m2:            sign, 5 exponent bits (bias 15), 2 fraction bits, IEEE-style: exponent
+#                    11111 is infinity (fraction 0) or NaN.
+#   e8m0:            the block scale: 8 exponent bits, bias 127, no sign and no fraction;
+#                    value 2^(E-127), and E = 255 is NaN.
+#
+# Every value embeds exactly in float64.
+
+_FP8 = {"e4m3": (4, 3), "e5m2": (5, 2)}
+
+
+def fp8_bits_to_f64(bits, fmt):
+    """OCP fp8 bit patterns (uint8 array) -> float64, exact.  fmt: 'e4m3' or 'e5m2'."""
+    if fmt not in _FP8:
+        raise ValueError(f"oracle: unknown 8-bit format {fmt!r}")
+    ebits, mbits = _FP8[fmt]
+    bias = (1 << (ebits - 1)) - 1
+    u = np.ascontiguousarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(u >> 7, -1.0, 1.0)
+    e = (u >> mbits) & ((1 << ebits) - 1)
+    m = u & ((1 << mbits) - 1)
+    normal = np.ldexp((1 << mbits) + m, e - bias - mbits)
+    sub = np.ldexp(m.astype(np.float64), 1 - bias - mbits)
+    v = sign * np.where(e == 0, sub, normal)
+    emax = (1 << ebits) - 1
+    if fmt == "e4m3":
+        v = np.where((e == emax) & (m == (1 << mbits) - 1), np.nan, v)
+    else:
+        v = np.where(e == emax, np.where(m == 0, sign * np.inf, np.nan), v)
+    return v
+
+
+def e8m0_bits_to_f64(bits):
+    """E8M0 block-scale patterns (uint8 array) -> float64: 2^(E-127), E = 255 is NaN."""
+    u = np.ascontiguousarray(bits, dtype=np.uint8).astype(np.int64)
+    return np.where(u == 255, np.nan, np.ldexp(1.0, u - 127))

@@ -16,6 +16,8 @@ Workloads (seeds are part of the recipe):
   gemm8k   A, B bf16 [8192,8192] N(0,1)/sqrt(K) (51, 52), beta=0, sample seed 53
   gemm8kh  A stored [K,M] f16 N(0,1)/sqrt(K) (54), B f16 [K,N] (55), C f32 U[-1,1] (56),
            transA, beta=1, sample seed 57
+  gemm8kf8 A e4m3 [8192,8192] N(0,1) (61), B e4m3 stored [N,K] N(0,1) (62), transB,
+           beta=0, sample seed 63
 """
 
 import numpy as np
@@ -47,6 +49,32 @@ def bf16_bits(x):
     u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
+
+
+_FP8_FIELDS = {"e4m3": (3, 7, 448.0), "e5m2": (2, 15, 57344.0)}   # fraction bits, bias, max
+
+
+def fp8_bits(x, fmt):
+    """float32 array -> OCP fp8 bit patterns ('e4m3' or 'e5m2'), round to nearest even.
+
+    Inputs must be finite and round to at most the format's largest finite value."""
+    mbits, bias, top = _FP8_FIELDS[fmt]
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                                   # a = f·2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, 1 - bias)                      # unbiased exponent, subnormals clamped
+    quantum = np.ldexp(1.0, e - mbits)
+    r = np.rint(a / quantum) * quantum                    # exact scaling; rint is half-even
+    if np.any(r > top):
+        raise ValueError(f"synth: value beyond the {fmt} range")
+    _, ex2 = np.frexp(r)
+    normal = r >= np.ldexp(1.0, 1 - bias)
+    e2 = np.where(normal, ex2 - 1, 1 - bias)
+    frac = np.where(normal, r / np.ldexp(1.0, e2) - 1.0, r / np.ldexp(1.0, 1 - bias))
+    field_e = np.where(normal, e2 + bias, 0).astype(np.int64)
+    field_m = np.rint(frac * (1 << mbits)).astype(np.int64)
+    sign = np.signbit(x).astype(np.int64)
+    return ((sign << 7) | (field_e << mbits) | field_m).astype(np.uint8)
 
 
 def bits16(x, fmt):
@@ -121,6 +149,21 @@ def gemm8k_f16_inputs(K=8192):
     s = float(1.0 / np.sqrt(K))
     return gemm_inputs(K, K, K, "f16", True, False, 1.0, (54, 55, 56), a_scale=s, b_scale=s,
                        c_dist="uniform")
+
+
+def gemm_fp8_inputs(M, N, K, a_fmt, b_fmt, trans_a, trans_b, beta, seeds, scale=1.0):
+    """fp8 bits of A and B (stored orientations), N(0, scale) before rounding, and C
+    (float32 U[-1, 1]) or None."""
+    sa, sb, sc = seeds
+    a = fp8_bits(normal(sa, M * K, scale), a_fmt).reshape((K, M) if trans_a else (M, K))
+    b = fp8_bits(normal(sb, K * N, scale), b_fmt).reshape((N, K) if trans_b else (K, N))
+    c = uniform(sc, M * N).reshape(M, N) if beta == 1.0 else None
+    return a, b, c
+
+
+def gemm8k_fp8_inputs(K=8192):
+    """A e4m3 [M, K] N(0,1) (61), B e4m3 stored [N, K] N(0,1) (62), beta = 0."""
+    return gemm_fp8_inputs(K, K, K, "e4m3", "e4m3", False, True, 0.0, (61, 62, 0))
 
 
 def copy32_input():

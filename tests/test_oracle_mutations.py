@@ -170,3 +170,101 @@ def test_layout_mutant_is_caught(kind, monkeypatch):
     checks += [lambda a=a: T.test_xor_layout_is_a_bijection_with_whole_chunks(*a) for a in T.TILES]
     checks += [lambda a=a: T.test_xor_layout_is_an_involution(*a) for a in T.TILES]
     assert any(_caught(lambda _: c(), None) for c in checks)
+
+
+# ---- fp8 GEMM and the 8-bit decoders ---------------------------------------------------
+
+def _mut_fp8_decode(kind):
+    from oracle.numerics import fp8_bits_to_f64
+
+    def fn(bits, fmt):
+        u = np.asarray(bits, np.uint8).astype(np.int64)
+        if kind == "fnuz_bias":            # e4m3 read with the bias of the FNUZ variant
+            v = fp8_bits_to_f64(bits, fmt)
+            return v / 2.0 if fmt == "e4m3" else v
+        if kind == "e4m3_ieee_specials":  # e4m3 given infinities like e5m2
+            v = fp8_bits_to_f64(bits, fmt)
+            if fmt == "e4m3":
+                e, m = (u >> 3) & 15, u & 7
+                v = np.where(e == 15, np.where(m == 0, np.where(u >> 7, -np.inf, np.inf), np.nan), v)
+            return v
+        if kind == "no_subnormals":        # exponent 0 read as a normal number
+            ebits, mbits = (4, 3) if fmt == "e4m3" else (5, 2)
+            bias = (1 << (ebits - 1)) - 1
+            v = fp8_bits_to_f64(bits, fmt)
+            e = (u >> mbits) & ((1 << ebits) - 1)
+            m = u & ((1 << mbits) - 1)
+            sub = np.where(u >> 7, -1.0, 1.0) * np.ldexp((1 << mbits) + m, -bias - mbits)
+            return np.where((e == 0) & (m != 0), sub, v)
+        if kind == "e5m2_inf_as_nan":
+            v = fp8_bits_to_f64(bits, fmt)
+            return np.where(np.isinf(v), np.nan, v) if fmt == "e5m2" else v
+        if kind == "lost_sign_of_zero":
+            v = fp8_bits_to_f64(bits, fmt)
+            return np.where(v == 0, 0.0, v)
+        raise AssertionError(kind)
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["fnuz_bias", "e4m3_ieee_specials", "no_subnormals",
+                                  "e5m2_inf_as_nan", "lost_sign_of_zero"])
+def test_fp8_decoder_mutant_is_caught(kind):
+    assert _caught(pins.pin_fp8_decode, _mut_fp8_decode(kind))
+
+
+def _mut_fp8_gemm(kind):
+    def fn(a_bits, b_bits, c, M, N, K, ta, tb, beta, a_fmt, b_fmt):
+        if kind == "b_in_a_format":
+            b_fmt = a_fmt
+        if kind == "formats_swapped":
+            a_fmt, b_fmt = b_fmt, a_fmt
+        a = decode(a_bits, a_fmt).reshape((K, M) if ta else (M, K))
+        b = decode(b_bits, b_fmt).reshape((N, K) if tb else (K, N))
+        a_l = a.T if ta else a
+        b_l = b.T if tb else b
+        if kind == "ignore_trans_b":
+            b_l = decode(b_bits, b_fmt).reshape(K, N)
+        if kind == "half_k" and K:
+            a_l = a_l[:, :K // 2]
+            b_l = b_l[:K // 2, :]
+        d = a_l @ b_l if a_l.shape[1] else np.zeros((M, N))
+        if kind == "saturate_products":
+            d = np.clip(d, -448.0, 448.0)
+        if beta == 1.0 and kind != "beta_ignored":
+            d = d + np.asarray(c, np.float32).reshape(M, N).astype(np.float64)
+        return d
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["b_in_a_format", "formats_swapped", "ignore_trans_b", "half_k",
+                                  "saturate_products", "beta_ignored"])
+def test_fp8_gemm_mutant_is_caught(kind):
+    fn = _mut_fp8_gemm(kind)
+    assert any(_caught(p, fn) for p in pins.FP8_GEMM_PINS)
+
+
+def test_fp8_acceptance_mutants_are_caught():
+    from tests.test_oracle_gemm_fp8 import test_acceptance_table as t
+    params = [m for m in t.pytestmark if m.name == "parametrize"][0].args[1]
+
+    def run(accepts_fn):
+        for args, cat in params:
+            ok, why = accepts_fn(**args)
+            assert ok == (cat is None) and why == cat
+
+    def k64(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+        return G.accepts_fp8(M, N, K - K % 128 if K % 64 == 0 else K, a_dtype, b_dtype, c_dtype,
+                             d_dtype, alpha, beta)
+
+    def n8(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+        return G.accepts_fp8(M, N - N % 16 if N % 8 == 0 else N, K, a_dtype, b_dtype, c_dtype,
+                             d_dtype, alpha, beta)
+
+    def any16(M, N, K, a_dtype, b_dtype, c_dtype="f32", d_dtype="f32", alpha=1.0, beta=0.0):
+        fix = {"f16": "e4m3", "bf16": "e5m2"}
+        return G.accepts_fp8(M, N, K, fix.get(a_dtype, a_dtype), fix.get(b_dtype, b_dtype),
+                             c_dtype, d_dtype, alpha, beta)
+
+    run(G.accepts_fp8)
+    for mutant in (k64, n8, any16):
+        assert _caught(run, mutant)

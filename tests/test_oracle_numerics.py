@@ -5,7 +5,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle.numerics import bf16_bits_to_f64, f16_bits_to_f64
+from oracle.numerics import bf16_bits_to_f64, e8m0_bits_to_f64, f16_bits_to_f64, fp8_bits_to_f64
+from tests import pins
 
 
 def ieee_value(bits, exp_bits, man_bits):
@@ -44,3 +45,36 @@ def test_decode_spot_values():
     assert bf16_bits_to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
     assert bf16_bits_to_f64(np.array([0xC040], np.uint16))[0] == -3.0
     assert bf16_bits_to_f64(np.array([0x0001], np.uint16))[0] == 2.0 ** -133
+
+
+def test_fp8_decode_against_torch_and_extremes():
+    pins.pin_fp8_decode(fp8_bits_to_f64)
+
+
+def test_e8m0_decode_against_torch():
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(bits).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = e8m0_bits_to_f64(bits)
+    assert np.array_equal(got[:255], want[:255]) and np.isnan(got[255]) and np.isnan(want[255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_synth_fp8_encoder_round_trips_and_rounds_to_nearest_even():
+    import synth
+    for fmt in ("e4m3", "e5m2"):
+        bits = np.arange(256, dtype=np.uint8)
+        vals = fp8_bits_to_f64(bits, fmt)
+        finite = np.isfinite(vals)
+        enc = synth.fp8_bits(vals[finite].astype(np.float32), fmt)
+        # every finite value encodes to its own pattern (-0 included)
+        assert np.array_equal(enc, bits[finite])
+        # midpoints of adjacent positive values round to the one with an even fraction
+        pos = np.sort(np.unique(vals[finite & (vals >= 0)]))
+        mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+        exact_mid = mid.astype(np.float64) == (pos[:-1] + pos[1:]) / 2
+        got = fp8_bits_to_f64(synth.fp8_bits(mid[exact_mid], fmt), fmt)
+        lo, hi = pos[:-1][exact_mid], pos[1:][exact_mid]
+        lo_bits = synth.fp8_bits(lo.astype(np.float32), fmt)
+        want = np.where(lo_bits % 2 == 0, lo, hi)
+        assert np.array_equal(got, want), fmt
