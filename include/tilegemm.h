@@ -36,8 +36,8 @@
 extern "C" {
 #endif
 
-/* Element formats.  GEMM operands A and B take TG_F16 or TG_BF16; copies move
- * any of them as raw bits. */
+/* Element formats.  tile_gemm operands take TG_F16 or TG_BF16, tile_gemm_fp8 operands
+ * TG_FP8_E4M3 or TG_FP8_E5M2; copies move any of them as raw bits. */
 typedef enum tg_dtype {
   TG_F16 = 1,       /* IEEE binary16 */
   TG_BF16 = 2,      /* bfloat16 */
@@ -114,7 +114,8 @@ typedef struct tg_copy_plan {
 typedef enum tg_gemm_kernel {
   TG_GEMM_NONE = 0,     /* nothing to launch (M == 0 or N == 0) */
   TG_GEMM_ATOM = 1,     /* register kernel: one wave per 16x16 output tile, v_mfma_f32_16x16x32 */
-  TG_GEMM_TILED = 2,    /* LDS double-buffered kernel, v_mfma_f32_32x32x16 */
+  TG_GEMM_TILED = 2,    /* LDS double-buffered kernel, v_mfma_f32_32x32x16 (fp8:
+                           v_mfma_f32_32x32x64_f8f6f4) */
   TG_GEMM_FILL = 3      /* K == 0: D = beta*C without a product */
 } tg_gemm_kernel;
 
@@ -164,6 +165,37 @@ int tile_gemm(const void* A, const void* B, const float* C, float* D,
 int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D,
                    int64_t M, int64_t N, int64_t K, int transA, int transB,
                    float beta, int dtype, tg_gemm_plan* out);
+
+/*
+ * tile_gemm_fp8 — D = A·B + beta·C with 8-bit floating-point operands: the fp8 member of the
+ * asynchronous GEMM's precision family ([SYNC-GEMM] 七: besides f16/bf16 it takes fp8 and
+ * fp4 operands, with A and B staged in shared memory and the product accumulated in fp32).
+ *
+ *   A      device, OCP fp8 of format a_dtype, stored row-major [M,K] (transA == 0).
+ *   B      device, OCP fp8 of format b_dtype, stored row-major [N,K] (transB == 1).
+ *          Both operands are read K-contiguous; transA == 1 or transB == 0 -> TG_E_LAYOUT.
+ *   C, D   as tile_gemm: fp32 [M,N] row-major packed, C read only when beta == 1, C may be
+ *          exactly D, D must not overlap A or B.
+ *   M,N,K  M % 16 == 0, N % 16 == 0, K % 128 == 0, all >= 0, and each operand under 2 GiB;
+ *          otherwise TG_E_SHAPE.  M == 0 or N == 0 is a no-op; K == 0 gives D = beta·C.
+ *   beta   exactly 0.0 or 1.0 (alpha is fixed at 1); otherwise TG_E_BETA.
+ *   a_dtype, b_dtype   each TG_FP8_E4M3 (e4m3fn: bias 7, largest finite 448, no infinities,
+ *          S.1111.111 is NaN) or TG_FP8_E5M2 (bias 15, IEEE-style infinities and NaNs); the
+ *          two may differ.  Anything else -> TG_E_DTYPE.  Every product of two fp8 values is
+ *          exact in fp32; products are accumulated in fp32 by MFMA.  No block scales (the
+ *          scaled variants of the page are a separate entry point).
+ *   Alignment: A and B 16-byte aligned, C and D 4-byte aligned; otherwise TG_E_ALIGN.
+ * Returns TG_OK or a tg_status; asynchronous on `stream`.
+ */
+int tile_gemm_fp8(const void* A, const void* B, const float* C, float* D,
+                  int64_t M, int64_t N, int64_t K, int transA, int transB,
+                  float beta, int a_dtype, int b_dtype, void* stream);
+
+/* tile_gemm_fp8_plan — host-only validation and kernel choice of tile_gemm_fp8 (as
+ * tile_gemm_plan).  Needs no GPU. */
+int tile_gemm_fp8_plan(const void* A, const void* B, const float* C, const float* D,
+                       int64_t M, int64_t N, int64_t K, int transA, int transB,
+                       float beta, int a_dtype, int b_dtype, tg_gemm_plan* out);
 
 /*
  * tile_copy — bit-exact copy of a shape[0] x shape[1] matrix from src to dst, staged
@@ -219,7 +251,7 @@ int tile_copy_partition(int64_t rows, int64_t cols, int elem_bits, int threads,
 /* Reason for the last failure on the calling thread ("" after a success). */
 const char* tile_last_error(void);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan). */
 int tile_abi_version(void);
 
 #ifdef __cplusplus

@@ -30,11 +30,13 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"tile_gemm", "tile_copy", "tile_copy_ex", "tile_copy_plan", "tile_gemm_plan",
-            "tile_copy_partition", "tile_last_error", "tile_abi_version"} <= set(names)
+            "tile_gemm_fp8", "tile_gemm_fp8_plan", "tile_copy_partition", "tile_last_error",
+            "tile_abi_version"} <= set(names)
     lib = tg.lib()
     for n in names:
         assert hasattr(lib, n), n
-    assert tg.tile_abi_version() == 1
+        assert n in tg._SIGS, n   # the binding marshals every declared entry point
+    assert tg.tile_abi_version() == 2
 
 
 # ------------------------------------------------------------- planner ----
@@ -246,4 +248,64 @@ def test_gemm_kernel_choice():
     p = tg.tile_gemm_plan(None, None, None, D_ADDR, 16, 8, 0, 0, 0, 0.0, tg.TG_F16)
     assert p.kernel == tg.TG_GEMM_FILL
     p = tg.tile_gemm_plan(None, None, None, None, 0, 8, 16, 0, 0, 0.0, tg.TG_F16)
+    assert p.kernel == tg.TG_GEMM_NONE
+
+
+# ------------------------------------------------------------ fp8 GEMM ----
+
+ODT8 = {tg.TG_FP8_E4M3: "e4m3", tg.TG_FP8_E5M2: "e5m2", tg.TG_F16: "f16", tg.TG_BF16: "bf16"}
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (8, 16, 128), (16, 8, 128), (16, 16, 64),
+                                   (16, 16, 192), (0, 16, 128), (16, 16, 0), (-16, 16, 128),
+                                   (272, 528, 384), (8192, 8192, 8192)])
+@pytest.mark.parametrize("a_dt,b_dt", [(tg.TG_FP8_E4M3, tg.TG_FP8_E4M3), (tg.TG_FP8_E5M2, tg.TG_FP8_E4M3),
+                                       (tg.TG_FP8_E4M3, tg.TG_F16), (tg.TG_BF16, tg.TG_FP8_E5M2),
+                                       (tg.TG_I8, tg.TG_FP8_E4M3)])
+@pytest.mark.parametrize("beta", [0.0, 1.0, 0.5])
+def test_fp8_validation_matches_oracle(M, N, K, a_dt, b_dt, beta):
+    want = ogemm.accepts_fp8(M, N, K, ODT8.get(a_dt, "other"), ODT8.get(b_dt, "other"), beta=beta)
+    try:
+        tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, C_ADDR, D_ADDR, M, N, K, 0, 1, beta, a_dt, b_dt)
+        got = (True, None)
+    except tg.TileError as e:
+        got = (False, CATEGORY.get(e.status, "other"))
+    assert got == want
+
+
+def test_fp8_layouts_and_errors_need_no_gpu():
+    e4 = tg.TG_FP8_E4M3
+    for ta, tb in ((1, 1), (0, 0), (1, 0)):
+        with pytest.raises(tg.TileError) as e:
+            tg.tile_gemm_fp8(A_ADDR, B_ADDR, None, D_ADDR, 256, 256, 256, ta, tb, 0.0, e4, e4)
+        assert e.value.status == tg.TG_E_LAYOUT and "K-contiguous" in e.value.reason
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm_fp8(A_ADDR, B_ADDR, None, D_ADDR, 256, 256, 256, 0, 2, 0.0, e4, e4)
+    assert e.value.status == tg.TG_E_ARG
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm_fp8(A_ADDR + 8, B_ADDR, None, D_ADDR, 256, 256, 256, 0, 1, 0.0, e4, e4)
+    assert e.value.status == tg.TG_E_ALIGN
+    with pytest.raises(tg.TileError) as e:   # D overlaps B (one-byte elements: N*K bytes)
+        tg.tile_gemm_fp8(A_ADDR, B_ADDR, None, B_ADDR + 256 * 256 - 4, 256, 256, 256, 0, 1, 0.0, e4, e4)
+    assert e.value.status == tg.TG_E_ALIAS
+    # D just past the end of B (N*K bytes) does not overlap
+    tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, B_ADDR + 256 * 256, 256, 256, 256, 0, 1, 0.0, e4, e4)
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm_fp8(A_ADDR, B_ADDR, None, D_ADDR, 256, 256, 256, 0, 1, 1.0, e4, e4)
+    assert e.value.status == tg.TG_E_NULL
+    with pytest.raises(tg.TileError) as e:   # an operand of 2 GiB
+        tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 16384, 256, 131072, 0, 1, 0.0, e4, e4)
+    assert e.value.status == tg.TG_E_SHAPE and "2 GiB" in e.value.reason
+
+
+def test_fp8_kernel_choice():
+    e4, e5 = tg.TG_FP8_E4M3, tg.TG_FP8_E5M2
+    p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 8192, 8192, 8192, 0, 1, 0.0, e4, e4)
+    assert (p.kernel, p.block_m, p.block_n, p.block_k, p.threads, p.grid, p.bounds_checked,
+            p.loader) == (tg.TG_GEMM_TILED, 256, 256, 128, 512, 1024, 0, 1)
+    p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, C_ADDR, D_ADDR, 272, 528, 384, 0, 1, 1.0, e5, e4)
+    assert (p.kernel, p.grid, p.bounds_checked) == (tg.TG_GEMM_TILED, 6, 1)
+    p = tg.tile_gemm_fp8_plan(None, None, C_ADDR, D_ADDR, 16, 16, 0, 0, 1, 1.0, e4, e5)
+    assert p.kernel == tg.TG_GEMM_FILL
+    p = tg.tile_gemm_fp8_plan(None, None, None, None, 0, 16, 128, 0, 1, 0.0, e4, e4)
     assert p.kernel == tg.TG_GEMM_NONE

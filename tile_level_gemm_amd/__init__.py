@@ -83,6 +83,10 @@ _SIGS = {
     "tile_gemm": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT, _VP]),
     "tile_gemm_plan": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT,
                               ctypes.POINTER(GemmPlan)]),
+    "tile_gemm_fp8": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT, _INT,
+                             _VP]),
+    "tile_gemm_fp8_plan": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT,
+                                  _INT, ctypes.POINTER(GemmPlan)]),
     "tile_copy": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
                          ctypes.POINTER(Layout), _VP]),
     "tile_copy_ex": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
@@ -186,6 +190,21 @@ def gemm(A, B, C=None, beta=0.0, trans_a=False, trans_b=False, alpha=1.0, out=No
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     tile_gemm(A, B, C, out, M, N, K, trans_a, trans_b, beta, TORCH_DTYPES[A.dtype], stream)
+    return out
+
+
+def tile_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype, stream=None):
+    """D = A·B + beta·C with fp8 operands through the library (see include/tilegemm.h)."""
+    _check(lib().tile_gemm_fp8(_addr(A), _addr(B), _addr(C), _addr(D), M, N, K, int(transA),
+                               int(transB), float(beta), int(a_dtype), int(b_dtype),
+                               _stream(stream)))
+
+
+def tile_gemm_fp8_plan(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype):
+    out = GemmPlan()
+    _check(lib().tile_gemm_fp8_plan(_addr(A), _addr(B), _addr(C), _addr(D), M, N, K, int(transA),
+                                    int(transB), float(beta), int(a_dtype), int(b_dtype),
+                                    ctypes.byref(out)))
     return out
 
 

@@ -17,7 +17,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilegemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "plan.cpp", "copy_kernels.hip", "gemm_kernels.hip", "gemm_direct.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "copy_kernels.hip", "gemm_kernels.hip", "gemm_direct.hip",
+           "gemm_fp8.hip"]
 
 # -packed-fp32-ops: no v_pk_*_f32 in generated code (the device pass honours it; the
 # host pass warns that it does not know the feature).

@@ -79,6 +79,67 @@ int validate_gemm(const void* A, const void* B, const float* C, const float* D, 
   return TG_OK;
 }
 
+bool is_fp8(int dtype) { return dtype == TG_FP8_E4M3 || dtype == TG_FP8_E5M2; }
+
+// tile_gemm_fp8 ([SYNC-GEMM] 七, the fp8 operands of the asynchronous GEMM): same checks
+// and order as validate_gemm, with the fp8 shape rule (M % 16, N % 16, K % 128), the fp8
+// formats, one-byte operand elements and the K-contiguous orientations.
+int validate_gemm_fp8(const void* A, const void* B, const float* C, const float* D, int64_t M,
+                      int64_t N, int64_t K, int transA, int transB, float beta, int a_dtype,
+                      int b_dtype) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(TG_E_SHAPE, fmt("negative extent (M=%lld, N=%lld, K=%lld)", M, N, K));
+  if (M % 16 || N % 16 || K % 128)
+    return fail(TG_E_SHAPE,
+                fmt("fp8 gemm needs M %% 16 == 0, N %% 16 == 0, K %% 128 == 0 (got M=%lld, N=%lld, "
+                    "K=%lld)", M, N, K));
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(TG_E_SHAPE, "extent above 2^30");
+  if (M * K >= ((int64_t)1 << 31) || N * K >= ((int64_t)1 << 31))
+    return fail(TG_E_SHAPE, "fp8 gemm needs each operand under 2 GiB (32-bit buffer offsets)");
+  if (!is_fp8(a_dtype) || !is_fp8(b_dtype))
+    return fail(TG_E_DTYPE, fmt("fp8 gemm operands must be TG_FP8_E4M3 or TG_FP8_E5M2 (got a_dtype "
+                                "%lld, b_dtype %lld); C and D are fp32", a_dtype, b_dtype));
+  if (transA != 0 && transA != 1) return fail(TG_E_ARG, "transA must be 0 or 1");
+  if (transB != 0 && transB != 1) return fail(TG_E_ARG, "transB must be 0 or 1");
+  if (transA != 0 || transB != 1)
+    return fail(TG_E_LAYOUT, "fp8 gemm reads both operands K-contiguous: A stored [M,K] "
+                             "(transA = 0) and B stored [N,K] (transB = 1)");
+  if (!(beta == 0.0f || beta == 1.0f))
+    return fail(TG_E_BETA, "beta must be exactly 0.0 or 1.0 (alpha is fixed at 1)");
+  if (M == 0 || N == 0) return TG_OK;
+  if (!D) return fail(TG_E_NULL, "D is NULL");
+  if (beta == 1.0f && !C) return fail(TG_E_NULL, "beta == 1 needs C");
+  if (K > 0 && (!A || !B)) return fail(TG_E_NULL, "A or B is NULL");
+  const int64_t dbytes = M * N * 4;
+  if (K > 0) {
+    if (overlaps(D, dbytes, A, M * K) || overlaps(D, dbytes, B, K * N))
+      return fail(TG_E_ALIAS, "D overlaps A or B");
+    if ((uintptr_t)A % 16 || (uintptr_t)B % 16)
+      return fail(TG_E_ALIGN, "A and B must be 16-byte aligned for 128-bit operand loads");
+  }
+  if (beta == 1.0f && C != D && overlaps(D, dbytes, C, dbytes))
+    return fail(TG_E_ALIAS, "C overlaps D without being exactly D");
+  if ((uintptr_t)D % 4 || (beta == 1.0f && (uintptr_t)C % 4))
+    return fail(TG_E_ALIGN, "C and D must be 4-byte aligned");
+  return TG_OK;
+}
+
+void fill_plan(const GemmConfig& c, tg_gemm_plan* out) {
+  out->kernel = c.kernel;
+  out->block_m = c.bm;
+  out->block_n = c.bn;
+  out->block_k = c.bk;
+  out->wave_m = c.wm;
+  out->wave_n = c.wn;
+  out->threads = c.threads;
+  out->bounds_checked = c.bounds;
+  out->lds_bytes = c.lds_bytes;
+  out->grid = c.grid;
+  out->loader = c.direct;
+  out->reserved = 0;
+}
+
 bool valid_kind(int k) { return k == TG_ROW_MAJOR || k == TG_COL_MAJOR || k == TG_XOR_SWIZZLE; }
 
 // Validates a copy and fills the plan and launch arguments.
@@ -230,7 +291,7 @@ extern "C" {
 
 const char* tile_last_error(void) { return g_last_error.c_str(); }
 
-int tile_abi_version(void) { return 1; }
+int tile_abi_version(void) { return 2; }
 
 int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D, int64_t M,
                    int64_t N, int64_t K, int transA, int transB, float beta, int dtype,
@@ -239,19 +300,7 @@ int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D,
   if (!out) return fail(TG_E_ARG, "out is NULL");
   int st = validate_gemm(A, B, C, D, M, N, K, transA, transB, beta, dtype);
   if (st) return st;
-  const GemmConfig c = choose_gemm(M, N, K);
-  out->kernel = c.kernel;
-  out->block_m = c.bm;
-  out->block_n = c.bn;
-  out->block_k = c.bk;
-  out->wave_m = c.wm;
-  out->wave_n = c.wn;
-  out->threads = c.threads;
-  out->bounds_checked = c.bounds;
-  out->lds_bytes = c.lds_bytes;
-  out->grid = c.grid;
-  out->loader = c.direct;
-  out->reserved = 0;
+  fill_plan(choose_gemm(M, N, K), out);
   return TG_OK;
 }
 
@@ -277,6 +326,45 @@ int tile_gemm(const void* A, const void* B, const float* C, float* D, int64_t M,
     g.tiles_n = (int32_t)((N + cfg.bn - 1) / cfg.bn);
   }
   return launch_gemm(g, cfg, transA, transB, dtype, stream);
+}
+
+int tile_gemm_fp8_plan(const void* A, const void* B, const float* C, const float* D, int64_t M,
+                       int64_t N, int64_t K, int transA, int transB, float beta, int a_dtype,
+                       int b_dtype, tg_gemm_plan* out) {
+  clear_error();
+  if (!out) return fail(TG_E_ARG, "out is NULL");
+  int st = validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
+  if (st) return st;
+  fill_plan(choose_gemm_fp8(M, N, K), out);
+  return TG_OK;
+}
+
+int tile_gemm_fp8(const void* A, const void* B, const float* C, float* D, int64_t M, int64_t N,
+                  int64_t K, int transA, int transB, float beta, int a_dtype, int b_dtype,
+                  void* stream) {
+  clear_error();
+  int st = validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
+  if (st) return st;
+  const GemmConfig cfg = choose_gemm_fp8(M, N, K);
+  if (cfg.kernel == TG_GEMM_NONE) return TG_OK;
+  if (cfg.kernel == TG_GEMM_FILL && beta == 1.0f && C == D) return TG_OK;
+  GemmArgs g{};
+  g.A = (const uint16_t*)A;
+  g.B = (const uint16_t*)B;
+  g.C = beta == 1.0f ? C : nullptr;
+  g.D = D;
+  g.M = (int32_t)M;
+  g.N = (int32_t)N;
+  g.K = (int32_t)K;
+  g.use_c = beta == 1.0f;
+  if (cfg.kernel == TG_GEMM_FILL) return launch_gemm(g, cfg, 0, 0, TG_BF16, stream);
+  g.tiles_m = (int32_t)((M + 255) / 256);
+  g.tiles_n = (int32_t)((N + 255) / 256);
+  const hipError_t e = launch_gemm_fp8(g, cfg.grid, a_dtype, b_dtype, cfg.bounds != 0,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(TG_E_HIP, std::string("tile_gemm_fp8 launch: ") + hipGetErrorString(e));
+  return TG_OK;
 }
 
 int tile_copy_plan(const void* src, const void* dst, const int64_t shape[2], int dtype,

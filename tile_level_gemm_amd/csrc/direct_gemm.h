@@ -1,0 +1,544 @@
+// Large-tile GEMM on gfx950 with direct global -> LDS operand loads (kernel template).
+//
+// Same contract as gemm_tiled ([SYNC-GEMM] "TVM TIRx 同步 GEMM 深度解析…": D = A·B (+C),
+// fp32 accumulation in place over K, 二 / 四 step 3), for 256x256 blocks.  The template
+// serves the 16-bit operands of the synchronous GEMM and the fp8 operands of the
+// asynchronous GEMM's precision family (七: A and B staged in shared memory, fp8 among the
+// operand formats).  What the kernel does:
+//
+//  * global -> LDS with buffer_load_dwordx4 ... lds: each instruction moves 64 lanes x 16 bytes
+//    and lane i's bytes land at LDS base + 16·i, so no VGPR staging and no ds_write.  The
+//    LDS swizzle is applied on the global side: lane i fetches the logical 16-byte chunk
+//    that belongs at physical slot i.
+//  * one K stage is one 128-byte row of K per operand row: 64 K of a 16-bit operand, 128 K of
+//    an fp8 operand.  Both formats therefore share the LDS geometry, the DMA pattern and the
+//    bytes per stage; a stage is 4 MFMA K steps of 16 (v_mfma_f32_32x32x16_{f16,bf16}) or 2
+//    of 64 (v_mfma_f32_32x32x64_f8f6f4), the same MFMA cycles either way.
+//  * K-contiguous operands (A without transA, B with transB) keep [rows][128 bytes] stages
+//    (chunk XOR row bits) and are read as fragments with ds_read_b128: one per 16-bit
+//    fragment, two per fp8 fragment (32 bytes of K per lane).
+//  * M/N-contiguous 16-bit operands (A with transA, B without transB) keep the global
+//    orientation, [64 k][256 mn] stages of 512-byte rows, and are read with
+//    ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j%4 of the 8-byte
+//    reads of lanes 4q + j/4 (q = 0..3), so if lane i reads 4 consecutive mn at k-row
+//    k0 + i/4 and column block i%4, lane j receives k0..k0+3 at mn0 + j — four K-consecutive
+//    values, half of an MFMA fragment.
+//  * the K loop is unrolled by two so each half names its LDS stage at compile time; the
+//    next stage's loads are issued at the top of an iteration and the next K step's
+//    fragments are read while the current step's MFMAs run.
+//
+// Internal header: included by gemm_direct.hip (16-bit instantiations) and gemm_fp8.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "tg_internal.h"
+
+namespace tg {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(8))) uint32_t u32x8;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int BM = 256, BN = 256;
+constexpr int kRowBytes = 128;   // bytes of K per operand row and stage
+constexpr int kGroupM = 8;       // tile-rows per scheduling group (measured: 8 beats 2, 4, 16)
+
+// Format codes of the template's DT parameter: TG_F16 / TG_BF16, or an fp8 pair
+// kF8 + 2·a + b with a, b the MFMA's operand format codes (0 = e4m3, 1 = e5m2).
+constexpr int kF8 = 16;
+constexpr int fp8_code(int a_fmt, int b_fmt) { return kF8 + 2 * a_fmt + b_fmt; }
+
+template <int DT>
+struct Elem {
+  static constexpr bool kFp8 = DT >= kF8;
+  static constexpr int kBytes = kFp8 ? 1 : 2;
+  static constexpr int kBK = kRowBytes / kBytes;   // K elements per stage
+  static constexpr int kSteps = kFp8 ? 2 : 4;      // MFMA K steps per stage
+  static constexpr int kParts = kFp8 ? 2 : 1;      // 16-byte K-major reads per fragment
+  using Frag = typename std::conditional<kFp8, u32x8, u32x4>::type;
+};
+
+template <int DT, class F>
+__device__ __forceinline__ f32x16 mfma32(F a, F b, f32x16 c) {
+  if constexpr (DT == TG_F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else if constexpr (DT == TG_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    // cbsz / blgp name A's and B's formats; no block scales (scale operands 0).  Lane l
+    // carries 32 bytes of K of row / column l % 32; A and B put the same K in the same byte,
+    // so the sum is over matching K whatever order the unit reduces them in.
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, (DT - kF8) >> 1,
+        (DT - kF8) & 1, 0, 0, 0, 0);
+}
+
+// ---- LDS layouts --------------------------------------------------------------------
+// K-major stage: 256 rows x 128 bytes; physical chunk = kc ^ sk(row).
+//   SK 0: row & 7 — eight consecutive rows hit eight chunks (32 four-byte banks);
+//   SK 1: (row & 7) ^ ((row >> 3) & 1) — also sixteen consecutive rows hit sixteen distinct
+//         (row parity, chunk) pairs, i.e. distinct banks if the LDS has 64 banks.
+template <int SK>
+__device__ __forceinline__ uint32_t sk(uint32_t r) {
+  if constexpr (SK == 0) return r & 7u;
+  else return (r & 7u) ^ ((r >> 3) & 1u);
+}
+// M/N-major stage: 64 k-rows x 512 bytes (32 chunks); physical chunk = c ^ sm(k).  A
+// transposing read touches 32 bytes (2 chunks) in each of 4 consecutive k-rows per 16 lanes.
+//   SM 0: 2(k & 3) — the four rows land in four distinct 32-byte bank slots of 128 bytes;
+//   SM 1: 2(k & 3) ^ 8(k & 1) — additionally, two adjacent 16-lane groups (mn + 16) land
+//         in eight distinct slots of 256 bytes.
+template <int SM>
+__device__ __forceinline__ uint32_t sm(uint32_t k) {
+  if constexpr (SM == 0) return (k & 3u) << 1;
+  else return ((k & 3u) << 1) ^ ((k & 1u) << 3);
+}
+
+// ---- per-lane offsets, computed once ---------------------------------------------------
+// Every address below is a per-lane offset computed before the K loop plus compile-time
+// immediates (tile, K step, stage), so the loop keeps few address registers.
+constexpr int SKV = 1, SMV = 1;   // swizzle variants in use (see sk / sm)
+
+// DMA (global -> LDS) for a K-major operand: PER instructions per wave per stage; instruction
+// i writes 1 KiB block b = PER·wave + i = rows 8b .. 8b+7.  Lane l fills physical slot l%8
+// of row 8b + l/8 and so fetches logical chunk (l%8) ^ sk(row).  sk(row) depends on the
+// lane and on i's parity only (PER is even), so two byte offsets cover all instructions.
+template <int PER, int E>
+__device__ __forceinline__ void km_dma_offsets(int64_t ld, int wave, int lane, uint32_t (&off)[2]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t r = (uint32_t)(8 * PER * wave + 8 * p + (lane >> 3));
+    const uint32_t kc = ((uint32_t)lane & 7u) ^ sk<SKV>(r);
+    if constexpr (E == 2) off[p] = (r * (uint32_t)ld + kc * 8u) * 2u;   // bytes; < 256·K·2 < 2^32
+    else off[p] = r * (uint32_t)ld + kc * 16u;                          // bytes; < 256·K < 2^32
+  }
+}
+// DMA for an M/N-major 16-bit operand: instruction i writes block b = PER·wave + i = k-rows
+// 2b, 2b+1; lane l fills slot l%32 of k-row 2b + l/32, logical chunk (l%32) ^ sm(k); sm
+// depends on k & 3, i.e. on the lane and i's parity.
+template <int PER>
+__device__ __forceinline__ void mn_dma_offsets(int64_t ld, int wave, int lane, uint32_t (&off)[2]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t k = (uint32_t)(2 * PER * wave + 2 * p + (lane >> 5));
+    const uint32_t c = ((uint32_t)lane & 31u) ^ sm<SMV>(k);
+    off[p] = (k * (uint32_t)ld + c * 8u) * 2u;    // bytes; < 64·N·2 < 2^32
+  }
+}
+
+// K-major fragment reads (ds_read_b128) of 32-row tile t: lane l reads row base + 32t + l%32.
+// 16-bit, K step s: chunk 2s + l/32 (offset u = s).  fp8, K step s: chunks 4s + 2(l/32) + q
+// for q = 0, 1 (offsets u = 2s + q) — 32 bytes of K per lane.  sk(row) depends on the lane
+// only (32t is a multiple of 16), the chunk term on u: one byte offset per u; tiles are
+// +4096-byte immediates.
+template <bool FP8>
+__device__ __forceinline__ void km_frag_offsets(int row_base, int lane, uint32_t (&off)[4]) {
+  const uint32_t r = (uint32_t)(row_base + (lane & 31));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t kc = FP8 ? (uint32_t)(4 * (u >> 1) + 2 * (lane >> 5) + (u & 1))
+                            : (uint32_t)(2 * u + (lane >> 5));
+    off[u] = r * 128u + ((kc ^ sk<SKV>(r)) << 4);
+  }
+}
+// M/N-major fragment of 32-column tile t, K step s, half h (two ds_read_b64_tr_b16): lane
+// l = 16g + j supplies k-row 16s + 8(g/2) + 4h + j/4 and columns mn_base + 32t + 16(g&1) +
+// 4(j&3) .. +3.  sm(k) depends on j only; its bits 2-3 XOR with the tile index, so one byte
+// offset per tile t; s and h are immediates (16s + 4h rows of 512 bytes).
+template <int T>
+__device__ __forceinline__ void mn_frag_offsets(int mn_base, int lane, uint32_t (&off)[4]) {
+  const uint32_t g = (uint32_t)lane >> 4, j = (uint32_t)lane & 15u;
+  const uint32_t krow = 8u * (g >> 1) + (j >> 2);
+  const uint32_t x = sm<SMV>(krow);
+  const uint32_t mn_lane = 16u * (g & 1u) + 4u * (j & 3u);
+  const uint32_t byte = (mn_lane & 7u) * 2u;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t c = ((uint32_t)mn_base + 32u * (uint32_t)(t < T ? t : 0) + mn_lane) >> 3;
+    off[t] = krow * 512u + ((c ^ x) << 4) + byte;
+  }
+}
+
+// One operand of one wave: T fragments of 32 rows/columns per K step, PER DMA instructions
+// per stage.
+template <bool MN, int T, int PER, int DT>
+struct Operand {
+  using EL = Elem<DT>;
+  using Frag = typename EL::Frag;
+  static_assert(!(MN && EL::kFp8), "fp8 operands are read K-contiguous");
+  uint32_t dma[2];   // byte offsets of the two DMA parities
+  uint32_t frag[4];  // byte offsets: per K-major read slot, or per M/N-major tile
+
+  static constexpr int kReads = MN ? 2 * T : T * EL::kParts;   // LDS reads per K step
+
+  __device__ __forceinline__ void init(int64_t ld, int base, int wave, int lane) {
+    if constexpr (MN) {
+      mn_dma_offsets<PER>(ld, wave, lane, dma);
+      mn_frag_offsets<T>(base, lane, frag);
+    } else {
+      km_dma_offsets<PER, EL::kBytes>(ld, wave, lane, dma);
+      km_frag_offsets<EL::kFp8>(base, lane, frag);
+    }
+  }
+  // Buffer descriptor of this operand's panel: base = the block's first element at K stage
+  // 0, num_records = bytes from there to the end of the operand (reads past it return 0).
+  __amdgpu_buffer_rsrc_t rsrc;
+
+  __device__ __forceinline__ void bind(const uint8_t* panel, int64_t bytes_left) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)panel, (short)0, (int)bytes_left, 0x00020000);
+  }
+  // Issue the PER DMA instructions of one stage (buffer_load_dwordx4 ... lds): per-lane byte
+  // offset `dma[i & 1]` (VGPR), stage and instruction offset `soff` (SGPR), LDS block address
+  // in M0 — no per-instruction vector arithmetic.  `wave` is wave-uniform.
+  __device__ __forceinline__ void load(uint32_t stage_off, int64_t ld, uint8_t* stage,
+                                       int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      // K-major: +8 rows per instruction pair; M/N-major: +2 k-rows per instruction pair
+      const uint32_t step = MN ? (uint32_t)(2 * (i & ~1)) * (uint32_t)ld * 2u
+                               : (uint32_t)(8 * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * PER + i) * 1024),
+                                               16, dma[i & 1], stage_off + step, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void frags(const uint8_t* stage, int s, Frag (&f)[T]) const {
+    if constexpr (MN) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        u32x4 out;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint8_t* p = stage + frag[t] + (16 * s + 4 * h) * 512;
+          const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          out[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+          out[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+        }
+        f[t] = out;
+      }
+    } else if constexpr (EL::kFp8) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const u32x4 lo = *(const u32x4*)(stage + frag[2 * s] + t * 4096);
+        const u32x4 hi = *(const u32x4*)(stage + frag[2 * s + 1] + t * 4096);
+        f[t] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t) f[t] = *(const u32x4*)(stage + frag[s] + t * 4096);
+    }
+  }
+  // One K-major fp8 fragment (tile t, K step s): two ds_read_b128.
+  __device__ __forceinline__ void frag_tile(const uint8_t* stage, int s, int t, Frag& f) const {
+    static_assert(!MN && EL::kFp8, "per-tile reads are used for fp8 operands");
+    const u32x4 lo = *(const u32x4*)(stage + frag[2 * s] + t * 4096);
+    const u32x4 hi = *(const u32x4*)(stage + frag[2 * s + 1] + t * 4096);
+    f = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// Scheduling hints for one K step of NM MFMAs carrying NR LDS reads and ND DMA instructions.
+// The next step's fragment reads go out in the first RS slots (so they have almost a whole
+// step of MFMAs to land before the next step's first MFMA waits for them); the DMA
+// instructions are spread evenly over all slots.
+template <int NM, int NR, int ND, int RS, int Q>
+__device__ __forceinline__ void interleave_slot() {
+  constexpr int r = (NR * (Q + 1)) / RS - (NR * Q) / RS;
+  constexpr int d = (ND * (Q + 1)) / NM - (ND * Q) / NM;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+  if constexpr (Q < RS && r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);   // LDS reads
+  if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x020, d, 0);   // DMA (VMEM read)
+}
+template <int NM, int NR, int ND, int RS, int... Q>
+__device__ __forceinline__ void interleave_seq(std::integer_sequence<int, Q...>) {
+  (interleave_slot<NM, NR, ND, RS, Q>(), ...);
+}
+template <int NM, int NR, int ND>
+__device__ __forceinline__ void interleave() {
+  constexpr int rs = NM >= 4 ? NM / 4 : 1;   // read slots: first quarter of the step
+  interleave_seq<NM, NR, ND, rs>(std::make_integer_sequence<int, NM>{});
+}
+
+// Scheduling hints for one in-place K step (fp8): MFMAs run A-tile by A-tile (TN each); the
+// next step's B fragments (NRB reads) go out after the first MFMA into spare registers, and
+// A tile i's next fragment (NRA reads) right after the last MFMA that reads tile i, into the
+// same registers.  ND DMA instructions are spread evenly.
+template <int TN, int NM, int NRA, int NRB, int ND, int Q>
+__device__ __forceinline__ void inplace_slot() {
+  constexpr int d = (ND * (Q + 1)) / NM - (ND * Q) / NM;
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // MFMA
+  if constexpr (Q == 0 && NRB > 0) __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);  // B reads
+  if constexpr (Q % TN == TN - 1 && NRA > 0) __builtin_amdgcn_sched_group_barrier(0x100, NRA, 0);
+  if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x020, d, 0);             // DMA
+}
+template <int TN, int NM, int NRA, int NRB, int ND, int... Q>
+__device__ __forceinline__ void inplace_seq(std::integer_sequence<int, Q...>) {
+  (inplace_slot<TN, NM, NRA, NRB, ND, Q>(), ...);
+}
+template <int TN, int NM, int NRA, int NRB, int ND>
+__device__ __forceinline__ void interleave_inplace() {
+  inplace_seq<TN, NM, NRA, NRB, ND>(std::make_integer_sequence<int, NM>{});
+}
+
+// Number of K stages a kernel serves: even, odd and at least 3, or exactly one.  Each shape
+// has its own peeled tail, so every LDS address is a compile-time immediate and no
+// accumulator state merges across branches.
+enum KStages { kEven = 0, kOdd = 1, kSingle = 2 };
+
+// WGM x WGN waves; wave tile (256/WGM) x (256/WGN).  BOUNDS: M or N is not a whole number of
+// blocks; operand rows past the end read as zero (buffer range check) and the epilogue skips
+// rows and columns past M and N.  KS: the KStages shape of K / (K per stage).
+template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
+  using EL = Elem<DT>;
+  using Frag = typename EL::Frag;
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int PER = 32 / NW;   // DMA blocks per operand per wave per stage
+  constexpr int E = EL::kBytes, BK = EL::kBK, NS = EL::kSteps;
+  static_assert(PER % 2 == 0 && TM >= 1 && TN >= 1 && TM <= 4 && TN <= 4, "wave grid");
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[BN * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[BM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[BN * kRowBytes];
+
+  // tile scheduler: XCD-contiguous ranges, grouped tile-rows (as gemm_tiled)
+  const int nb = (int)gridDim.x;
+  int bid = (int)blockIdx.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int group = kGroupM * g.tiles_n;
+  const int first_m = (bid / group) * kGroupM;
+  const int gsz = min(g.tiles_m - first_m, kGroupM);
+  const int tm = first_m + (bid % group) % gsz;
+  const int tn = (bid % group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = (int)threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = (wave / WGN) * WM, wn = (wave % WGN) * WN;
+
+  const int64_t lda = A_MN ? g.M : g.K;
+  const int64_t ldb = B_MN ? g.N : g.K;
+  using OA = Operand<A_MN, TM, PER, DT>;
+  using OB = Operand<B_MN, TN, PER, DT>;
+  OA oa;
+  OB ob;
+  oa.init(lda, wm, wave, lane);
+  ob.init(ldb, wn, wave, lane);
+  // operand panels of this block at K stage 0, and the per-stage advance in bytes
+  const int64_t a0 = A_MN ? (int64_t)m0 : (int64_t)m0 * g.K;
+  const int64_t b0 = B_MN ? (int64_t)n0 : (int64_t)n0 * g.K;
+  oa.bind((const uint8_t*)g.A + a0 * E, ((int64_t)g.M * g.K - a0) * E);
+  ob.bind((const uint8_t*)g.B + b0 * E, ((int64_t)g.K * g.N - b0) * E);
+  const uint32_t adv_a = A_MN ? (uint32_t)(BK * g.M * E) : (uint32_t)(BK * E);
+  const uint32_t adv_b = B_MN ? (uint32_t)(BK * g.N * E) : (uint32_t)(BK * E);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  auto mfmas = [&](const Frag (&a)[TM], const Frag (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<DT>(a[i], b[j], acc[i][j]);
+  };
+
+  // Pipeline (K stage kt in buffer `cur`, kt+1 already loading into `nxt`):
+  //   steps 0..NS-2: read step s+1's fragments while step s's MFMAs run;
+  //   wait for this wave's DMA and LDS reads, barrier: stage kt+1 is complete in `nxt` and no
+  //   wave reads `cur` any more;
+  //   then step NS-1's MFMAs (operands already in registers) overlap the reads of stage
+  //   kt+1's first fragments and the DMA of stage kt+2 into `cur`.
+  // The last two stages are peeled off the loop so the steady-state body is branch free.
+  const int KT = g.K / BK;   // >= 1, of shape KS
+  oa.load(0u, lda, sa0, wave);
+  ob.load(0u, ldb, sb0, wave);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  Frag a[TM], b[TN], an[TM], bn[TN];
+  oa.frags(sa0, 0, a);
+  ob.frags(sb0, 0, b);
+  if constexpr (KS != kSingle) {
+    oa.load(adv_a, lda, sa1, wave);
+    ob.load(adv_b, ldb, sb1, wave);
+  }
+
+  constexpr int kMfma = TM * TN;
+  constexpr int kReads = OA::kReads + OB::kReads;
+  constexpr int kDma = 2 * PER;
+
+  // fp8 K step in place: this step's MFMAs, tile by tile of A, while the next step's
+  // fragments (K step `sn` of stages `xa` / `xb`) are read — B's into bn, A tile i's into
+  // a[i] once its MFMAs are issued.  READ false: last step of the last stage.
+  auto step_inplace = [&](const uint8_t* xa, const uint8_t* xb, int sn, auto read, auto dma) {
+    constexpr bool kRead = decltype(read)::value;
+    if constexpr (kRead) ob.frags(xb, sn, bn);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<DT>(a[i], b[j], acc[i][j]);
+      if constexpr (kRead) oa.frag_tile(xa, sn, i, a[i]);
+    }
+    constexpr int nra = kRead ? EL::kParts : 0, nrb = kRead ? OB::kReads : 0;
+    if constexpr (decltype(dma)::value) interleave_inplace<TN, kMfma, nra, nrb, kDma>();
+    else interleave_inplace<TN, kMfma, nra, nrb, 0>();
+    if constexpr (kRead) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = bn[j];
+    }
+  };
+
+  // One K stage.  DMA: also load stage kt+2 into the buffer this stage frees; NEXT: read
+  // the next stage's first fragments (false only for the last stage).
+  auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, int kt,
+                   auto dma, auto next) {
+    if constexpr (EL::kFp8) {
+#pragma unroll
+      for (int s = 0; s < NS - 1; ++s) step_inplace(ca, cb, s + 1, std::true_type{}, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if constexpr (decltype(dma)::value) {
+        oa.load((uint32_t)(kt + 2) * adv_a, lda, ca, wave);
+        ob.load((uint32_t)(kt + 2) * adv_b, ldb, cb, wave);
+      }
+      step_inplace(na, nb_, 0, next, dma);
+      return;
+    }
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+      oa.frags(ca, s + 1, an);
+      ob.frags(cb, s + 1, bn);
+      mfmas(a, b);
+      interleave<kMfma, kReads, 0>();
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = bn[j];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep step NS-2's MFMAs ahead of the wait
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if constexpr (decltype(next)::value) {
+      oa.frags(na, 0, an);
+      ob.frags(nb_, 0, bn);
+    }
+    if constexpr (decltype(dma)::value) {
+      oa.load((uint32_t)(kt + 2) * adv_a, lda, ca, wave);
+      ob.load((uint32_t)(kt + 2) * adv_b, ldb, cb, wave);
+    }
+    mfmas(a, b);
+    if constexpr (decltype(dma)::value) interleave<kMfma, kReads, kDma>();
+    else if constexpr (decltype(next)::value) interleave<kMfma, kReads, 0>();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = an[i];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = bn[j];
+  };
+
+  // epilogue: lane holds column n = lane%32 of each tile, rows 8(r/4) + 4(lane/32) + r%4
+  auto epilogue = [&]() {
+    const int lrow = lane & 31, khalf = lane >> 5;
+    float* dbase = g.D + (int64_t)(m0 + wm + 4 * khalf) * g.N + (n0 + wn + lrow);
+    if constexpr (BOUNDS) {
+      // ragged block: per-element range check (C read only where D is written)
+      const int row0 = m0 + wm + 4 * khalf, col0 = n0 + wn + lrow;
+      const float* cbase = g.C + (int64_t)row0 * g.N + col0;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int dr = 32 * i + 8 * (r >> 2) + (r & 3);
+            if (row0 + dr < g.M && col0 + 32 * j < g.N) {
+              const int64_t o = (int64_t)dr * g.N + 32 * j;
+              dbase[o] = g.use_c ? acc[i][j][r] + cbase[o] : acc[i][j][r];
+            }
+          }
+    } else if (g.use_c) {
+      // C may be exactly D, so the compiler may not move a C load above an earlier D store.
+      // Loads are therefore issued in program order one batch (one 32-row band) ahead of the
+      // stores: every element is still read before it is written, and each batch costs one
+      // memory round trip instead of one per element.
+      const float* cbase = g.C + (int64_t)(m0 + wm + 4 * khalf) * g.N + (n0 + wn + lrow);
+      float cv[2][TN][16];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cv[0][j][r] = cbase[(int64_t)(8 * (r >> 2) + (r & 3)) * g.N + 32 * j];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (i + 1 < TM) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              cv[(i + 1) & 1][j][r] =
+                  cbase[(int64_t)(32 * (i + 1) + 8 * (r >> 2) + (r & 3)) * g.N + 32 * j];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t o = (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * g.N + 32 * j;
+            dbase[o] = acc[i][j][r] + cv[i & 1][j][r];
+          }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t o = (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * g.N + 32 * j;
+            dbase[o] = acc[i][j][r];
+          }
+    }
+  };
+
+  // Steady state: stages kt, kt+1 while both issue DMA (kt + 3 < KT, one more stage kept
+  // for an odd count); then the last two (or three, or the only one).
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if constexpr (KS == kSingle) {
+    stage(sa0, sb0, sa1, sb1, 0, F_{}, F_{});
+  } else {
+    constexpr int odd = KS == kOdd ? 1 : 0;
+    int kt = 0;
+    for (; kt + 2 + odd < KT; kt += 2) {
+      stage(sa0, sb0, sa1, sb1, kt, T_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, kt + 1, T_{}, T_{});
+    }
+    if constexpr (KS == kEven) {
+      stage(sa0, sb0, sa1, sb1, kt, F_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, kt + 1, F_{}, F_{});
+    } else {
+      stage(sa0, sb0, sa1, sb1, kt, T_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, kt + 1, F_{}, T_{});
+      stage(sa0, sb0, sa1, sb1, kt + 2, F_{}, F_{});
+    }
+  }
+  epilogue();
+}
+
+}  // namespace
+}  // namespace tg

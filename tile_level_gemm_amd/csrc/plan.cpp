@@ -200,4 +200,29 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   return c;
 }
 
+GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K) {
+  GemmConfig c{};
+  if (M == 0 || N == 0) {
+    c.kernel = TG_GEMM_NONE;
+    return c;
+  }
+  if (K == 0) {
+    c.kernel = TG_GEMM_FILL;
+    c.threads = 256;
+    c.grid = std::min<int64_t>((M * N + 1023) / 1024, 65536);
+    return c;
+  }
+  c.kernel = TG_GEMM_TILED;
+  c.bm = c.bn = 256;
+  c.bk = 128;
+  c.wm = 128;
+  c.wn = 64;
+  c.threads = 512;
+  c.bounds = (M % 256) != 0 || (N % 256) != 0;
+  c.lds_bytes = 4 * 256 * 128;
+  c.grid = ((M + 255) / 256) * ((N + 255) / 256);
+  c.direct = 1;
+  return c;
+}
+
 }  // namespace tg

@@ -66,7 +66,7 @@ int launch_tile_copy(const CopyArgs& a, int vec_bytes_load, int vec_bytes_store,
                      void* stream);
 
 struct GemmArgs {
-  const uint16_t* A;
+  const uint16_t* A;   // operand base addresses (fp8 kernels read them as bytes)
   const uint16_t* B;
   const float* C;
   float* D;
@@ -91,6 +91,12 @@ int launch_gemm(const GemmArgs& g, const GemmConfig& cfg, int trans_a, int trans
                 void* stream);
 
 bool direct_gemm_fits(int64_t M, int64_t N, int64_t K);
+
+// fp8 GEMM (K-contiguous A [M,K] and B [N,K]): 256x256 blocks, 512 threads, grid =
+// ceil(M/256)·ceil(N/256); bounds = M or N not a multiple of 256.
+GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int a_dtype, int b_dtype, bool bounds,
+                           hipStream_t s);
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
                               hipStream_t s);
 
