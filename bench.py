@@ -8,7 +8,8 @@ Inputs are resident in HBM before the timed region.  Each kernel is bracketed by
 events on the stream it is launched on (torch's current stream, which the binding
 passes to the library); `value` is the GEMM's TFLOP/s over the timed steps, the copy's
 GB/s is reported beside it.  The fp16 transA beta=1 variant of the same GEMM is timed
-after the steps and reported as an extra field.
+after the steps and reported as an extra field, and so is the fp8 (e4m3 x e4m3, A [M,K], B [N,K])
+GEMM of the same size against the dense fp8 peak.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -26,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2516.6   # dense fp16/bf16: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8: twice the fp16/bf16 rate
 PEAK_HBM_GBS = 8000.0       # HBM3E
 M = N = K = 8192
 ROWS = COLS = 16384
@@ -33,7 +35,8 @@ METRIC = "GEMM TFLOP/s + % MFMA peak (bf16 8192³); tile-copy GB/s + % HBM peak"
 
 
 KERNEL_SOURCES = {
-    "gemm": ("gemm_direct.hip", "gemm_kernels.hip", "lds_layout.h", "tg_internal.h"),
+    "gemm": ("gemm_direct.hip", "direct_gemm.h", "gemm_kernels.hip", "lds_layout.h", "tg_internal.h"),
+    "fp8": ("gemm_fp8.hip", "direct_gemm.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
 }
 
@@ -64,8 +67,10 @@ def traffic_for(kernel):
 
 TRAFFIC_KERNELS = {
     # traffic.json key: (kernel-name substring in the rocprofv3 csv, sources, algorithmic bytes)
-    "gemm_direct_256x256_bf16_nn": ("gemm_direct<false, true, 2, 2, 4>", "gemm",
+    "gemm_direct_256x256_bf16_nn": ("gemm_direct<false, true, 2, 2, 4, false, 0>", "gemm",
                                     2 * M * K * 2 + M * N * 4),
+    "gemm_fp8_256x256_e4m3_tn": ("gemm_direct<false, false, 16, 2, 4, false, 0>", "fp8",
+                                 2 * M * K + M * N * 4),
     "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4>", "copy", 2 * ROWS * COLS * 2),
 }
 
@@ -249,6 +254,30 @@ def main():
     hev[1].record()
     torch.cuda.synchronize()
     h_ms = hev[0].elapsed_time(hev[1]) / reps
+    del Ah, Bh, Ch
+
+    # fp8 e4m3 x e4m3 GEMM of the same size, K-contiguous A [M,K] and B [N,K]
+    print("bench: fp8 gemm", file=sys.stderr, flush=True)
+    fin = synth.gemm8k_fp8_inputs()
+    A8 = torch.from_numpy(np.ascontiguousarray(fin[0])).to(dev)
+    B8 = torch.from_numpy(np.ascontiguousarray(fin[1])).to(dev)
+    e4 = tg.TG_FP8_E4M3
+    for _ in range(args.warmup):
+        tg.tile_gemm_fp8(A8, B8, None, D, M, N, K, 0, 1, 0.0, e4, e4)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for ev in fev:
+        ev[0].record()
+        tg.tile_gemm_fp8(A8, B8, None, D, M, N, K, 0, 1, 0.0, e4, e4)
+        ev[1].record()
+    torch.cuda.synchronize()
+    f8_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in fev]))
+    f8_tflops = flops / (f8_ms * 1e-3) / 1e12
+    ref8, bound8 = og.gemm_fp8_ref_at(fin[0], fin[1], None, M, N, K, False, True, 0.0, "e4m3",
+                                      "e4m3", rows, cols)
+    f8_ok, f8_worst = og.check_fp8(D.cpu().numpy()[rows, cols], ref8, bound8, fin[0], fin[1], M, N,
+                                   K, False, True, "e4m3", "e4m3", rows, cols)
+    del A8, B8
 
     base = None
     if not args.no_cpu_baseline:
@@ -289,6 +318,15 @@ def main():
         "gemm_f16_transA_beta1": {"value": round(flops / (h_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
                                    "avg_ms": round(h_ms, 5),
                                    "frac": round(flops / (h_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)},
+        "gemm_fp8_e4m3_tn": {
+            "value": round(f8_tflops, 3), "unit": "TFLOP/s", "avg_ms": round(f8_ms, 5),
+            "workload": "tile_gemm_fp8 8192x8192x8192, A e4m3 [M,K] N(0,1), B e4m3 [N,K] N(0,1), "
+                        "fp32 D, beta=0",
+            "roofline": {"bound": "mfma", "achieved": round(f8_tflops, 3), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4),
+                         "traffic": traffic_for("gemm_fp8_256x256_e4m3_tn")},
+            "parity": {"sampled_ok": bool(f8_ok), "worst_err_over_tol": round(f8_worst, 5)},
+        },
         "parity": {"gemm_sampled_ok": bool(g_ok), "gemm_worst_err_over_tol": round(g_worst, 5),
                    "copy_bit_exact": c_ok},
         "cpu_baseline": base,
