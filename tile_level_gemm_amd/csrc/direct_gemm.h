@@ -452,7 +452,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
     for (int j = 0; j < TN; ++j) b[j] = bn[j];
   };
 
-  // epilogue: lane holds column n = lane%32 of each tile, rows 8(r/4) + 4(lane/32) + r%4
+  // epilogue: lane holds column n = lane%32 of each tile, rows 8(r/4) + 4(lane/32) + r%4.
+  // D is written with nontemporal stores: it is not read again here, and streaming it past
+  // the L2 keeps the operand panels of the blocks that follow resident (measured 8-14 %
+  // faster at 8192^3 than ordinary stores).
   auto epilogue = [&]() {
     const int lrow = lane & 31, khalf = lane >> 5;
     float* dbase = g.D + (int64_t)(m0 + wm + 4 * khalf) * g.N + (n0 + wn + lrow);
@@ -469,7 +472,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
             const int dr = 32 * i + 8 * (r >> 2) + (r & 3);
             if (row0 + dr < g.M && col0 + 32 * j < g.N) {
               const int64_t o = (int64_t)dr * g.N + 32 * j;
-              dbase[o] = g.use_c ? acc[i][j][r] + cbase[o] : acc[i][j][r];
+              __builtin_nontemporal_store(g.use_c ? acc[i][j][r] + cbase[o] : acc[i][j][r],
+                                          &dbase[o]);
             }
           }
     } else if (g.use_c) {
@@ -499,7 +503,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t o = (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * g.N + 32 * j;
-            dbase[o] = acc[i][j][r] + cv[i & 1][j][r];
+            __builtin_nontemporal_store(acc[i][j][r] + cv[i & 1][j][r], &dbase[o]);
           }
       }
     } else {
@@ -510,7 +514,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t o = (int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * g.N + 32 * j;
-            dbase[o] = acc[i][j][r];
+            __builtin_nontemporal_store(acc[i][j][r], &dbase[o]);
           }
     }
   };
