@@ -171,9 +171,10 @@ int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D,
  * asynchronous GEMM's precision family ([SYNC-GEMM] 七: besides f16/bf16 it takes fp8 and
  * fp4 operands, with A and B staged in shared memory and the product accumulated in fp32).
  *
- *   A      device, OCP fp8 of format a_dtype, stored row-major [M,K] (transA == 0).
- *   B      device, OCP fp8 of format b_dtype, stored row-major [N,K] (transB == 1).
- *          Both operands are read K-contiguous; transA == 1 or transB == 0 -> TG_E_LAYOUT.
+ *   A      device, OCP fp8 of format a_dtype, stored row-major [M,K] (transA == 0) or [K,M]
+ *          (transA == 1).
+ *   B      device, OCP fp8 of format b_dtype, stored row-major [K,N] (transB == 0) or [N,K]
+ *          (transB == 1).  As for tile_gemm the flags only describe the stored orientation.
  *   C, D   as tile_gemm: fp32 [M,N] row-major packed, C read only when beta == 1, C may be
  *          exactly D, D must not overlap A or B.
  *   M,N,K  M % 16 == 0, N % 16 == 0, K % 128 == 0, all >= 0, and each operand under 2 GiB;

@@ -275,10 +275,13 @@ def test_fp8_validation_matches_oracle(M, N, K, a_dt, b_dt, beta):
 
 def test_fp8_layouts_and_errors_need_no_gpu():
     e4 = tg.TG_FP8_E4M3
-    for ta, tb in ((1, 1), (0, 0), (1, 0)):
-        with pytest.raises(tg.TileError) as e:
-            tg.tile_gemm_fp8(A_ADDR, B_ADDR, None, D_ADDR, 256, 256, 256, ta, tb, 0.0, e4, e4)
-        assert e.value.status == tg.TG_E_LAYOUT and "K-contiguous" in e.value.reason
+    # every stored orientation is served, with the same plan
+    plans = set()
+    for ta in (0, 1):
+        for tb in (0, 1):
+            p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 256, 512, 384, ta, tb, 0.0, e4, e4)
+            plans.add((p.kernel, p.block_m, p.block_n, p.block_k, p.grid, p.bounds_checked, p.loader))
+    assert plans == {(tg.TG_GEMM_TILED, 256, 256, 128, 2, 0, 1)}
     with pytest.raises(tg.TileError) as e:
         tg.tile_gemm_fp8(A_ADDR, B_ADDR, None, D_ADDR, 256, 256, 256, 0, 2, 0.0, e4, e4)
     assert e.value.status == tg.TG_E_ARG

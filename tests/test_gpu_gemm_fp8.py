@@ -19,23 +19,24 @@ FMT = {"e4m3": tg.TG_FP8_E4M3, "e5m2": tg.TG_FP8_E5M2}
 PAIRS = [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]
 
 
-def run_fp8(a_bits, b_bits, c, M, N, K, beta, af, bf, c_is_d=False):
-    """A stored [M, K], B stored [N, K] (the K-contiguous orientation)."""
+def run_fp8(a_bits, b_bits, c, M, N, K, beta, af, bf, c_is_d=False, ta=False, tb=True):
+    """A stored [M, K] or [K, M] (ta), B stored [K, N] or [N, K] (tb)."""
     A = upload_bits(a_bits)
     B = upload_bits(b_bits)
     D = Guarded(M * N * 4, fill=(c if c_is_d else np.full((M, N), np.nan, np.float32)))
     Cd = upload_f32(c) if beta == 1.0 and not c_is_d else None
-    tg.tile_gemm_fp8(A, B, D.ptr if c_is_d else Cd, D.ptr, M, N, K, 0, 1, beta, FMT[af], FMT[bf])
+    tg.tile_gemm_fp8(A, B, D.ptr if c_is_d else Cd, D.ptr, M, N, K, int(ta), int(tb), beta, FMT[af],
+                     FMT[bf])
     torch.cuda.synchronize()
     return D.host(np.float32).reshape(M, N), D.guards_intact()
 
 
-def full_check(M, N, K, af, bf, beta, seeds, scale=1.0, c_is_d=False):
-    a_bits, b_bits, c = synth.gemm_fp8_inputs(M, N, K, af, bf, False, True, beta, seeds, scale)
-    d, guards = run_fp8(a_bits, b_bits, c, M, N, K, beta, af, bf, c_is_d=c_is_d)
-    ref = og.gemm_fp8_ref(a_bits, b_bits, c, M, N, K, False, True, beta, af, bf)
-    bound = og.abs_bound_fp8(a_bits, b_bits, M, N, K, False, True, af, bf)
-    ok, worst = og.check_fp8(d, ref, bound, a_bits, b_bits, M, N, K, False, True, af, bf)
+def full_check(M, N, K, af, bf, beta, seeds, scale=1.0, c_is_d=False, ta=False, tb=True):
+    a_bits, b_bits, c = synth.gemm_fp8_inputs(M, N, K, af, bf, ta, tb, beta, seeds, scale)
+    d, guards = run_fp8(a_bits, b_bits, c, M, N, K, beta, af, bf, c_is_d=c_is_d, ta=ta, tb=tb)
+    ref = og.gemm_fp8_ref(a_bits, b_bits, c, M, N, K, ta, tb, beta, af, bf)
+    bound = og.abs_bound_fp8(a_bits, b_bits, M, N, K, ta, tb, af, bf)
+    ok, worst = og.check_fp8(d, ref, bound, a_bits, b_bits, M, N, K, ta, tb, af, bf)
     assert guards, "guard band written"
     assert ok, f"worst |D-D_ref|/tol = {worst}"
     return worst
@@ -60,6 +61,30 @@ def test_shapes_e4m3(M, N, K, beta):
 def test_format_pairs(M, N, K, af, bf):
     say(f"gemm_fp8 {M}x{N}x{K} {af} x {bf} beta=1")
     full_check(M, N, K, af, bf, 1.0, (5, 6, 7), scale=4.0)
+
+
+@pytest.mark.parametrize("M,N,K", [(48, 32, 128), (272, 528, 384), (784, 1040, 640),
+                                   (1296, 1040, 1280), (512, 768, 2048)])
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, True), (True, False), (False, True)])
+def test_transposes(M, N, K, ta, tb):
+    """Every stored orientation: M/N-contiguous operands go through ds_read_b64_tr_b8."""
+    say(f"gemm_fp8 {M}x{N}x{K} e4m3 x e5m2 transA={ta} transB={tb} beta=1")
+    full_check(M, N, K, "e4m3", "e5m2", 1.0, (M + 7, N + 8, K + 9), ta=ta, tb=tb)
+
+
+@pytest.mark.parametrize("ta,tb", [(True, False), (False, False)])
+def test_every_finite_code_mn(ta, tb):
+    """All finite codes with M/N-contiguous operands: the transposing reads must hand each
+    lane the same K order as the K-contiguous path (the fp8 bar's groups of 8 rely on it)."""
+    say(f"gemm_fp8 all finite codes e5m2 x e5m2 transA={ta} transB={tb}")
+    M, N, K = 256, 256, 512
+    a_bits = finite_codes(71, M * K, "e5m2").reshape((K, M) if ta else (M, K))
+    b_bits = finite_codes(72, N * K, "e5m2").reshape((N, K) if tb else (K, N))
+    d, guards = run_fp8(a_bits, b_bits, None, M, N, K, 0.0, "e5m2", "e5m2", ta=ta, tb=tb)
+    ref = og.gemm_fp8_ref(a_bits, b_bits, None, M, N, K, ta, tb, 0.0, "e5m2", "e5m2")
+    bound = og.abs_bound_fp8(a_bits, b_bits, M, N, K, ta, tb, "e5m2", "e5m2")
+    ok, worst = og.check_fp8(d, ref, bound, a_bits, b_bits, M, N, K, ta, tb, "e5m2", "e5m2")
+    assert guards and ok, worst
 
 
 def finite_codes(seed, n, fmt):
@@ -144,34 +169,36 @@ def test_beta0_ignores_nan_c():
     assert torch.isfinite(D1).all() and torch.equal(D1, D2)
 
 
-@pytest.mark.parametrize("af,bf,K", [("e4m3", "e4m3", 8192), ("e5m2", "e4m3", 8064)])
-def test_large_sampled(af, bf, K):
+@pytest.mark.parametrize("af,bf,K,tb", [("e4m3", "e4m3", 8192, True), ("e5m2", "e4m3", 8064, True),
+                                        ("e4m3", "e4m3", 8192, False)])
+def test_large_sampled(af, bf, K, tb):
     """The 8192 x 8192 x 8192 e4m3 workload (and a mixed-format one whose stage count is
-    odd) in the launch configuration the benchmark times: 4096 sampled outputs plus tile
-    boundaries against one float64 dot each, and bitwise repeatability."""
+    odd, and one with B stored [K, N]) in the launch configuration the benchmark times:
+    4096 sampled outputs plus tile boundaries against one float64 dot each, and bitwise
+    repeatability."""
     M = N = 8192
-    say(f"gemm_fp8 {M}x{N}x{K} {af} x {bf} sampled")
-    if (af, bf, K) == ("e4m3", "e4m3", 8192):
+    say(f"gemm_fp8 {M}x{N}x{K} {af} x {bf} transB={tb} sampled")
+    if (af, bf, K, tb) == ("e4m3", "e4m3", 8192, True):
         a_bits, b_bits, c = synth.gemm8k_fp8_inputs()
     else:
-        a_bits, b_bits, c = synth.gemm_fp8_inputs(M, N, K, af, bf, False, True, 1.0, (64, 65, 66))
+        beta_in = 1.0 if af != bf else 0.0
+        a_bits, b_bits, c = synth.gemm_fp8_inputs(M, N, K, af, bf, False, tb, beta_in, (64, 65, 66))
     beta = 0.0 if c is None else 1.0
     A, B = upload_bits(a_bits), upload_bits(b_bits)
-    plan = tg.tile_gemm_fp8_plan(A, B, None if c is None else 1 << 40, 1 << 41, M, N, K, 0, 1, beta,
-                                 FMT[af], FMT[bf])
+    plan = tg.tile_gemm_fp8_plan(A, B, None if c is None else 1 << 40, 1 << 41, M, N, K, 0, int(tb),
+                                 beta, FMT[af], FMT[bf])
     assert (plan.block_m, plan.block_n, plan.bounds_checked, plan.loader) == (256, 256, 0, 1)
     Cd = upload_f32(c) if c is not None else None
     D = torch.empty((M, N), device="cuda:0")
-    tg.tile_gemm_fp8(A, B, Cd, D, M, N, K, 0, 1, beta, FMT[af], FMT[bf])
+    tg.tile_gemm_fp8(A, B, Cd, D, M, N, K, 0, int(tb), beta, FMT[af], FMT[bf])
     D2 = torch.empty((M, N), device="cuda:0")
-    tg.tile_gemm_fp8(A, B, Cd, D2, M, N, K, 0, 1, beta, FMT[af], FMT[bf])
+    tg.tile_gemm_fp8(A, B, Cd, D2, M, N, K, 0, int(tb), beta, FMT[af], FMT[bf])
     torch.cuda.synchronize()
     assert torch.equal(D, D2), "not bitwise repeatable"
     rows, cols = synth.sample_points(M, N, 63)
     got = D[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
-    ref, bound = og.gemm_fp8_ref_at(a_bits, b_bits, c, M, N, K, False, True, beta, af, bf, rows, cols)
-    ok, worst = og.check_fp8(got, ref, bound, a_bits, b_bits, M, N, K, False, True, af, bf, rows,
-                             cols)
+    ref, bound = og.gemm_fp8_ref_at(a_bits, b_bits, c, M, N, K, False, tb, beta, af, bf, rows, cols)
+    ok, worst = og.check_fp8(got, ref, bound, a_bits, b_bits, M, N, K, False, tb, af, bf, rows, cols)
     assert ok, worst
 
 

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libtilegemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.cpp", "plan.cpp", "copy_kernels.hip", "gemm_kernels.hip", "gemm_direct.hip",
-           "gemm_fp8.hip"]
+           "gemm_fp8.hip", "gemm_fp8_km.hip", "gemm_fp8_mk.hip", "gemm_fp8_mm.hip"]
 
 # -packed-fp32-ops: no v_pk_*_f32 in generated code (the device pass honours it; the
 # host pass warns that it does not know the feature).
@@ -41,7 +41,7 @@ def _compile(src):
     return obj
 
 
-def build(jobs=4):
+def build(jobs=8):
     """Compile every source and link libtilegemm.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:

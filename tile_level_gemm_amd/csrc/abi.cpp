@@ -83,7 +83,7 @@ bool is_fp8(int dtype) { return dtype == TG_FP8_E4M3 || dtype == TG_FP8_E5M2; }
 
 // tile_gemm_fp8 ([SYNC-GEMM] 七, the fp8 operands of the asynchronous GEMM): same checks
 // and order as validate_gemm, with the fp8 shape rule (M % 16, N % 16, K % 128), the fp8
-// formats, one-byte operand elements and the K-contiguous orientations.
+// formats and one-byte operand elements.
 int validate_gemm_fp8(const void* A, const void* B, const float* C, const float* D, int64_t M,
                       int64_t N, int64_t K, int transA, int transB, float beta, int a_dtype,
                       int b_dtype) {
@@ -102,9 +102,6 @@ int validate_gemm_fp8(const void* A, const void* B, const float* C, const float*
                                 "%lld, b_dtype %lld); C and D are fp32", a_dtype, b_dtype));
   if (transA != 0 && transA != 1) return fail(TG_E_ARG, "transA must be 0 or 1");
   if (transB != 0 && transB != 1) return fail(TG_E_ARG, "transB must be 0 or 1");
-  if (transA != 0 || transB != 1)
-    return fail(TG_E_LAYOUT, "fp8 gemm reads both operands K-contiguous: A stored [M,K] "
-                             "(transA = 0) and B stored [N,K] (transB = 1)");
   if (!(beta == 0.0f || beta == 1.0f))
     return fail(TG_E_BETA, "beta must be exactly 0.0 or 1.0 (alpha is fixed at 1)");
   if (M == 0 || N == 0) return TG_OK;
@@ -360,8 +357,8 @@ int tile_gemm_fp8(const void* A, const void* B, const float* C, float* D, int64_
   if (cfg.kernel == TG_GEMM_FILL) return launch_gemm(g, cfg, 0, 0, TG_BF16, stream);
   g.tiles_m = (int32_t)((M + 255) / 256);
   g.tiles_n = (int32_t)((N + 255) / 256);
-  const hipError_t e = launch_gemm_fp8(g, cfg.grid, a_dtype, b_dtype, cfg.bounds != 0,
-                                       (hipStream_t)stream);
+  const hipError_t e = launch_gemm_fp8(g, cfg.grid, transA, transB, a_dtype, b_dtype,
+                                       cfg.bounds != 0, (hipStream_t)stream);
   if (e != hipSuccess)
     return fail(TG_E_HIP, std::string("tile_gemm_fp8 launch: ") + hipGetErrorString(e));
   return TG_OK;

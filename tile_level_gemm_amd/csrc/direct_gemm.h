@@ -49,6 +49,8 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int BM = 256, BN = 256;
 constexpr int kRowBytes = 128;   // bytes of K per operand row and stage
@@ -107,6 +109,12 @@ __device__ __forceinline__ uint32_t sm(uint32_t k) {
   else return ((k & 3u) << 1) ^ ((k & 1u) << 3);
 }
 
+// M/N-major fp8 stage: 128 k-rows x 256 bytes (16 chunks); physical chunk = c ^ s8(k).  A
+// transposing read (ds_read_b64_tr_b8) of 32 lanes touches two adjacent chunks (an even one
+// and the next) in each of 8 consecutive k-rows; 2(k & 7) sends the 16 of them to 16 distinct
+// 16-byte bank slots.
+__device__ __forceinline__ uint32_t s8(uint32_t k) { return (k & 7u) << 1; }
+
 // ---- per-lane offsets, computed once ---------------------------------------------------
 // Every address below is a per-lane offset computed before the K loop plus compile-time
 // immediates (tile, K step, stage), so the loop keeps few address registers.
@@ -136,6 +144,19 @@ __device__ __forceinline__ void mn_dma_offsets(int64_t ld, int wave, int lane, u
     const uint32_t k = (uint32_t)(2 * PER * wave + 2 * p + (lane >> 5));
     const uint32_t c = ((uint32_t)lane & 31u) ^ sm<SMV>(k);
     off[p] = (k * (uint32_t)ld + c * 8u) * 2u;    // bytes; < 64·N·2 < 2^32
+  }
+}
+
+// DMA for an M/N-major fp8 operand: instruction i writes block b = PER·wave + i = k-rows 4b ..
+// 4b+3; lane l fills slot l%16 of k-row 4b + l/16, logical chunk (l%16) ^ s8(k); s8 depends on
+// the lane and i's parity.
+template <int PER>
+__device__ __forceinline__ void mn8_dma_offsets(int64_t ld, int wave, int lane, uint32_t (&off)[2]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t k = (uint32_t)(4 * PER * wave + 4 * p + (lane >> 4));
+    const uint32_t c = ((uint32_t)lane & 15u) ^ s8(k);
+    off[p] = k * (uint32_t)ld + c * 16u;   // bytes; < 128·M < 2^32
   }
 }
 
@@ -172,20 +193,43 @@ __device__ __forceinline__ void mn_frag_offsets(int mn_base, int lane, uint32_t 
   }
 }
 
+// M/N-major fp8 fragment of 32-column tile t, K step s (64 k), read u = 0..3 (four
+// ds_read_b64_tr_b8): within each 16-lane group g, lane j receives byte j%8 of the 8-byte
+// reads of lanes 2k + j/8 (k = 0..7).  So lane l = 16g + j reads k-row 64s + 32(g/2) + 8u +
+// j/2 at columns mn_base + 32t + 16(g&1) + 8(j&1) .. +7, and receives k 32(g/2) + 8u .. +7 of
+// column mn_base + 32t + l%32 — the K order of the K-major fp8 fragment.  s8 depends on j only
+// (s and u add multiples of 8 rows); the chunk of tile t is kept per t (2t carries into the
+// swizzled bits), s and u are immediates.
+template <int T>
+__device__ __forceinline__ void mn8_frag_offsets(int mn_base, int lane, uint32_t (&off)[4]) {
+  const uint32_t g = (uint32_t)lane >> 4, j = (uint32_t)lane & 15u;
+  const uint32_t krow = 32u * (g >> 1) + (j >> 1);
+  const uint32_t x = s8(krow);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t c = ((uint32_t)mn_base + 32u * (uint32_t)(t < T ? t : 0)) / 16u + (g & 1u);
+    off[t] = krow * 256u + ((c ^ x) << 4) + 8u * (j & 1u);
+  }
+}
+
 // One operand of one wave: T fragments of 32 rows/columns per K step, PER DMA instructions
 // per stage.
 template <bool MN, int T, int PER, int DT>
 struct Operand {
   using EL = Elem<DT>;
   using Frag = typename EL::Frag;
-  static_assert(!(MN && EL::kFp8), "fp8 operands are read K-contiguous");
   uint32_t dma[2];   // byte offsets of the two DMA parities
   uint32_t frag[4];  // byte offsets: per K-major read slot, or per M/N-major tile
 
-  static constexpr int kReads = MN ? 2 * T : T * EL::kParts;   // LDS reads per K step
+  // LDS read instructions per fragment and per K step
+  static constexpr int kTileReads = MN ? (EL::kFp8 ? 4 : 2) : EL::kParts;
+  static constexpr int kReads = T * kTileReads;
 
   __device__ __forceinline__ void init(int64_t ld, int base, int wave, int lane) {
-    if constexpr (MN) {
+    if constexpr (MN && EL::kFp8) {
+      mn8_dma_offsets<PER>(ld, wave, lane, dma);
+      mn8_frag_offsets<T>(base, lane, frag);
+    } else if constexpr (MN) {
       mn_dma_offsets<PER>(ld, wave, lane, dma);
       mn_frag_offsets<T>(base, lane, frag);
     } else {
@@ -207,15 +251,19 @@ struct Operand {
                                        int wave) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      // K-major: +8 rows per instruction pair; M/N-major: +2 k-rows per instruction pair
-      const uint32_t step = MN ? (uint32_t)(2 * (i & ~1)) * (uint32_t)ld * 2u
+      // K-major: +8 rows per instruction pair; M/N-major: +2 (16-bit) or +4 (fp8) k-rows
+      const uint32_t step = MN ? (EL::kFp8 ? (uint32_t)(4 * (i & ~1)) * (uint32_t)ld
+                                           : (uint32_t)(2 * (i & ~1)) * (uint32_t)ld * 2u)
                                : (uint32_t)(8 * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * PER + i) * 1024),
                                                16, dma[i & 1], stage_off + step, 0, 0);
     }
   }
   __device__ __forceinline__ void frags(const uint8_t* stage, int s, Frag (&f)[T]) const {
-    if constexpr (MN) {
+    if constexpr (MN && EL::kFp8) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) frag_tile(stage, s, t, f[t]);
+    } else if constexpr (MN) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         u32x4 out;
@@ -240,12 +288,25 @@ struct Operand {
       for (int t = 0; t < T; ++t) f[t] = *(const u32x4*)(stage + frag[s] + t * 4096);
     }
   }
-  // One K-major fp8 fragment (tile t, K step s): two ds_read_b128.
+  // One fp8 fragment (tile t, K step s): two ds_read_b128 (K-major) or four
+  // ds_read_b64_tr_b8 (M/N-major).
   __device__ __forceinline__ void frag_tile(const uint8_t* stage, int s, int t, Frag& f) const {
-    static_assert(!MN && EL::kFp8, "per-tile reads are used for fp8 operands");
-    const u32x4 lo = *(const u32x4*)(stage + frag[2 * s] + t * 4096);
-    const u32x4 hi = *(const u32x4*)(stage + frag[2 * s + 1] + t * 4096);
-    f = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    static_assert(EL::kFp8, "per-tile reads are used for fp8 operands");
+    if constexpr (MN) {
+      u32x8 out;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint8_t* p = stage + frag[t] + (64 * s + 8 * u) * 256;
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+        out[2 * u] = (uint32_t)v[0];
+        out[2 * u + 1] = (uint32_t)v[1];
+      }
+      f = out;
+    } else {
+      const u32x4 lo = *(const u32x4*)(stage + frag[2 * s] + t * 4096);
+      const u32x4 hi = *(const u32x4*)(stage + frag[2 * s + 1] + t * 4096);
+      f = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
   }
 };
 
@@ -395,7 +456,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<DT>(a[i], b[j], acc[i][j]);
       if constexpr (kRead) oa.frag_tile(xa, sn, i, a[i]);
     }
-    constexpr int nra = kRead ? EL::kParts : 0, nrb = kRead ? OB::kReads : 0;
+    constexpr int nra = kRead ? OA::kTileReads : 0, nrb = kRead ? OB::kReads : 0;
     if constexpr (decltype(dma)::value) interleave_inplace<TN, kMfma, nra, nrb, kDma>();
     else interleave_inplace<TN, kMfma, nra, nrb, 0>();
     if constexpr (kRead) {

@@ -1,0 +1,11 @@
+// fp8 GEMM instantiations of the direct-load kernel template for A stored [M,K] and B stored [K,N].
+#include "gemm_fp8_launch.h"
+
+namespace tg {
+
+hipError_t launch_fp8_km(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds,
+                         hipStream_t s) {
+  return launch_fp8_layout<false, true>(g, grid, af, bf, bounds, s);
+}
+
+}  // namespace tg

@@ -92,11 +92,11 @@ int launch_gemm(const GemmArgs& g, const GemmConfig& cfg, int trans_a, int trans
 
 bool direct_gemm_fits(int64_t M, int64_t N, int64_t K);
 
-// fp8 GEMM (K-contiguous A [M,K] and B [N,K]): 256x256 blocks, 512 threads, grid =
+// fp8 GEMM (any operand orientation): 256x256 blocks, 512 threads, grid =
 // ceil(M/256)·ceil(N/256); bounds = M or N not a multiple of 256.
 GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int a_dtype, int b_dtype, bool bounds,
-                           hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int a_dtype,
+                           int b_dtype, bool bounds, hipStream_t s);
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
                               hipStream_t s);
 
