@@ -34,7 +34,7 @@ products, and their acceptance table.
 
 import numpy as np
 
-from .numerics import decode
+from .numerics import decode, e8m0_bits_to_f64
 
 FORMATS = ("f16", "bf16")
 
@@ -182,6 +182,53 @@ def gemm_fp8_ref_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype,
                     cols, chunk)
 
 
+# ---- block-scaled (MX) fp8: the page's SFA / SFB ----------------------------------------
+# [SYNC-GEMM] 七 lists block-scaled operands (scale factors SFA for A and SFB for B) among the
+# asynchronous GEMM's modes.  Reading (the page names no block size or scale format): the OCP
+# microscaling convention — every 32 consecutive K of a row of A (of a column of B) share one
+# E8M0 scale 2^(e-127).  SA is [M][K/32] and SB is [N][K/32] bytes, row-major, whatever the
+# stored orientation of A and B:
+#     D[m][n] = sum_k (SA[m][k/32] A[m][k]) (SB[n][k/32] B[k][n])  (+ C[m][n]).
+# Shapes, formats, alpha and beta are those of the fp8 GEMM.
+
+MX_BLOCK = 32
+
+
+def _scaled_operands(a_bits, b_bits, sa_bits, sb_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype):
+    a_l, b_l = logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype)
+    sa = e8m0_bits_to_f64(np.asarray(sa_bits, np.uint8).reshape(M, K // MX_BLOCK))
+    sb = e8m0_bits_to_f64(np.asarray(sb_bits, np.uint8).reshape(N, K // MX_BLOCK))
+    a_s = a_l * np.repeat(sa, MX_BLOCK, axis=1)
+    b_s = b_l * np.repeat(sb, MX_BLOCK, axis=1).T
+    return a_s, b_s
+
+
+def gemm_mx_ref(a_bits, b_bits, sa_bits, sb_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype,
+                b_dtype):
+    """Full float64 D_ref of the block-scaled fp8 GEMM (scales applied exactly: powers of 2)."""
+    ok, why = accepts_fp8(M, N, K, a_dtype, b_dtype, beta=beta)
+    if not ok:
+        raise ValueError(f"oracle: call rejected ({why})")
+    if K == 0:
+        d = np.zeros((M, N))
+    else:
+        a_s, b_s = _scaled_operands(a_bits, b_bits, sa_bits, sb_bits, M, N, K, trans_a, trans_b,
+                                    a_dtype, b_dtype)
+        d = np.matmul(a_s, b_s)
+    if beta == 1.0:
+        d = d + np.asarray(c, dtype=np.float32).reshape(M, N).astype(np.float64)
+    return d
+
+
+def abs_bound_mx(a_bits, b_bits, sa_bits, sb_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype):
+    """sum_k |scaled A_ik · scaled B_kj| for every (i, j)."""
+    if K == 0:
+        return np.zeros((M, N))
+    a_s, b_s = _scaled_operands(a_bits, b_bits, sa_bits, sb_bits, M, N, K, trans_a, trans_b,
+                                a_dtype, b_dtype)
+    return np.matmul(np.abs(a_s), np.abs(b_s))
+
+
 # ---- the fp8 comparison bar ------------------------------------------------------------
 # The fp8 product unit of gfx950 (v_mfma_*_f8f6f4) does not add its products in fp32.
 # Measured with structured operands: each group of 8 consecutive K products (aligned to 8 in
@@ -200,9 +247,11 @@ FP8_WINDOW = 13
 
 
 def fp8_unit_allowance_at(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype, rows,
-                          cols):
+                          cols, sa_bits=None, sb_bits=None):
     """Allowance T at outputs (rows[s], cols[s]): sum over aligned K groups of 8 of
-    min(|p|, q_g) for the products p not on their group's grid q_g."""
+    min(|p|, q_g) for the products p not on their group's grid q_g.  With block scales
+    (sa_bits, sb_bits: [M][K/32], [N][K/32]) the products are the scaled ones; a scale is
+    uniform over a group of 8, so the grid rule carries over unchanged."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
     out = np.zeros(rows.size)
@@ -210,6 +259,11 @@ def fp8_unit_allowance_at(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_
         return out
     a = decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, rows)), a_dtype)
     b = decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, cols)), b_dtype)
+    if sa_bits is not None:
+        sa = e8m0_bits_to_f64(np.asarray(sa_bits, np.uint8).reshape(M, K // MX_BLOCK)[rows])
+        sb = e8m0_bits_to_f64(np.asarray(sb_bits, np.uint8).reshape(N, K // MX_BLOCK)[cols])
+        a = a * np.repeat(sa, MX_BLOCK, axis=1)
+        b = b * np.repeat(sb, MX_BLOCK, axis=1)
     p = np.abs(a * b).reshape(rows.size, K // FP8_GROUP, FP8_GROUP)
     mx = p.max(axis=2, keepdims=True)
     e = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
@@ -219,7 +273,7 @@ def fp8_unit_allowance_at(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_
 
 
 def check_fp8(d_gpu, d_ref, bound, a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype,
-              rows=None, cols=None):
+              rows=None, cols=None, sa_bits=None, sb_bits=None):
     """The fp8 bar: |D - D_ref| <= 1e-4·bound + T + 1e-6, T = fp8_unit_allowance_at.
 
     d_gpu, d_ref, bound are [M, N] arrays (rows, cols None) or values at (rows, cols).  T is
@@ -239,7 +293,7 @@ def check_fp8(d_gpu, d_ref, bound, a_bits, b_bits, M, N, K, trans_a, trans_b, a_
             r, c = np.asarray(rows)[over[0]], np.asarray(cols)[over[0]]
         tol = tol.copy()
         tol[over] += fp8_unit_allowance_at(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype,
-                                           b_dtype, r, c)
+                                           b_dtype, r, c, sa_bits, sb_bits)
     worst = float((err / tol).max())
     return worst <= 1.0, worst
 
