@@ -184,7 +184,7 @@ int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D,
  *          S.1111.111 is NaN) or TG_FP8_E5M2 (bias 15, IEEE-style infinities and NaNs); the
  *          two may differ.  Anything else -> TG_E_DTYPE.  Every product of two fp8 values is
  *          exact in fp32; products are accumulated in fp32 by MFMA.  No block scales (the
- *          scaled variants of the page are a separate entry point).
+ *          block-scaled mode is tile_gemm_mx).
  *   Alignment: A and B 16-byte aligned, C and D 4-byte aligned; otherwise TG_E_ALIGN.
  * Returns TG_OK or a tg_status; asynchronous on `stream`.
  */
@@ -197,6 +197,32 @@ int tile_gemm_fp8(const void* A, const void* B, const float* C, float* D,
 int tile_gemm_fp8_plan(const void* A, const void* B, const float* C, const float* D,
                        int64_t M, int64_t N, int64_t K, int transA, int transB,
                        float beta, int a_dtype, int b_dtype, tg_gemm_plan* out);
+
+/*
+ * tile_gemm_mx — block-scaled fp8 GEMM: the block-scaled mode of the asynchronous GEMM
+ * ([SYNC-GEMM] 七: scale factors SFA for A and SFB for B), in the OCP microscaling form:
+ *
+ *   D[m][n] = sum_k (SA[m][k/32]·A[m][k]) · (SB[n][k/32]·B[k][n])  + beta·C[m][n]
+ *
+ *   A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype, stream: as tile_gemm_fp8.
+ *   SA     device, E8M0 scale bytes of A, [M][K/32] row-major whatever A's orientation: byte
+ *          SA[m][kb] scales A[m][32kb .. 32kb+31] by 2^(SA[m][kb] - 127).  255 is NaN.
+ *   SB     device, E8M0 scale bytes of B, [N][K/32] row-major: SB[n][kb] scales B[32kb ..][n].
+ *          SA and SB are read only when K > 0; they must then be non-NULL (TG_E_NULL), 4-byte
+ *          aligned (TG_E_ALIGN) and must not overlap D (TG_E_ALIAS).
+ *   The scales are applied by the matrix unit per 32-K block (exact: powers of two) and the
+ *   scaled products accumulated in fp32.
+ * Returns TG_OK or a tg_status; asynchronous on `stream`.
+ */
+int tile_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                 const float* C, float* D, int64_t M, int64_t N, int64_t K, int transA,
+                 int transB, float beta, int a_dtype, int b_dtype, void* stream);
+
+/* tile_gemm_mx_plan — host-only validation and kernel choice of tile_gemm_mx.  Needs no GPU. */
+int tile_gemm_mx_plan(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                      const float* C, const float* D, int64_t M, int64_t N, int64_t K,
+                      int transA, int transB, float beta, int a_dtype, int b_dtype,
+                      tg_gemm_plan* out);
 
 /*
  * tile_copy — bit-exact copy of a shape[0] x shape[1] matrix from src to dst, staged
@@ -252,7 +278,8 @@ int tile_copy_partition(int64_t rows, int64_t cols, int elem_bits, int threads,
 /* Reason for the last failure on the calling thread ("" after a success). */
 const char* tile_last_error(void);
 
-/* Library ABI version (this header: 2; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan). */
+/* Library ABI version (this header: 3; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
+ * tile_gemm_mx and tile_gemm_mx_plan). */
 int tile_abi_version(void);
 
 #ifdef __cplusplus

@@ -220,6 +220,33 @@ def gemm_mx_ref(a_bits, b_bits, sa_bits, sb_bits, c, M, N, K, trans_a, trans_b, 
     return d
 
 
+def gemm_mx_ref_at(a_bits, b_bits, sa_bits, sb_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype,
+                   b_dtype, rows, cols, chunk=512):
+    """D_ref and the bound of the block-scaled GEMM at sampled outputs, one float64 dot each."""
+    ok, why = accepts_fp8(M, N, K, a_dtype, b_dtype, beta=beta)
+    if not ok:
+        raise ValueError(f"oracle: call rejected ({why})")
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    sa = np.asarray(sa_bits, np.uint8).reshape(M, K // MX_BLOCK)
+    sb = np.asarray(sb_bits, np.uint8).reshape(N, K // MX_BLOCK)
+    d = np.empty(rows.size)
+    bound = np.empty(rows.size)
+    for s0 in range(0, rows.size, chunk):
+        r = rows[s0:s0 + chunk]
+        q = cols[s0:s0 + chunk]
+        a = decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, r)), a_dtype)
+        b = decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, q)), b_dtype)
+        a = a * np.repeat(e8m0_bits_to_f64(sa[r]), MX_BLOCK, axis=1)
+        b = b * np.repeat(e8m0_bits_to_f64(sb[q]), MX_BLOCK, axis=1)
+        prod = a * b
+        d[s0:s0 + chunk] = prod.sum(axis=1)
+        bound[s0:s0 + chunk] = np.abs(prod).sum(axis=1)
+    if beta == 1.0:
+        d = d + np.asarray(c, dtype=np.float32).reshape(M, N)[rows, cols].astype(np.float64)
+    return d, bound
+
+
 def abs_bound_mx(a_bits, b_bits, sa_bits, sb_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype):
     """sum_k |scaled A_ik · scaled B_kj| for every (i, j)."""
     if K == 0:

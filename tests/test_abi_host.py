@@ -30,13 +30,14 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert {"tile_gemm", "tile_copy", "tile_copy_ex", "tile_copy_plan", "tile_gemm_plan",
-            "tile_gemm_fp8", "tile_gemm_fp8_plan", "tile_copy_partition", "tile_last_error",
+            "tile_gemm_fp8", "tile_gemm_fp8_plan", "tile_gemm_mx", "tile_gemm_mx_plan",
+            "tile_copy_partition", "tile_last_error",
             "tile_abi_version"} <= set(names)
     lib = tg.lib()
     for n in names:
         assert hasattr(lib, n), n
         assert n in tg._SIGS, n   # the binding marshals every declared entry point
-    assert tg.tile_abi_version() == 2
+    assert tg.tile_abi_version() == 3
 
 
 # ------------------------------------------------------------- planner ----
@@ -312,3 +313,43 @@ def test_fp8_kernel_choice():
     assert p.kernel == tg.TG_GEMM_FILL
     p = tg.tile_gemm_fp8_plan(None, None, None, None, 0, 16, 128, 0, 1, 0.0, e4, e4)
     assert p.kernel == tg.TG_GEMM_NONE
+
+
+# ---------------------------------------------------- block-scaled fp8 ----
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (8, 16, 128), (16, 16, 64), (0, 16, 128),
+                                   (16, 16, 0), (272, 528, 384)])
+@pytest.mark.parametrize("a_dt", [tg.TG_FP8_E4M3, tg.TG_FP8_E5M2, tg.TG_F16])
+@pytest.mark.parametrize("beta", [0.0, 1.0, 2.0])
+def test_mx_validation_matches_oracle(M, N, K, a_dt, beta):
+    want = ogemm.accepts_fp8(M, N, K, ODT8.get(a_dt, "other"), "e4m3", beta=beta)
+    SA_ADDR, SB_ADDR = 1 << 36, 1 << 37
+    try:
+        tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, SA_ADDR, SB_ADDR, C_ADDR, D_ADDR, M, N, K, 0, 1, beta,
+                             a_dt, tg.TG_FP8_E4M3)
+        got = (True, None)
+    except tg.TileError as e:
+        got = (False, CATEGORY.get(e.status, "other"))
+    assert got == want
+
+
+def test_mx_scale_arguments():
+    e4 = tg.TG_FP8_E4M3
+    SA_ADDR, SB_ADDR = 1 << 36, 1 << 37
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm_mx(A_ADDR, B_ADDR, None, SB_ADDR, None, D_ADDR, 256, 256, 256, 0, 1, 0.0, e4, e4)
+    assert e.value.status == tg.TG_E_NULL
+    with pytest.raises(tg.TileError) as e:
+        tg.tile_gemm_mx(A_ADDR, B_ADDR, SA_ADDR + 2, SB_ADDR, None, D_ADDR, 256, 256, 256, 0, 1, 0.0,
+                        e4, e4)
+    assert e.value.status == tg.TG_E_ALIGN
+    with pytest.raises(tg.TileError) as e:   # D overlaps SB ([N][K/32] bytes)
+        tg.tile_gemm_mx(A_ADDR, B_ADDR, SA_ADDR, D_ADDR + 64, None, D_ADDR, 256, 256, 256, 0, 1, 0.0,
+                        e4, e4)
+    assert e.value.status == tg.TG_E_ALIAS
+    # K == 0 reads no scales
+    p = tg.tile_gemm_mx_plan(None, None, None, None, C_ADDR, D_ADDR, 32, 16, 0, 0, 1, 1.0, e4, e4)
+    assert p.kernel == tg.TG_GEMM_FILL
+    p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, SA_ADDR, SB_ADDR, None, D_ADDR, 8192, 8192, 8192, 1, 0,
+                             0.0, e4, tg.TG_FP8_E5M2)
+    assert (p.kernel, p.block_m, p.block_k, p.grid, p.loader) == (tg.TG_GEMM_TILED, 256, 128, 1024, 1)

@@ -149,3 +149,15 @@ def test_mx_mutants_are_caught(kind):
             return True
         return False
     assert any(caught(p) for p in MX_PINS)
+
+
+def test_sampled_equals_full():
+    M, N, K = 96, 80, 256
+    for ta, tb in ((False, True), (True, False)):
+        a, b, sa, sb, c = mx_inputs(M, N, K, "e5m2", "e4m3", ta, tb, 1.0, 55)
+        full = G.gemm_mx_ref(a, b, sa, sb, c, M, N, K, ta, tb, 1.0, "e5m2", "e4m3")
+        bound = G.abs_bound_mx(a, b, sa, sb, M, N, K, ta, tb, "e5m2", "e4m3")
+        rows, cols = synth.sample_points(M, N, 8, count=400, tile=(16, 16))
+        d, bd = G.gemm_mx_ref_at(a, b, sa, sb, c, M, N, K, ta, tb, 1.0, "e5m2", "e4m3", rows, cols)
+        assert np.allclose(d, full[rows, cols], rtol=1e-13, atol=1e-13)
+        assert np.allclose(bd, bound[rows, cols], rtol=1e-13, atol=0)

@@ -87,6 +87,10 @@ _SIGS = {
                              _VP]),
     "tile_gemm_fp8_plan": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT,
                                   _INT, ctypes.POINTER(GemmPlan)]),
+    "tile_gemm_mx": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F, _INT,
+                            _INT, _VP]),
+    "tile_gemm_mx_plan": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _INT, _INT, _F,
+                                 _INT, _INT, ctypes.POINTER(GemmPlan)]),
     "tile_copy": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
                          ctypes.POINTER(Layout), _VP]),
     "tile_copy_ex": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
@@ -205,6 +209,22 @@ def tile_gemm_fp8_plan(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dty
     _check(lib().tile_gemm_fp8_plan(_addr(A), _addr(B), _addr(C), _addr(D), M, N, K, int(transA),
                                     int(transB), float(beta), int(a_dtype), int(b_dtype),
                                     ctypes.byref(out)))
+    return out
+
+
+def tile_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype,
+                 stream=None):
+    """Block-scaled fp8 GEMM through the library (see include/tilegemm.h)."""
+    _check(lib().tile_gemm_mx(_addr(A), _addr(B), _addr(SA), _addr(SB), _addr(C), _addr(D), M, N,
+                              K, int(transA), int(transB), float(beta), int(a_dtype),
+                              int(b_dtype), _stream(stream)))
+
+
+def tile_gemm_mx_plan(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype):
+    out = GemmPlan()
+    _check(lib().tile_gemm_mx_plan(_addr(A), _addr(B), _addr(SA), _addr(SB), _addr(C), _addr(D),
+                                   M, N, K, int(transA), int(transB), float(beta), int(a_dtype),
+                                   int(b_dtype), ctypes.byref(out)))
     return out
 
 

@@ -122,6 +122,22 @@ int validate_gemm_fp8(const void* A, const void* B, const float* C, const float*
   return TG_OK;
 }
 
+// tile_gemm_mx: the fp8 checks plus the block scales SA [M][K/32] and SB [N][K/32]
+// (present when K > 0, 4-byte aligned for the 4-byte scale loads, not overlapping D).
+int validate_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                     const float* C, const float* D, int64_t M, int64_t N, int64_t K, int transA,
+                     int transB, float beta, int a_dtype, int b_dtype) {
+  int st = validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
+  if (st || M == 0 || N == 0 || K == 0) return st;
+  if (!SA || !SB) return fail(TG_E_NULL, "SA or SB is NULL");
+  if ((uintptr_t)SA % 4 || (uintptr_t)SB % 4)
+    return fail(TG_E_ALIGN, "SA and SB must be 4-byte aligned");
+  const int64_t dbytes = M * N * 4;
+  if (overlaps(D, dbytes, SA, M * (K / 32)) || overlaps(D, dbytes, SB, N * (K / 32)))
+    return fail(TG_E_ALIAS, "D overlaps SA or SB");
+  return TG_OK;
+}
+
 void fill_plan(const GemmConfig& c, tg_gemm_plan* out) {
   out->kernel = c.kernel;
   out->block_m = c.bm;
@@ -288,7 +304,7 @@ extern "C" {
 
 const char* tile_last_error(void) { return g_last_error.c_str(); }
 
-int tile_abi_version(void) { return 2; }
+int tile_abi_version(void) { return 3; }
 
 int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D, int64_t M,
                    int64_t N, int64_t K, int transA, int transB, float beta, int dtype,
@@ -336,12 +352,10 @@ int tile_gemm_fp8_plan(const void* A, const void* B, const float* C, const float
   return TG_OK;
 }
 
-int tile_gemm_fp8(const void* A, const void* B, const float* C, float* D, int64_t M, int64_t N,
-                  int64_t K, int transA, int transB, float beta, int a_dtype, int b_dtype,
-                  void* stream) {
-  clear_error();
-  int st = validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
-  if (st) return st;
+static int run_gemm_fp8(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                        const float* C, float* D, int64_t M, int64_t N, int64_t K, int transA,
+                        int transB, float beta, int a_dtype, int b_dtype, bool scaled,
+                        void* stream) {
   const GemmConfig cfg = choose_gemm_fp8(M, N, K);
   if (cfg.kernel == TG_GEMM_NONE) return TG_OK;
   if (cfg.kernel == TG_GEMM_FILL && beta == 1.0f && C == D) return TG_OK;
@@ -357,11 +371,45 @@ int tile_gemm_fp8(const void* A, const void* B, const float* C, float* D, int64_
   if (cfg.kernel == TG_GEMM_FILL) return launch_gemm(g, cfg, 0, 0, TG_BF16, stream);
   g.tiles_m = (int32_t)((M + 255) / 256);
   g.tiles_n = (int32_t)((N + 255) / 256);
+  g.SA = SA;
+  g.SB = SB;
   const hipError_t e = launch_gemm_fp8(g, cfg.grid, transA, transB, a_dtype, b_dtype,
-                                       cfg.bounds != 0, (hipStream_t)stream);
+                                       cfg.bounds != 0, scaled, (hipStream_t)stream);
   if (e != hipSuccess)
-    return fail(TG_E_HIP, std::string("tile_gemm_fp8 launch: ") + hipGetErrorString(e));
+    return fail(TG_E_HIP, std::string(scaled ? "tile_gemm_mx launch: " : "tile_gemm_fp8 launch: ") +
+                              hipGetErrorString(e));
   return TG_OK;
+}
+
+int tile_gemm_fp8(const void* A, const void* B, const float* C, float* D, int64_t M, int64_t N,
+                  int64_t K, int transA, int transB, float beta, int a_dtype, int b_dtype,
+                  void* stream) {
+  clear_error();
+  int st = validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
+  if (st) return st;
+  return run_gemm_fp8(A, B, nullptr, nullptr, C, D, M, N, K, transA, transB, beta, a_dtype,
+                      b_dtype, false, stream);
+}
+
+int tile_gemm_mx_plan(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                      const float* C, const float* D, int64_t M, int64_t N, int64_t K, int transA,
+                      int transB, float beta, int a_dtype, int b_dtype, tg_gemm_plan* out) {
+  clear_error();
+  if (!out) return fail(TG_E_ARG, "out is NULL");
+  int st = validate_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
+  if (st) return st;
+  fill_plan(choose_gemm_fp8(M, N, K), out);
+  return TG_OK;
+}
+
+int tile_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                 const float* C, float* D, int64_t M, int64_t N, int64_t K, int transA, int transB,
+                 float beta, int a_dtype, int b_dtype, void* stream) {
+  clear_error();
+  int st = validate_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
+  if (st) return st;
+  return run_gemm_fp8(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype, true,
+                      stream);
 }
 
 int tile_copy_plan(const void* src, const void* dst, const int64_t shape[2], int dtype,

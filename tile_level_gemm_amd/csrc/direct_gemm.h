@@ -56,14 +56,17 @@ constexpr int BM = 256, BN = 256;
 constexpr int kRowBytes = 128;   // bytes of K per operand row and stage
 constexpr int kGroupM = 8;       // tile-rows per scheduling group (measured: 8 beats 2, 4, 16)
 
-// Format codes of the template's DT parameter: TG_F16 / TG_BF16, or an fp8 pair
-// kF8 + 2·a + b with a, b the MFMA's operand format codes (0 = e4m3, 1 = e5m2).
-constexpr int kF8 = 16;
+// Format codes of the template's DT parameter: TG_F16 / TG_BF16, an fp8 pair kF8 + 2·a + b,
+// or a block-scaled fp8 pair kMX + 2·a + b, with a, b the MFMA's operand format codes
+// (0 = e4m3, 1 = e5m2).
+constexpr int kF8 = 16, kMX = 32;
 constexpr int fp8_code(int a_fmt, int b_fmt) { return kF8 + 2 * a_fmt + b_fmt; }
+constexpr int mx_code(int a_fmt, int b_fmt) { return kMX + 2 * a_fmt + b_fmt; }
 
 template <int DT>
 struct Elem {
   static constexpr bool kFp8 = DT >= kF8;
+  static constexpr bool kScaled = DT >= kMX;      // E8M0 scale per 32 K of each row / column
   static constexpr int kBytes = kFp8 ? 1 : 2;
   static constexpr int kBK = kRowBytes / kBytes;   // K elements per stage
   static constexpr int kSteps = kFp8 ? 2 : 4;      // MFMA K steps per stage
@@ -81,11 +84,19 @@ __device__ __forceinline__ f32x16 mfma32(F a, F b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   else
     // cbsz / blgp name A's and B's formats; no block scales (scale operands 0).  Lane l
-    // carries 32 bytes of K of row / column l % 32; A and B put the same K in the same byte,
-    // so the sum is over matching K whatever order the unit reduces them in.
+    // carries 32 bytes of K of row / column l % 32; A and B put the same K in the same byte.
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, (DT - kF8) >> 1,
-        (DT - kF8) & 1, 0, 0, 0, 0);
+        __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, (DT & 3) >> 1, DT & 1, 0,
+        0, 0, 0);
+}
+// Block-scaled fp8 MFMA: the unit's 32-K block q of the 64-K step is bytes 16q .. 16q+15 of
+// both lane halves (lanes n and n + 32 of row / column n); its scale is the byte OPSEL selects
+// from the scale register of lane n + 32q.
+template <int DT, int OPSEL, class F>
+__device__ __forceinline__ f32x16 mfma32s(F a, F b, f32x16 c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, (DT & 3) >> 1, DT & 1,
+      OPSEL, (int)sa, OPSEL, (int)sb);
 }
 
 // ---- LDS layouts --------------------------------------------------------------------
@@ -161,16 +172,18 @@ __device__ __forceinline__ void mn8_dma_offsets(int64_t ld, int wave, int lane, 
 }
 
 // K-major fragment reads (ds_read_b128) of 32-row tile t: lane l reads row base + 32t + l%32.
-// 16-bit, K step s: chunk 2s + l/32 (offset u = s).  fp8, K step s: chunks 4s + 2(l/32) + q
-// for q = 0, 1 (offsets u = 2s + q) — 32 bytes of K per lane.  sk(row) depends on the lane
-// only (32t is a multiple of 16), the chunk term on u: one byte offset per u; tiles are
-// +4096-byte immediates.
+// 16-bit, K step s: chunk 2s + l/32 (offset u = s).  fp8, K step s: chunks 4s + 2q + l/32
+// for q = 0, 1 (offsets u = 2s + q) — 32 bytes of K per lane.  The fp8 order follows the
+// unit's 32-K blocks: block q of a 64-K step is bytes 16q .. 16q+15 of both lane halves
+// (measured with per-half scales), so lane half h holds K 16h .. 16h+15 of each block.
+// sk(row) depends on the lane only (32t is a multiple of 16), the chunk term on u: one byte
+// offset per u; tiles are +4096-byte immediates.
 template <bool FP8>
 __device__ __forceinline__ void km_frag_offsets(int row_base, int lane, uint32_t (&off)[4]) {
   const uint32_t r = (uint32_t)(row_base + (lane & 31));
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const uint32_t kc = FP8 ? (uint32_t)(4 * (u >> 1) + 2 * (lane >> 5) + (u & 1))
+    const uint32_t kc = FP8 ? (uint32_t)(4 * (u >> 1) + 2 * (u & 1) + (lane >> 5))
                             : (uint32_t)(2 * u + (lane >> 5));
     off[u] = r * 128u + ((kc ^ sk<SKV>(r)) << 4);
   }
@@ -195,15 +208,16 @@ __device__ __forceinline__ void mn_frag_offsets(int mn_base, int lane, uint32_t 
 
 // M/N-major fp8 fragment of 32-column tile t, K step s (64 k), read u = 0..3 (four
 // ds_read_b64_tr_b8): within each 16-lane group g, lane j receives byte j%8 of the 8-byte
-// reads of lanes 2k + j/8 (k = 0..7).  So lane l = 16g + j reads k-row 64s + 32(g/2) + 8u +
-// j/2 at columns mn_base + 32t + 16(g&1) + 8(j&1) .. +7, and receives k 32(g/2) + 8u .. +7 of
-// column mn_base + 32t + l%32 — the K order of the K-major fp8 fragment.  s8 depends on j only
-// (s and u add multiples of 8 rows); the chunk of tile t is kept per t (2t carries into the
-// swizzled bits), s and u are immediates.
+// reads of lanes 2k + j/8 (k = 0..7).  So lane l = 16g + j reads k-row 64s + kr(u) + 16(g/2)
+// + j/2, kr(u) = 32(u/2) + 8(u%2), at columns mn_base + 32t + 16(g&1) + 8(j&1) .. +7, and
+// receives its bytes 8u .. 8u+7 = k kr(u) + 16(g/2) .. +7 of column mn_base + 32t + l%32 —
+// the K order of the K-major fp8 fragment.  s8 depends on j only (s, u and g/2 add multiples
+// of 8 rows); the chunk of tile t is kept per t (2t carries into the swizzled bits), s and u
+// are immediates.
 template <int T>
 __device__ __forceinline__ void mn8_frag_offsets(int mn_base, int lane, uint32_t (&off)[4]) {
   const uint32_t g = (uint32_t)lane >> 4, j = (uint32_t)lane & 15u;
-  const uint32_t krow = 32u * (g >> 1) + (j >> 1);
+  const uint32_t krow = 16u * (g >> 1) + (j >> 1);
   const uint32_t x = s8(krow);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -296,7 +310,7 @@ struct Operand {
       u32x8 out;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint8_t* p = stage + frag[t] + (64 * s + 8 * u) * 256;
+        const uint8_t* p = stage + frag[t] + (64 * s + 32 * (u >> 1) + 8 * (u & 1)) * 256;
         const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
         out[2 * u] = (uint32_t)v[0];
         out[2 * u + 1] = (uint32_t)v[1];
@@ -375,6 +389,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[BN * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[BM * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sb1[BN * kRowBytes];
+  // block scales of one stage (scaled fp8 only): A's 256 rows x 4 bytes, then B's
+  __shared__ __attribute__((aligned(1024))) uint8_t qs0[EL::kScaled ? 2048 : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs1[EL::kScaled ? 2048 : 1];
 
   // tile scheduler: XCD-contiguous ranges, grouped tile-rows (as gemm_tiled)
   const int nb = (int)gridDim.x;
@@ -428,58 +445,122 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   //   kt+1's first fragments and the DMA of stage kt+2 into `cur`.
   // The last two stages are peeled off the loop so the steady-state body is branch free.
   const int KT = g.K / BK;   // >= 1, of shape KS
+
+  // Block scales (scaled fp8): each stage's 4 scale bytes of every row of the block (K/32
+  // bytes per row, 4 per 128-K stage) go to LDS by one 4-byte-per-lane DMA per wave: waves
+  // 0-3 carry A's 256 rows, 64 each, waves 4-7 B's.  Rows past M or N read as zero.
+  __amdgpu_buffer_rsrc_t qrsrc;
+  uint32_t qvoff = 0, qlds = 0;
+  if constexpr (EL::kScaled) {
+    const int kb = g.K / 32;
+    const bool is_a = wave < 4;
+    const int row0 = is_a ? m0 : n0, rows = is_a ? g.M : g.N;
+    const uint8_t* qbase = (is_a ? g.SA : g.SB) + (int64_t)row0 * kb;
+    qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, (rows - row0) * kb, 0x00020000);
+    qvoff = (uint32_t)(64 * (wave & 3) + lane) * (uint32_t)kb;
+    qlds = (is_a ? 0u : 1024u) + 256u * (uint32_t)(wave & 3);
+  }
+  auto qload = [&](uint32_t kt, uint8_t* q) {
+    if constexpr (EL::kScaled)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(q + qlds), 4, qvoff, 4u * kt, 0, 0);
+  };
+  // This lane's scales of one stage for A tile i / B tile j, shifted so that byte 2s holds
+  // the block of K step s this lane supplies (K half lane / 32).  One per-lane LDS offset per
+  // operand; tiles are immediates.
+  uint32_t qa[TM], qb[TN], qbn[TN];
+  const uint32_t qsh = 8u * (uint32_t)(lane >> 5);
+  const uint32_t qoa = 4u * (uint32_t)(wm + (lane & 31)), qob = 1024u + 4u * (uint32_t)(wn + (lane & 31));
+  auto qread_a = [&](const uint8_t* q, int i) -> uint32_t {
+    return *(const uint32_t*)(q + qoa + 128 * i) >> qsh;
+  };
+  auto qread_b = [&](const uint8_t* q, int j) -> uint32_t {
+    return *(const uint32_t*)(q + qob + 128 * j) >> qsh;
+  };
+  auto qread = [&](const uint8_t* q) {
+    if constexpr (EL::kScaled) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) qa[i] = qread_a(q, i);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) qb[j] = qread_b(q, j);
+    }
+  };
+
   oa.load(0u, lda, sa0, wave);
   ob.load(0u, ldb, sb0, wave);
+  qload(0u, qs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frag a[TM], b[TN], an[TM], bn[TN];
   oa.frags(sa0, 0, a);
   ob.frags(sb0, 0, b);
+  qread(qs0);
   if constexpr (KS != kSingle) {
     oa.load(adv_a, lda, sa1, wave);
     ob.load(adv_b, ldb, sb1, wave);
+    qload(1u, qs1);
   }
 
   constexpr int kMfma = TM * TN;
   constexpr int kReads = OA::kReads + OB::kReads;
-  constexpr int kDma = 2 * PER;
+  constexpr int kDma = 2 * PER + (EL::kScaled ? 1 : 0);
 
   // fp8 K step in place: this step's MFMAs, tile by tile of A, while the next step's
   // fragments (K step `sn` of stages `xa` / `xb`) are read — B's into bn, A tile i's into
   // a[i] once its MFMAs are issued.  READ false: last step of the last stage.
-  auto step_inplace = [&](const uint8_t* xa, const uint8_t* xb, int sn, auto read, auto dma) {
+  // MS: the K step of the MFMAs issued (selects the scale byte); XQ: the next stage's scales
+  // to read (nullptr: none).
+  auto step_inplace = [&](const uint8_t* xa, const uint8_t* xb, int sn, auto read, auto dma,
+                          auto MS, const uint8_t* xq) {
     constexpr bool kRead = decltype(read)::value;
+    constexpr int ms = decltype(MS)::value;
+    // the next stage's scales: B's into qbn now, A tile i's into qa[i] after its MFMAs
+    constexpr bool kQ = EL::kScaled && kRead && ms == NS - 1;
     if constexpr (kRead) ob.frags(xb, sn, bn);
+    if constexpr (kQ) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) qbn[j] = qread_b(xq, j);
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<DT>(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (EL::kScaled) acc[i][j] = mfma32s<DT, 2 * ms>(a[i], b[j], acc[i][j], qa[i], qb[j]);
+        else acc[i][j] = mfma32<DT>(a[i], b[j], acc[i][j]);
+      }
       if constexpr (kRead) oa.frag_tile(xa, sn, i, a[i]);
+      if constexpr (kQ) qa[i] = qread_a(xq, i);
     }
-    constexpr int nra = kRead ? OA::kTileReads : 0, nrb = kRead ? OB::kReads : 0;
+    constexpr int nra = kRead ? OA::kTileReads + (kQ ? 1 : 0) : 0;
+    constexpr int nrb = kRead ? OB::kReads + (kQ ? TN : 0) : 0;
     if constexpr (decltype(dma)::value) interleave_inplace<TN, kMfma, nra, nrb, kDma>();
     else interleave_inplace<TN, kMfma, nra, nrb, 0>();
     if constexpr (kRead) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) b[j] = bn[j];
     }
+    if constexpr (kQ) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) qb[j] = qbn[j];
+    }
   };
 
   // One K stage.  DMA: also load stage kt+2 into the buffer this stage frees; NEXT: read
   // the next stage's first fragments (false only for the last stage).
-  auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, int kt,
-                   auto dma, auto next) {
+  auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, uint8_t* cq,
+                   const uint8_t* nq, int kt, auto dma, auto next) {
     if constexpr (EL::kFp8) {
-#pragma unroll
-      for (int s = 0; s < NS - 1; ++s) step_inplace(ca, cb, s + 1, std::true_type{}, std::false_type{});
+      static_assert(NS == 2, "fp8 stages are two 64-K steps");
+      step_inplace(ca, cb, 1, std::true_type{}, std::false_type{}, std::integral_constant<int, 0>{},
+                   nullptr);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if constexpr (decltype(dma)::value) {
         oa.load((uint32_t)(kt + 2) * adv_a, lda, ca, wave);
         ob.load((uint32_t)(kt + 2) * adv_b, ldb, cb, wave);
+        qload((uint32_t)(kt + 2), cq);
       }
-      step_inplace(na, nb_, 0, next, dma);
+      step_inplace(na, nb_, 0, next, dma, std::integral_constant<int, 1>{}, nq);
       return;
     }
 #pragma unroll
@@ -585,21 +666,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   using T_ = std::true_type;
   using F_ = std::false_type;
   if constexpr (KS == kSingle) {
-    stage(sa0, sb0, sa1, sb1, 0, F_{}, F_{});
+    stage(sa0, sb0, sa1, sb1, qs0, qs1, 0, F_{}, F_{});
   } else {
     constexpr int odd = KS == kOdd ? 1 : 0;
     int kt = 0;
     for (; kt + 2 + odd < KT; kt += 2) {
-      stage(sa0, sb0, sa1, sb1, kt, T_{}, T_{});
-      stage(sa1, sb1, sa0, sb0, kt + 1, T_{}, T_{});
+      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, T_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, T_{}, T_{});
     }
     if constexpr (KS == kEven) {
-      stage(sa0, sb0, sa1, sb1, kt, F_{}, T_{});
-      stage(sa1, sb1, sa0, sb0, kt + 1, F_{}, F_{});
+      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, F_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, F_{}, F_{});
     } else {
-      stage(sa0, sb0, sa1, sb1, kt, T_{}, T_{});
-      stage(sa1, sb1, sa0, sb0, kt + 1, F_{}, T_{});
-      stage(sa0, sb0, sa1, sb1, kt + 2, F_{}, F_{});
+      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, T_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, F_{}, T_{});
+      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt + 2, F_{}, F_{});
     }
   }
   epilogue();

@@ -1,6 +1,6 @@
-// Host launch of the fp8 instantiations of the direct-load GEMM template, one operand
-// orientation per translation unit (gemm_fp8.hip, gemm_fp8_km.hip, gemm_fp8_mk.hip,
-// gemm_fp8_mm.hip) so that they compile in parallel.  Internal header.
+// Host launch of the fp8 and block-scaled fp8 instantiations of the direct-load GEMM template,
+// one operand orientation per translation unit (gemm_fp8*.hip, gemm_mx*.hip) so that they
+// compile in parallel.  Internal header.
 #pragma once
 
 #include "direct_gemm.h"
@@ -9,12 +9,14 @@ namespace tg {
 
 // A_MN: A stored [K][M]; B_MN: B stored [K][N].  af / bf: the MFMA format codes (0 = e4m3,
 // 1 = e5m2).  The stage-count shape (K / 128 even, odd, or one) is fixed at compile time.
-template <bool A_MN, bool B_MN>
+// SCALED: block-scaled fp8 (g.SA, g.SB hold the E8M0 scales).
+template <bool A_MN, bool B_MN, bool SCALED = false>
 hipError_t launch_fp8_layout(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds,
                              hipStream_t s) {
   auto go = [&](auto AF, auto BF, auto BOUNDS, auto KS) {
-    hipLaunchKernelGGL((gemm_direct<A_MN, B_MN, fp8_code(decltype(AF)::value, decltype(BF)::value),
-                                    2, 4, decltype(BOUNDS)::value, decltype(KS)::value>),
+    constexpr int dt = SCALED ? mx_code(decltype(AF)::value, decltype(BF)::value)
+                              : fp8_code(decltype(AF)::value, decltype(BF)::value);
+    hipLaunchKernelGGL((gemm_direct<A_MN, B_MN, dt, 2, 4, decltype(BOUNDS)::value, decltype(KS)::value>),
                        dim3((unsigned)grid), dim3(512), 0, s, g);
     return hipGetLastError();
   };
@@ -39,5 +41,9 @@ hipError_t launch_fp8_kk(const GemmArgs& g, int64_t grid, int af, int bf, bool b
 hipError_t launch_fp8_km(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
 hipError_t launch_fp8_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
 hipError_t launch_fp8_mm(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
+hipError_t launch_mx_kk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
+hipError_t launch_mx_km(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
+hipError_t launch_mx_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
+hipError_t launch_mx_mm(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
 
 }  // namespace tg

@@ -1,0 +1,12 @@
+// Block-scaled fp8 GEMM ([SYNC-GEMM] 七: block-scaled operands, SFA / SFB) instantiations of the
+// direct-load kernel template for A stored [K,M] and B stored [K,N].
+#include "gemm_fp8_launch.h"
+
+namespace tg {
+
+hipError_t launch_mx_mm(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds,
+                        hipStream_t s) {
+  return launch_fp8_layout<true, true, true>(g, grid, af, bf, bounds, s);
+}
+
+}  // namespace tg

@@ -73,6 +73,8 @@ struct GemmArgs {
   int32_t M, N, K;
   int32_t use_c;
   int32_t tiles_m, tiles_n;
+  const uint8_t* SA;   // block-scaled fp8: E8M0 scales of A [M][K/32] and B [N][K/32]
+  const uint8_t* SB;
 };
 
 struct GemmConfig {
@@ -95,8 +97,9 @@ bool direct_gemm_fits(int64_t M, int64_t N, int64_t K);
 // fp8 GEMM (any operand orientation): 256x256 blocks, 512 threads, grid =
 // ceil(M/256)·ceil(N/256); bounds = M or N not a multiple of 256.
 GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K);
+// scaled: block-scaled fp8 (E8M0 scales in g.SA, g.SB).
 hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int a_dtype,
-                           int b_dtype, bool bounds, hipStream_t s);
+                           int b_dtype, bool bounds, bool scaled, hipStream_t s);
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
                               hipStream_t s);
 
