@@ -36,7 +36,8 @@ METRIC = "GEMM TFLOP/s + % MFMA peak (bf16 8192³); tile-copy GB/s + % HBM peak"
 
 KERNEL_SOURCES = {
     "gemm": ("gemm_direct.hip", "direct_gemm.h", "gemm_kernels.hip", "lds_layout.h", "tg_internal.h"),
-    "fp8": ("gemm_fp8.hip", "direct_gemm.h", "tg_internal.h"),
+    "fp8": ("gemm_fp8.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
+    "mx": ("gemm_mx_kk.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
 }
 
@@ -71,6 +72,8 @@ TRAFFIC_KERNELS = {
                                     2 * M * K * 2 + M * N * 4),
     "gemm_fp8_256x256_e4m3_tn": ("gemm_direct<false, false, 16, 2, 4, false, 0>", "fp8",
                                  2 * M * K + M * N * 4),
+    "gemm_mx_256x256_e4m3_tn": ("gemm_direct<false, false, 32, 2, 4, false, 0>", "mx",
+                                2 * M * K + 2 * M * (K // 32) + M * N * 4),
     "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4>", "copy", 2 * ROWS * COLS * 2),
 }
 
@@ -277,7 +280,30 @@ def main():
                                       "e4m3", rows, cols)
     f8_ok, f8_worst = og.check_fp8(D.cpu().numpy()[rows, cols], ref8, bound8, fin[0], fin[1], M, N,
                                    K, False, True, "e4m3", "e4m3", rows, cols)
-    del A8, B8
+
+    # block-scaled (MX) e4m3 GEMM: E8M0 scales per 32 K, 2^-10 .. 2^10
+    print("bench: mx gemm", file=sys.stderr, flush=True)
+    g = synth.rng(64)
+    sa = g.integers(117, 138, size=(M, K // 32)).astype(np.uint8)
+    sb = g.integers(117, 138, size=(N, K // 32)).astype(np.uint8)
+    SA = torch.from_numpy(sa).to(dev)
+    SB = torch.from_numpy(sb).to(dev)
+    for _ in range(args.warmup):
+        tg.tile_gemm_mx(A8, B8, SA, SB, None, D, M, N, K, 0, 1, 0.0, e4, e4)
+    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for ev in mev:
+        ev[0].record()
+        tg.tile_gemm_mx(A8, B8, SA, SB, None, D, M, N, K, 0, 1, 0.0, e4, e4)
+        ev[1].record()
+    torch.cuda.synchronize()
+    mx_ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in mev]))
+    mx_tflops = flops / (mx_ms * 1e-3) / 1e12
+    refm, boundm = og.gemm_mx_ref_at(fin[0], fin[1], sa, sb, None, M, N, K, False, True, 0.0, "e4m3",
+                                     "e4m3", rows, cols)
+    mx_ok, mx_worst = og.check_fp8(D.cpu().numpy()[rows, cols], refm, boundm, fin[0], fin[1], M, N, K,
+                                   False, True, "e4m3", "e4m3", rows, cols, sa_bits=sa, sb_bits=sb)
+    del A8, B8, SA, SB
 
     base = None
     if not args.no_cpu_baseline:
@@ -326,6 +352,15 @@ def main():
                          "unit": "TFLOP/s", "frac": round(f8_tflops / PEAK_FP8_TFLOPS, 4),
                          "traffic": traffic_for("gemm_fp8_256x256_e4m3_tn")},
             "parity": {"sampled_ok": bool(f8_ok), "worst_err_over_tol": round(f8_worst, 5)},
+        },
+        "gemm_mx_e4m3_tn": {
+            "value": round(mx_tflops, 3), "unit": "TFLOP/s", "avg_ms": round(mx_ms, 5),
+            "workload": "tile_gemm_mx 8192x8192x8192, A e4m3 [M,K], B e4m3 [N,K], E8M0 scales per "
+                        "32 K in 2^-10..2^10, fp32 D, beta=0",
+            "roofline": {"bound": "mfma", "achieved": round(mx_tflops, 3), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(mx_tflops / PEAK_FP8_TFLOPS, 4),
+                         "traffic": traffic_for("gemm_mx_256x256_e4m3_tn")},
+            "parity": {"sampled_ok": bool(mx_ok), "worst_err_over_tol": round(mx_worst, 5)},
         },
         "parity": {"gemm_sampled_ok": bool(g_ok), "gemm_worst_err_over_tol": round(g_worst, 5),
                    "copy_bit_exact": c_ok},
