@@ -275,11 +275,125 @@ int tile_copy_partition(int64_t rows, int64_t cols, int elem_bits, int threads,
                         const tg_layout* other, int64_t other_base,
                         tg_copy_phase* out);
 
+/* ---------------------------------------------------------------------------------------
+ * Register fragments ([SYNC-GEMM] 一 and 四: the register-level gemm takes its A / B fragments
+ * and its C / D accumulator in registers, which the caller fills first — typically by a copy
+ * of the ldstmatrix kind; [VEC-AUTO] closing reading list: vec_auto's register path, whose
+ * partition comes from the register layout's thread axis, and the warp-collective ldstmatrix
+ * copy).  On gfx950 those registers are the operands and accumulator of the matrix
+ * instructions.  A fragment kind is a tile_rows x tile_cols tile and the map
+ * (lane l < 64, register element e < elems) -> (row, col) of the tile below.
+ *
+ * A register image holds what the wavefront's registers hold: for each tile, in row-major
+ * tile order over the matrix, 64 lanes x elems elements, each lane's elements contiguous in
+ * register order (tile t, lane l, element e at (t*64 + l)*elems + e).  Every lane's
+ * registers are groups of 16 bytes that run along one axis of the tile (a "run").
+ * ------------------------------------------------------------------------------------- */
+typedef enum tg_frag_kind {
+  TG_FRAG_A16_32x32x16 = 1,  /* 32 x 16, 16-bit, 8 per lane: (l%32, 8(l/32) + e)        */
+  TG_FRAG_B16_32x32x16 = 2,  /* 16 x 32, 16-bit, 8 per lane: (8(l/32) + e, l%32)        */
+  TG_FRAG_A16_16x16x32 = 3,  /* 16 x 32, 16-bit, 8 per lane: (l%16, 8(l/16) + e)        */
+  TG_FRAG_B16_16x16x32 = 4,  /* 32 x 16, 16-bit, 8 per lane: (8(l/16) + e, l%16)        */
+  TG_FRAG_A8_32x32x64 = 5,   /* 32 x 64, 8-bit, 32 per lane: (l%32, 32(e/16) + 16(l/32) + e%16) */
+  TG_FRAG_B8_32x32x64 = 6,   /* 64 x 32, 8-bit, 32 per lane: (32(e/16) + 16(l/32) + e%16, l%32) */
+  TG_FRAG_C32_32x32 = 7,     /* 32 x 32 fp32 accumulator, 16 per lane: (8(e/4) + 4(l/32) + e%4, l%32) */
+  TG_FRAG_C32_16x16 = 8      /* 16 x 16 fp32 accumulator, 4 per lane: (4(l/16) + e, l%16) */
+} tg_frag_kind;
+
+typedef enum tg_frag_route {
+  TG_FRAG_AUTO = 0,    /* DIRECT when its transfers are 128-bit, else LDS when LDS is usable */
+  TG_FRAG_DIRECT = 1,  /* global <-> registers; the width rule on the registers' runs */
+  TG_FRAG_LDS = 2      /* global <-> LDS with 128-bit transfers, LDS <-> registers with
+                          ds_read_b128 / ds_write_b128 along memory lines, and
+                          ds_read_b64_tr_b16 / ds_read_b64_tr_b8 across them */
+} tg_frag_route;
+
+typedef struct tg_frag_plan {
+  int32_t route;           /* TG_FRAG_DIRECT or TG_FRAG_LDS */
+  int32_t vec;             /* elements per global transfer */
+  int32_t vec_bits;        /* vec * element bits: 128, 64, 32, 16 or 8 */
+  int32_t transposed;      /* 1 when each run crosses memory lines */
+  int32_t tile_rows, tile_cols, elems, elem_bits;
+  int32_t threads;         /* per workgroup */
+  int32_t lds_bytes;       /* per workgroup (0 on the direct route) */
+  int64_t tiles;
+  int64_t grid;            /* workgroups */
+} tg_frag_plan;
+
+/*
+ * tile_frag_load — fill a register image from a matrix (the ldstmatrix direction: memory ->
+ * registers), then write the registers to `image`.  Bit-exact.
+ *
+ *   src     device, shape[0] x shape[1] elements of dtype laid out as src_layout
+ *           (TG_ROW_MAJOR or TG_COL_MAJOR, ld 0 = packed); element aligned.
+ *   image   device, shape[0]*shape[1] elements, 16-byte aligned; must not overlap src.
+ *   shape   whole tiles of the kind: rows % tile_rows == 0, cols % tile_cols == 0 (else
+ *           TG_E_SHAPE); an empty shape is a no-op.
+ *   dtype   of the kind's width: 16-bit kinds TG_F16 / TG_BF16, 8-bit kinds TG_U8 / TG_I8 /
+ *           TG_FP8_E4M3 / TG_FP8_E5M2, accumulator kinds TG_F32 (else TG_E_DTYPE).
+ *   kind    tg_frag_kind; route   tg_frag_route (else TG_E_ARG).
+ * The direct route moves each run with the widest of 128/64/32/16/8-bit transfers that keep
+ * every transfer of every lane contiguous and aligned ([VEC-AUTO] 算法核心 step 2, the register
+ * layout as the driving side): 128-bit along memory lines when lines and base are 16-byte
+ * aligned, one element at a time when the run crosses lines.  TG_FRAG_LDS needs 16-byte
+ * aligned memory lines (base and ld*element size), else TG_E_ALIGN.
+ */
+int tile_frag_load(const void* src, void* image, const int64_t shape[2], int dtype,
+                   const tg_layout* src_layout, int kind, int route, void* stream);
+
+/*
+ * tile_frag_store — write a register image back to a matrix (registers -> memory): each lane
+ * first loads its own registers from `image`, then the fragments are stored through the route.
+ * Arguments as tile_frag_load with the roles of the buffers exchanged; elements of dst outside
+ * the matrix (the gaps of ld) are not written.
+ */
+int tile_frag_store(const void* image, void* dst, const int64_t shape[2], int dtype,
+                    const tg_layout* dst_layout, int kind, int route, void* stream);
+
+/*
+ * tile_frag_plan — host-only: the plan tile_frag_load (store == 0) or tile_frag_store
+ * (store == 1) would run, with the same status.  mem and image are used for their alignment
+ * only.  Needs no GPU.
+ */
+int tile_frag_plan(int store, const void* mem, const void* image, const int64_t shape[2],
+                   int dtype, const tg_layout* layout, int kind, int route, tg_frag_plan* out);
+
+/* Matrix-instruction shapes of tile_frag_mma: the A, B and accumulator kinds they use. */
+typedef enum tg_mma_shape {
+  TG_MMA_32x32x16 = 1,     /* v_mfma_f32_32x32x16_{f16,bf16}: A16_32x32x16, B16_32x32x16, C32_32x32 */
+  TG_MMA_16x16x32 = 2,     /* v_mfma_f32_16x16x32_{f16,bf16}: A16_16x16x32, B16_16x16x32, C32_16x16 */
+  TG_MMA_32x32x64_F8 = 3   /* v_mfma_f32_32x32x64_f8f6f4 (fp8): A8_32x32x64, B8_32x32x64, C32_32x32 */
+} tg_mma_shape;
+
+/*
+ * tile_frag_mma — the register-level gemm over register images ([SYNC-GEMM] 一 and 四 step 3):
+ * D = A·B (+ C) where each output tile runs one matrix instruction per K atom, accumulating
+ * in place.
+ *
+ *   a_image  device, A [M, K] as a register image of the shape's A kind (16-byte aligned).
+ *   b_image  device, B [K, N] as an image of the B kind.
+ *   c_image  device fp32, C [M, N] as an image of the accumulator kind; read only when
+ *            beta == 1 (may be NULL when beta == 0); may be exactly d_image.
+ *   d_image  device fp32, D [M, N] as an image of the accumulator kind; written; must not
+ *            overlap a_image or b_image.
+ *   M, N, K  whole atoms of the shape (32x32x16: M%32, N%32, K%16; 16x16x32: M%16, N%16,
+ *            K%32; 32x32x64: M%32, N%32, K%64), else TG_E_SHAPE; M == 0 or N == 0 is a no-op,
+ *            K == 0 gives D = beta·C.
+ *   beta     exactly 0.0 or 1.0 (alpha is 1), else TG_E_BETA.
+ *   a_dtype, b_dtype  TG_F16 or TG_BF16 (equal) for the 16-bit shapes; TG_FP8_E4M3 or
+ *            TG_FP8_E5M2 (each) for the fp8 shape; else TG_E_DTYPE.
+ *   shape    tg_mma_shape, else TG_E_ARG.
+ * Products are exact and summed in fp32 by the matrix unit.
+ */
+int tile_frag_mma(const void* a_image, const void* b_image, const float* c_image, float* d_image,
+                  int64_t M, int64_t N, int64_t K, float beta, int a_dtype, int b_dtype,
+                  int shape, void* stream);
+
 /* Reason for the last failure on the calling thread ("" after a success). */
 const char* tile_last_error(void);
 
-/* Library ABI version (this header: 3; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
- * tile_gemm_mx and tile_gemm_mx_plan). */
+/* Library ABI version (this header: 4; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
+ * tile_gemm_mx and tile_gemm_mx_plan, 4 the register fragment calls tile_frag_*). */
 int tile_abi_version(void);
 
 #ifdef __cplusplus

@@ -24,6 +24,10 @@ TG_OK, TG_E_NULL, TG_E_SHAPE, TG_E_DTYPE, TG_E_BETA, TG_E_ALIAS = 0, -1, -2, -3,
 TG_E_ALIGN, TG_E_THREADS, TG_E_LAYOUT, TG_E_HIP, TG_E_ARG = -6, -7, -8, -9, -10
 TG_ROW_MAJOR, TG_COL_MAJOR, TG_XOR_SWIZZLE = 0, 1, 2
 TG_GEMM_NONE, TG_GEMM_ATOM, TG_GEMM_TILED, TG_GEMM_FILL = 0, 1, 2, 3
+(TG_FRAG_A16_32x32x16, TG_FRAG_B16_32x32x16, TG_FRAG_A16_16x16x32, TG_FRAG_B16_16x16x32,
+ TG_FRAG_A8_32x32x64, TG_FRAG_B8_32x32x64, TG_FRAG_C32_32x32, TG_FRAG_C32_16x16) = range(1, 9)
+TG_FRAG_AUTO, TG_FRAG_DIRECT, TG_FRAG_LDS = 0, 1, 2
+TG_MMA_32x32x16, TG_MMA_16x16x32, TG_MMA_32x32x64_F8 = 1, 2, 3
 
 STATUS_NAMES = {0: "TG_OK", -1: "TG_E_NULL", -2: "TG_E_SHAPE", -3: "TG_E_DTYPE", -4: "TG_E_BETA",
                 -5: "TG_E_ALIAS", -6: "TG_E_ALIGN", -7: "TG_E_THREADS", -8: "TG_E_LAYOUT",
@@ -67,6 +71,14 @@ class GemmPlan(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class FragPlan(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_int32), ("vec", ctypes.c_int32), ("vec_bits", ctypes.c_int32),
+                ("transposed", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("tile_cols", ctypes.c_int32), ("elems", ctypes.c_int32),
+                ("elem_bits", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("tiles", ctypes.c_int64), ("grid", ctypes.c_int64)]
+
+
 class TileError(RuntimeError):
     """A non-TG_OK status; .status holds the code, str() the library's reason."""
 
@@ -100,6 +112,13 @@ _SIGS = {
                               ctypes.POINTER(CopyPlan)]),
     "tile_copy_partition": (_INT, [_I64, _I64, _INT, _INT, ctypes.POINTER(Layout), _I64,
                                    ctypes.POINTER(Layout), _I64, ctypes.POINTER(CopyPhase)]),
+    "tile_frag_load": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout), _INT,
+                              _INT, _VP]),
+    "tile_frag_store": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout), _INT,
+                               _INT, _VP]),
+    "tile_frag_plan": (_INT, [_INT, _VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
+                              _INT, _INT, ctypes.POINTER(FragPlan)]),
+    "tile_frag_mma": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _INT, _INT, _INT, _VP]),
     "tile_last_error": (ctypes.c_char_p, []),
     "tile_abi_version": (_INT, []),
 }
@@ -266,3 +285,35 @@ def tile_copy_partition(rows, cols, elem_bits, threads, drive, drive_base, other
     _check(lib().tile_copy_partition(rows, cols, elem_bits, threads, ctypes.byref(d), drive_base,
                                      ctypes.byref(o), other_base, ctypes.byref(out)))
     return out
+
+
+# ------------------------------------------------------------- fragments ----
+
+def tile_frag_load(src, image, shape, dtype, src_layout, kind, route=TG_FRAG_AUTO, stream=None):
+    """Matrix -> register image of fragment `kind` (see include/tilegemm.h)."""
+    lay = _layout(src_layout)
+    _check(lib().tile_frag_load(_addr(src), _addr(image), _shape(shape), int(dtype),
+                                ctypes.byref(lay), int(kind), int(route), _stream(stream)))
+
+
+def tile_frag_store(image, dst, shape, dtype, dst_layout, kind, route=TG_FRAG_AUTO, stream=None):
+    """Register image of fragment `kind` -> matrix."""
+    lay = _layout(dst_layout)
+    _check(lib().tile_frag_store(_addr(image), _addr(dst), _shape(shape), int(dtype),
+                                 ctypes.byref(lay), int(kind), int(route), _stream(stream)))
+
+
+def tile_frag_plan(store, mem, image, shape, dtype, layout, kind, route=TG_FRAG_AUTO):
+    lay = _layout(layout)
+    out = FragPlan()
+    _check(lib().tile_frag_plan(int(store), _addr(mem), _addr(image), _shape(shape), int(dtype),
+                                ctypes.byref(lay), int(kind), int(route), ctypes.byref(out)))
+    return out
+
+
+def tile_frag_mma(a_image, b_image, c_image, d_image, M, N, K, beta, a_dtype, b_dtype, shape,
+                  stream=None):
+    """D = A·B (+ C) over register images of the shape's kinds."""
+    _check(lib().tile_frag_mma(_addr(a_image), _addr(b_image), _addr(c_image), _addr(d_image), M,
+                               N, K, float(beta), int(a_dtype), int(b_dtype), int(shape),
+                               _stream(stream)))

@@ -103,4 +103,39 @@ hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int tra
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
                               hipStream_t s);
 
+// ------------------------------------------------------------ fragments ---
+// Register fragment copies (tile_frag_load / tile_frag_store).  Memory is seen as lines: Q
+// lines of LN elements (row-major: Q = rows, LN = cols; column-major: Q = cols, LN = rows).
+struct FragArgs {
+  uint8_t* mem;         // src of a load, dst of a store
+  uint8_t* img;         // register image: dst of a load, src of a store
+  int64_t ld;           // elements between memory lines
+  int64_t lines, line_len;   // Q and LN
+  int64_t tiles_r, tiles_c;  // fragment tiles along the matrix rows / columns
+  int64_t ntiles;
+};
+
+constexpr int kFragThreads = 256;          // four waves per workgroup
+constexpr int kFragLdsLines = 64;          // LDS route: a block of 64 lines x 256 bytes
+constexpr int kFragLdsLineBytes = 256;
+
+// Tiles one wave moves per direct-route launch iteration (4 KiB of registers per wave).
+int frag_tiles_per_wave(int kind);
+
+// route: TG_FRAG_DIRECT or TG_FRAG_LDS; vec_bytes: direct-route transfer width.
+hipError_t launch_frag(const FragArgs& a, int kind, bool store, bool transposed, int route,
+                       int vec_bytes, int64_t grid, hipStream_t s);
+
+struct FragMmaArgs {
+  const uint8_t* a;     // images
+  const uint8_t* b;
+  const float* c;
+  float* d;
+  int32_t tiles_m, tiles_n, tiles_k;
+  int32_t use_c;
+};
+
+hipError_t launch_frag_mma(const FragMmaArgs& a, int shape, int a_dtype, int b_dtype, int64_t grid,
+                           hipStream_t s);
+
 }  // namespace tg
