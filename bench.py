@@ -9,7 +9,10 @@ events on the stream it is launched on (torch's current stream, which the bindin
 passes to the library); `value` is the GEMM's TFLOP/s over the timed steps, the copy's
 GB/s is reported beside it.  The fp16 transA beta=1 variant of the same GEMM is timed
 after the steps and reported as an extra field, and so is the fp8 (e4m3 x e4m3, A [M,K], B [N,K])
-GEMM of the same size against the dense fp8 peak.
+GEMM of the same size against the dense fp8 peak, the block-scaled fp8 GEMM, and two register
+fragment copies: the 16384 x 16384 fp16 matrix stored column-major loaded into 32x32x16 A
+fragments (runs across memory lines: transposing LDS reads), and 8192 x 16384 fp32 32x32
+accumulator fragments stored to a row-major matrix, both against the HBM peak.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -39,6 +42,7 @@ KERNEL_SOURCES = {
     "fp8": ("gemm_fp8.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "mx": ("gemm_mx_kk.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
+    "frag": ("frag_kernels.hip", "tg_internal.h"),
 }
 
 
@@ -74,7 +78,11 @@ TRAFFIC_KERNELS = {
                                  2 * M * K + M * N * 4),
     "gemm_mx_256x256_e4m3_tn": ("gemm_direct<false, false, 32, 2, 4, false, 0>", "mx",
                                 2 * M * K + 2 * M * (K // 32) + M * N * 4),
-    "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4>", "copy", 2 * ROWS * COLS * 2),
+    "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4, 4>", "copy", 2 * ROWS * COLS * 2),
+    "frag_load_a16_32x32x16_col_16384x16384": ("frag_lds<1, false, true>", "frag",
+                                               2 * ROWS * COLS * 2),
+    "frag_store_c32_32x32_row_8192x16384": ("frag_lds<7, true, true>", "frag",
+                                            2 * (ROWS // 2) * COLS * 4),
 }
 
 
@@ -305,6 +313,73 @@ def main():
                                    False, True, "e4m3", "e4m3", rows, cols, sa_bits=sa, sb_bits=sb)
     del A8, B8, SA, SB
 
+    # register fragment copies (tile_frag_load / tile_frag_store, LDS route)
+    print("bench: fragment copies", file=sys.stderr, flush=True)
+    from oracle import fragment as ofr
+    from oracle.layout import Layout as OLayout
+    img = torch.empty_like(S)
+    col = (tg.TG_COL_MAJOR, 0)
+    frag = {}
+
+    def time_call(call, nbytes):
+        for _ in range(args.warmup):
+            call()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for ev in evs:
+            ev[0].record()
+            call()
+            ev[1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in evs]))
+        gb = nbytes / (ms * 1e-3) / 1e9
+        return ms, gb
+
+    fl_ms, fl_gbs = time_call(lambda: tg.tile_frag_load(S, img, (ROWS, COLS), tg.TG_F16, col,
+                                                        tg.TG_FRAG_A16_32x32x16), 2.0 * ROWS * COLS * 2)
+    gi = synth.rng(79)
+    fl_ok = True
+    imgv = img.view(-1, 64, 8)
+    for _ in range(64):
+        ti, tj = int(gi.integers(ROWS // 32)), int(gi.integers(COLS // 16))
+        want = ofr.frag_load(copy_src_bits, 32, 16, OLayout("col", ld=ROWS, base=tj * 16 * ROWS + ti * 32),
+                             "a16_32x32x16")[0]
+        fl_ok &= bool(np.array_equal(imgv[ti * (COLS // 16) + tj].cpu().numpy().view(np.uint16), want))
+    frag["frag_load_a16_32x32x16_col"] = {
+        "value": round(fl_gbs, 2), "unit": "GB/s", "avg_ms": round(fl_ms, 5),
+        "workload": "tile_frag_load: 16384x16384 fp16 U[-1,1] stored column-major -> 32x32x16 A "
+                    "fragments (runs across memory lines, LDS route with ds_read_b64_tr_b16)",
+        "roofline": {"bound": "hbm", "achieved": round(fl_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(fl_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("frag_load_a16_32x32x16_col_16384x16384")},
+        "parity": {"sampled_tiles_bit_exact": fl_ok, "tiles_checked": 64},
+    }
+    cr, cc = ROWS // 2, COLS
+    acc_bits = synth.uniform(43, cr * cc).view(np.uint32)
+    acc = torch.from_numpy(acc_bits.view(np.int32)).to(dev)
+    mat = torch.empty_like(acc)
+    fs_ms, fs_gbs = time_call(lambda: tg.tile_frag_store(acc, mat, (cr, cc), tg.TG_F32,
+                                                         (tg.TG_ROW_MAJOR, 0), tg.TG_FRAG_C32_32x32),
+                              2.0 * cr * cc * 4)
+    r_, c_ = ofr.coords("c32_32x32")
+    host = mat.view(cr, cc)
+    accv = acc_bits.reshape(-1, 64, 16)
+    fs_ok = True
+    for _ in range(64):
+        ti, tj = int(gi.integers(cr // 32)), int(gi.integers(cc // 32))
+        got = host[ti * 32:(ti + 1) * 32, tj * 32:(tj + 1) * 32].cpu().numpy().view(np.uint32)
+        fs_ok &= bool(np.array_equal(got[r_, c_], accv[ti * (cc // 32) + tj]))
+    frag["frag_store_c32_32x32_row"] = {
+        "value": round(fs_gbs, 2), "unit": "GB/s", "avg_ms": round(fs_ms, 5),
+        "workload": "tile_frag_store: 8192x16384 fp32 32x32 accumulator fragments -> row-major "
+                    "matrix (runs across memory lines, LDS route)",
+        "roofline": {"bound": "hbm", "achieved": round(fs_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(fs_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("frag_store_c32_32x32_row_8192x16384")},
+        "parity": {"sampled_tiles_bit_exact": fs_ok, "tiles_checked": 64},
+    }
+    del img, acc, mat
+
     base = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -362,6 +437,7 @@ def main():
                          "traffic": traffic_for("gemm_mx_256x256_e4m3_tn")},
             "parity": {"sampled_ok": bool(mx_ok), "worst_err_over_tol": round(mx_worst, 5)},
         },
+        **frag,
         "parity": {"gemm_sampled_ok": bool(g_ok), "gemm_worst_err_over_tol": round(g_worst, 5),
                    "copy_bit_exact": c_ok},
         "cpu_baseline": base,

@@ -301,7 +301,7 @@ typedef enum tg_frag_kind {
 } tg_frag_kind;
 
 typedef enum tg_frag_route {
-  TG_FRAG_AUTO = 0,    /* DIRECT when its transfers are 128-bit, else LDS when LDS is usable */
+  TG_FRAG_AUTO = 0,    /* LDS when the memory lines are 16-byte aligned, else DIRECT */
   TG_FRAG_DIRECT = 1,  /* global <-> registers; the width rule on the registers' runs */
   TG_FRAG_LDS = 2      /* global <-> LDS with 128-bit transfers, LDS <-> registers with
                           ds_read_b128 / ds_write_b128 along memory lines, and

@@ -54,13 +54,11 @@ def test_direct_width_matches_the_oracle_rule(kind):
 
 
 @pytest.mark.parametrize("kind,lk,route", [
-    ("a16_32x32x16", "row", tg.TG_FRAG_DIRECT),   # 128-bit along lines: direct
-    ("a16_32x32x16", "col", tg.TG_FRAG_LDS),      # runs cross lines: transposing LDS reads
-    ("b16_32x32x16", "row", tg.TG_FRAG_LDS),
-    ("b16_32x32x16", "col", tg.TG_FRAG_DIRECT),
-    ("a8_32x32x64", "col", tg.TG_FRAG_LDS),
-    ("c32_32x32", "row", tg.TG_FRAG_LDS),
-    ("c32_16x16", "col", tg.TG_FRAG_DIRECT),
+    # 16-byte aligned lines: the LDS route, along lines and across them
+    ("a16_32x32x16", "row", tg.TG_FRAG_LDS), ("a16_32x32x16", "col", tg.TG_FRAG_LDS),
+    ("b16_32x32x16", "row", tg.TG_FRAG_LDS), ("b16_32x32x16", "col", tg.TG_FRAG_LDS),
+    ("a8_32x32x64", "col", tg.TG_FRAG_LDS), ("c32_32x32", "row", tg.TG_FRAG_LDS),
+    ("c32_16x16", "col", tg.TG_FRAG_LDS),
 ])
 def test_auto_route(kind, lk, route):
     tr, tc, _, _ = fr.KINDS[kind]

