@@ -9,7 +9,7 @@ rows x cols and a map (lane, register element) -> (row, col) of the tile; a matr
 tiles is copied tile by tile (row-major tile order), and a tile's register image is
 [64 lanes][E elements], each lane's elements contiguous as they sit in its VGPRs.
 
-Readings (also in the design notes):
+Readings:
 * Kinds and maps (wave64, e is the register element index):
     a16_32x32x16  32 x 16   16-bit  e < 8   (l % 32, 8 (l / 32) + e)
     b16_32x32x16  16 x 32   16-bit  e < 8   (8 (l / 32) + e, l % 32)

@@ -11,7 +11,7 @@ Definitions followed, all from [SYNC-GEMM]:
   C and D are always (M, N).
 * 三 (demo): with beta = 0 the value of C does not matter.
 
-Readings where the page is silent (each also listed in the design notes):
+Readings where the page is silent:
 
 * Zero extents satisfy the divisibility rules; an empty product is zero, so
   K = 0 gives D = beta·C and M = 0 or N = 0 gives an empty D.
@@ -129,7 +129,7 @@ def _dots_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype, b_dtyp
 # ---- fp8 operands: the asynchronous GEMM's precision family -----------------------------
 # [SYNC-GEMM] 七: besides f16/bf16, the asynchronous GEMM takes fp8 operands (and fp4, and
 # block-scaled variants).  The product is the same D = A·B (+C) with fp32 C and D; the page
-# gives no shape table for these precisions.  Readings (also in the design notes):
+# gives no shape table for these precisions.  Readings:
 #
 # * A and B may each be e4m3 or e5m2, independently (mixed pairs included);
 # * M and N multiples of 16, K a multiple of 128: one 128-byte operand row of K per step of

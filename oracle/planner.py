@@ -19,7 +19,7 @@ Restates [VEC-AUTO]:
 * 对齐约束的兜底: misaligned strides or a region starting at an odd column narrow
   the width, down to one element.
 
-Readings (the page is silent; each also listed in the design notes):
+Readings (the page is silent):
 
 * widths narrower than the element, or not a multiple of it, are skipped;
 * the width must also divide elements/threads, so that elements = outer·threads·vec;
