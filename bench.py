@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "mx": ("gemm_mx_kk.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
     "frag": ("frag_kernels.hip", "tg_internal.h"),
+    "async": ("async_copy.hip", "lds_layout.h", "tg_internal.h"),
 }
 
 
@@ -83,6 +84,8 @@ TRAFFIC_KERNELS = {
                                                2 * ROWS * COLS * 2),
     "frag_store_c32_32x32_row_8192x16384": ("frag_lds<7, true, true>", "frag",
                                             2 * (ROWS // 2) * COLS * 4),
+    "tile_copy_async_16384x16384_f16_depth4": ("tile_copy_async_kernel<16, 4, 4>", "async",
+                                               2 * ROWS * COLS * 2),
 }
 
 
@@ -379,6 +382,22 @@ def main():
         "parity": {"sampled_tiles_bit_exact": fs_ok, "tiles_checked": 64},
     }
     del img, acc, mat
+
+    # asynchronous tile copy: issue-only global -> LDS transfers, 4 tiles in flight per workgroup
+    print("bench: async copy", file=sys.stderr, flush=True)
+    aopts = dict(tile_rows=128, tile_cols=64, threads=256, lds_kind=tg.TG_XOR_SWIZZLE, depth=4)
+    T.zero_()
+    ac_ms, ac_gbs = time_call(lambda: tg.tile_copy_async(S, T, (ROWS, COLS), tg.TG_F16, None, None,
+                                                         aopts), 2.0 * ROWS * COLS * 2)
+    frag["copy_async_depth4"] = {
+        "value": round(ac_gbs, 2), "unit": "GB/s", "avg_ms": round(ac_ms, 5),
+        "workload": "tile_copy_async: 16384x16384 fp16, 128x64 tiles, 256 threads, XOR LDS, 4 tiles "
+                    "in flight per workgroup (buffer_load ... lds issue, vmcnt wait for the oldest)",
+        "roofline": {"bound": "hbm", "achieved": round(ac_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ac_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("tile_copy_async_16384x16384_f16_depth4")},
+        "parity": {"bit_exact": bool(torch.equal(S, T))},
+    }
 
     base = None
     if not args.no_cpu_baseline:

@@ -276,6 +276,61 @@ int tile_copy_partition(int64_t rows, int64_t cols, int elem_bits, int threads,
                         tg_copy_phase* out);
 
 /* ---------------------------------------------------------------------------------------
+ * Asynchronous tile copy ([TCGEN05-CP] 一个算子、六个变体 and 与其他异步变体的协作关系: every
+ * copy_async variant, the per-thread vectorised global -> shared one among them, only issues the
+ * transfer, and the code that issued it owns the completion, waiting when it needs the data).  On gfx950 the issue is
+ * global_load_lds_dwordx4 / global_load_lds_dword: each lane's chunk goes from HBM straight to
+ * LDS without passing through registers, and completion is the issuing wave's own
+ * s_waitcnt vmcnt followed by a workgroup barrier.
+ * ------------------------------------------------------------------------------------- */
+typedef struct tg_async_opts {
+  int32_t tile_rows, tile_cols;  /* one LDS stage holds one tile (at most 16 KiB) */
+  int32_t threads;               /* 64 .. 1024, a multiple of 64 (a wave issues together) */
+  int32_t lds_kind;              /* TG_ROW_MAJOR or TG_XOR_SWIZZLE */
+  int32_t depth;                 /* LDS stages, i.e. tiles in flight per workgroup: 1 .. 4 */
+  int32_t tiles_per_workgroup;   /* consecutive tiles a workgroup streams: 1 .. 64, or 0 for the
+                                    default (up to 4, keeping 2048 workgroups or more) */
+  int32_t flags;                 /* must be 0 */
+} tg_async_opts;
+
+typedef struct tg_async_plan {
+  tg_copy_plan copy;             /* load = the issue-only DMA partition, store = LDS -> dst;
+                                    lds_bytes = depth stages */
+  int32_t depth;
+  int32_t tiles_per_workgroup;   /* consecutive tiles one workgroup streams through its stages */
+  int64_t grid;                  /* workgroups */
+} tg_async_plan;
+
+/*
+ * tile_copy_async — bit-exact copy of a shape[0] x shape[1] matrix like tile_copy_ex, with the
+ * global -> LDS half issued asynchronously: each workgroup keeps `depth` tiles in flight, and
+ * before it reads a tile from LDS it waits only until that tile's own transfers have landed
+ * (the newer ones stay in flight), then synchronises the workgroup.
+ *
+ *   src, dst, shape, dtype   as tile_copy.
+ *   src_layout   TG_ROW_MAJOR (any ld).  dst_layout   TG_ROW_MAJOR (any ld), or TG_XOR_SWIZZLE for
+ *                a one-tile tensor (the LDS image of the tile).  Other layouts: TG_E_LAYOUT.
+ *   opts         required (see tg_async_opts).
+ * The partition is that of tile_copy: round f of thread t moves chunk f·threads + t of the
+ * tile, in the tile's row-major order.  With an XOR-swizzled LDS tile, a lane's LDS slot is
+ * fixed by the transfer (lane i of a wave writes 16 or 4 bytes at the wave's base + i·size), so
+ * the lane fetches the chunk whose swizzled position is that slot: the chunks of each tile row
+ * are assigned to threads in swizzled order.  Transfers are 128 or 32 bits (the widths the
+ * hardware's global -> LDS loads have): the width is the widest of those that the width rule
+ * accepts on both sides; a copy whose rows admit neither is rejected (TG_E_ALIGN).  Rounds per
+ * thread must be 1, 2, 4 or 8 (TG_E_THREADS otherwise), a tile at most 16 KiB (TG_E_SHAPE).
+ */
+int tile_copy_async(const void* src, void* dst, const int64_t shape[2], int dtype,
+                    const tg_layout* src_layout, const tg_layout* dst_layout,
+                    const tg_async_opts* opts, void* stream);
+
+/* tile_copy_async_plan — host-only: the plan tile_copy_async would run, with the same status.
+ * Needs no GPU. */
+int tile_copy_async_plan(const void* src, const void* dst, const int64_t shape[2], int dtype,
+                         const tg_layout* src_layout, const tg_layout* dst_layout,
+                         const tg_async_opts* opts, tg_async_plan* out);
+
+/* ---------------------------------------------------------------------------------------
  * Register fragments ([SYNC-GEMM] 一 and 四: the register-level gemm takes its A / B fragments
  * and its C / D accumulator in registers, which the caller fills first — typically by a copy
  * of the ldstmatrix kind; [VEC-AUTO] closing reading list: vec_auto's register path, whose
@@ -392,8 +447,9 @@ int tile_frag_mma(const void* a_image, const void* b_image, const float* c_image
 /* Reason for the last failure on the calling thread ("" after a success). */
 const char* tile_last_error(void);
 
-/* Library ABI version (this header: 4; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
- * tile_gemm_mx and tile_gemm_mx_plan, 4 the register fragment calls tile_frag_*). */
+/* Library ABI version (this header: 5; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
+ * tile_gemm_mx and tile_gemm_mx_plan, 4 the register fragment calls tile_frag_*, 5
+ * tile_copy_async and tile_copy_async_plan). */
 int tile_abi_version(void);
 
 #ifdef __cplusplus

@@ -179,3 +179,54 @@ def plan_tiles(rows, cols, tile_rows, tile_cols, elem_bits, threads, tensor_side
             if best is None or p.vec < best.vec:
                 best = p
     return best
+
+
+# ---- the asynchronous copy ([TCGEN05-CP] 一个算子、六个变体, 与其他异步变体的协作关系) ----------
+#
+# Readings (the pages describe the variant family, not these limits):
+# * the issue-only global -> LDS transfer has the widths of the hardware's direct loads to LDS:
+#   128 and 32 bits are used (there is no 64-bit one); both directions move the same width, the
+#   widest of those two that the copy's own widest-first width (step 2) allows in each direction;
+# * a wave issues together, so the thread count is a multiple of 64;
+# * one LDS stage holds one tile of at most 16 KiB, and 1 .. 4 stages are in flight;
+# * the source is row-major; the destination row-major or the one-tile LDS image;
+# * a thread runs 1, 2, 4 or 8 rounds per tile.
+ASYNC_WIDTHS_BITS = (128, 32)
+ASYNC_STAGE_BYTES = 16384
+
+
+def plan_async(rows, cols, tile_rows, tile_cols, elem_bits, threads, src_side, dst_side, lds_side,
+               depth):
+    """(load plan, store plan) of the asynchronous tile copy, or a Reject.
+
+    Reject categories: "arg" (depth), "layout", "threads", "shape", "align", and those of
+    plan_tiles."""
+    if depth not in (1, 2, 3, 4):
+        return Reject("arg", "depth must be 1 .. 4")
+    if src_side.kind != ROW:
+        return Reject("layout", "the source must be row-major")
+    if dst_side.kind not in (ROW, XOR):
+        return Reject("layout", "the destination must be row-major or the LDS image")
+    tile_bits = tile_rows * tile_cols * elem_bits
+    if tile_rows > 0 and tile_cols > 0 and tile_bits > 8 * ASYNC_STAGE_BYTES:
+        return Reject("shape", "a stage holds at most 16 KiB")
+    load = plan_tiles(rows, cols, tile_rows, tile_cols, elem_bits, threads, src_side, lds_side)
+    if isinstance(load, Reject):
+        return load
+    store = plan_tiles(rows, cols, tile_rows, tile_cols, elem_bits, threads, dst_side, lds_side)
+    if isinstance(store, Reject):
+        return store
+    if rows == 0 or cols == 0:
+        return load, store
+    if threads % 64:
+        return Reject("threads", "whole waves only")
+    allowed = min(load.vec_bits, store.vec_bits)
+    widths = [w for w in ASYNC_WIDTHS_BITS if w <= allowed]
+    if not widths:
+        return Reject("align", "neither 128- nor 32-bit transfers fit the rows")
+    w = widths[0]
+    rounds = tile_bits // (threads * w)
+    if rounds not in (1, 2, 4, 8):
+        return Reject("threads", "1, 2, 4 or 8 rounds per thread")
+    p = Plan(rounds, threads, w // elem_bits, w)
+    return p, p

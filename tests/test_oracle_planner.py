@@ -122,3 +122,31 @@ def test_tiled_plan_is_min_over_tiles():
     assert p.vec == 2
     assert isinstance(plan_tiles(8, 60, 4, 16, 16, 64, Layout(ROW), Layout(ROW)), Reject)
     assert plan_tiles(0, 64, 4, 16, 16, 64, Layout(ROW), Layout(ROW)).outer == 0
+
+
+# ---- the asynchronous copy's plan (oracle.planner.plan_async), hand-derived ---------------------
+
+def test_plan_async_hand_derived():
+    from oracle.planner import Plan, Reject, plan_async
+    from oracle.layout import Layout
+    lds = Layout("xor", 0, 0)
+    # 128x64 fp16 tiles, 256 threads: 16 KiB per tile = 256 threads x 16 B x 4 rounds
+    p = plan_async(16384, 16384, 128, 64, 16, 256, Layout("row"), Layout("row"), lds, 2)
+    assert p == (Plan(4, 256, 8, 128), Plan(4, 256, 8, 128))
+    # 132-byte source rows (ld 66 fp16): the copy's width is 32 bits -> 32-bit transfers, 8 rounds
+    # for a 16 x 64 tile on 64 threads (2 KiB = 64 x 4 B x 8)
+    rl = Layout("row", 0, 0)
+    p = plan_async(32, 64, 16, 64, 16, 64, Layout("row", 66), Layout("row"), rl, 1)
+    assert p == (Plan(8, 64, 2, 32), Plan(8, 64, 2, 32))
+    # 136-byte rows allow 64-bit copies, but there is no 64-bit direct load: 32-bit
+    p = plan_async(32, 64, 16, 64, 16, 64, Layout("row", 68), Layout("row"), rl, 1)
+    assert p[0].vec_bits == 32
+    # 130-byte rows: 16-bit only -> rejected
+    assert plan_async(32, 64, 16, 64, 16, 64, Layout("row", 65), Layout("row"), rl, 1).category == "align"
+    # a 32 KiB stage, 96 threads, depth 5, a column-major source: rejected
+    assert plan_async(256, 64, 256, 64, 16, 256, Layout("row"), Layout("row"), rl, 2).category == "shape"
+    assert plan_async(128, 64, 128, 64, 16, 96, Layout("row"), Layout("row"), rl, 2).category == "threads"
+    assert plan_async(128, 64, 128, 64, 16, 256, Layout("row"), Layout("row"), rl, 5).category == "arg"
+    assert plan_async(128, 64, 128, 64, 16, 256, Layout("col"), Layout("row"), rl, 2).category == "layout"
+    # 16 rounds per thread (16 KiB on 64 threads at 128 bits) is outside 1, 2, 4, 8
+    assert plan_async(128, 64, 128, 64, 16, 64, Layout("row"), Layout("row"), lds, 2).category == "threads"

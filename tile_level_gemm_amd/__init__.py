@@ -63,6 +63,17 @@ class CopyPlan(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("tiles", ctypes.c_int64)]
 
 
+class AsyncOpts(ctypes.Structure):
+    _fields_ = [("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("lds_kind", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("tiles_per_workgroup", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class AsyncPlan(ctypes.Structure):
+    _fields_ = [("copy", CopyPlan), ("depth", ctypes.c_int32),
+                ("tiles_per_workgroup", ctypes.c_int32), ("grid", ctypes.c_int64)]
+
+
 class GemmPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("block_k", ctypes.c_int32), ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
@@ -119,6 +130,11 @@ _SIGS = {
     "tile_frag_plan": (_INT, [_INT, _VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
                               _INT, _INT, ctypes.POINTER(FragPlan)]),
     "tile_frag_mma": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _INT, _INT, _INT, _VP]),
+    "tile_copy_async": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
+                               ctypes.POINTER(Layout), ctypes.POINTER(AsyncOpts), _VP]),
+    "tile_copy_async_plan": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
+                                    ctypes.POINTER(Layout), ctypes.POINTER(AsyncOpts),
+                                    ctypes.POINTER(AsyncPlan)]),
     "tile_last_error": (ctypes.c_char_p, []),
     "tile_abi_version": (_INT, []),
 }
@@ -276,6 +292,31 @@ def tile_copy_plan(src, dst, shape, dtype, src_layout=None, dst_layout=None, opt
     _check(lib().tile_copy_plan(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
                                 ctypes.byref(dl), ctypes.byref(o) if o is not None else None,
                                 ctypes.byref(out)))
+    return out
+
+
+def _async_opts(opts):
+    if opts is None or isinstance(opts, AsyncOpts):
+        return opts
+    return AsyncOpts(int(opts["tile_rows"]), int(opts["tile_cols"]), int(opts["threads"]),
+                     int(opts.get("lds_kind", TG_XOR_SWIZZLE)), int(opts.get("depth", 2)),
+                     int(opts.get("tiles_per_workgroup", 0)), int(opts.get("flags", 0)))
+
+
+def tile_copy_async(src, dst, shape, dtype, src_layout, dst_layout, opts, stream=None):
+    """Copy with issue-only global -> LDS transfers, `depth` tiles in flight per workgroup."""
+    sl, dl, o = _layout(src_layout), _layout(dst_layout), _async_opts(opts)
+    _check(lib().tile_copy_async(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
+                                 ctypes.byref(dl), ctypes.byref(o) if o is not None else None,
+                                 _stream(stream)))
+
+
+def tile_copy_async_plan(src, dst, shape, dtype, src_layout, dst_layout, opts):
+    sl, dl, o = _layout(src_layout), _layout(dst_layout), _async_opts(opts)
+    out = AsyncPlan()
+    _check(lib().tile_copy_async_plan(_addr(src), _addr(dst), _shape(shape), int(dtype),
+                                      ctypes.byref(sl), ctypes.byref(dl),
+                                      ctypes.byref(o) if o is not None else None, ctypes.byref(out)))
     return out
 
 

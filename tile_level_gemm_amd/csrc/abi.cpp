@@ -298,13 +298,77 @@ int plan_copy(const void* src, const void* dst, const int64_t shape[2], int dtyp
   return TG_OK;
 }
 
+// tile_copy_async: the copy's checks and partition (plan_copy), then the asynchronous
+// variant's own limits.  Both sides move the same width: the widest of 128 / 32 bits (the
+// global -> LDS load widths) that the width rule accepts for both directions.
+int plan_async(const void* src, const void* dst, const int64_t shape[2], int dtype,
+               const tg_layout* sl, const tg_layout* dl, const tg_async_opts* ao,
+               tg_async_plan* plan, CopyArgs* args) {
+  if (!ao) return fail(TG_E_ARG, "opts is NULL (tile_copy_async takes explicit options)");
+  if (ao->flags) return fail(TG_E_ARG, "opts->flags must be 0");
+  if (ao->depth < 1 || ao->depth > 4) return fail(TG_E_ARG, "depth must be 1 .. 4");
+  if (ao->tiles_per_workgroup < 0 || ao->tiles_per_workgroup > 64)
+    return fail(TG_E_ARG, "tiles_per_workgroup must be 0 (default) or 1 .. 64");
+  if (!sl || !dl) return fail(TG_E_NULL, "src_layout or dst_layout is NULL");
+  if (sl->kind != TG_ROW_MAJOR)
+    return fail(TG_E_LAYOUT, "tile_copy_async reads a row-major source (each chunk lands whole in LDS)");
+  if (dl->kind != TG_ROW_MAJOR && dl->kind != TG_XOR_SWIZZLE)
+    return fail(TG_E_LAYOUT, "tile_copy_async writes a row-major destination (or the one-tile LDS image)");
+  tg_copy_opts o{ao->tile_rows, ao->tile_cols, ao->threads, ao->lds_kind, 0};
+  {
+    const int eb0 = elem_bytes(dtype);
+    if (eb0 && o.tile_rows > 0 && o.tile_cols > 0 &&
+        (int64_t)o.tile_rows * o.tile_cols * eb0 > kAsyncStageBytes)
+      return fail(TG_E_SHAPE, "an asynchronous stage holds at most 16 KiB");
+  }
+  std::memset(plan, 0, sizeof *plan);
+  int st = plan_copy(src, dst, shape, dtype, sl, dl, &o, &plan->copy, args);
+  if (st) return st;
+  plan->depth = ao->depth;
+  if (plan->copy.tiles == 0) return TG_OK;
+  if (o.threads % 64) return fail(TG_E_THREADS, "tile_copy_async needs whole waves (threads % 64 == 0)");
+  const int eb = args->eb;
+  const int64_t tile_bytes = (int64_t)o.tile_rows * o.tile_cols * eb;
+  // per-thread offsets inside a tile are 32-bit
+  if ((int64_t)(o.tile_rows - 1) * args->src_ld * eb + (int64_t)o.tile_cols * eb >= ((int64_t)1 << 32) ||
+      (int64_t)(o.tile_rows - 1) * args->dst_ld * eb + (int64_t)o.tile_cols * eb >= ((int64_t)1 << 32))
+    return fail(TG_E_SHAPE, "a tile of tile_copy_async must span under 4 GiB of either side");
+  const int wl = plan->copy.load.vec * eb, ws = plan->copy.store.vec * eb;
+  const int w = std::min(wl, ws) >= 16 ? 16 : std::min(wl, ws) >= 4 ? 4 : 0;
+  if (!w)
+    return fail(TG_E_ALIGN, "tile_copy_async moves 128- or 32-bit chunks; the rows admit neither");
+  const int64_t rounds = tile_bytes / ((int64_t)o.threads * w);
+  if (rounds != 1 && rounds != 2 && rounds != 4 && rounds != 8)
+    return fail(TG_E_THREADS, fmt("tile_copy_async runs 1, 2, 4 or 8 rounds per thread (got %lld); "
+                                  "change threads or the tile", rounds));
+  for (tg_copy_phase* ph : {&plan->copy.load, &plan->copy.store}) {
+    ph->vec = w / eb;
+    ph->vec_bits = 8 * w;
+    ph->outer = (int32_t)rounds;
+  }
+  args->load.vec = args->store.vec = w / eb;
+  args->load.outer = args->store.outer = (int32_t)rounds;
+  plan->copy.lds_bytes = (int32_t)(ao->depth * kAsyncStageBytes);
+  // Consecutive tiles per workgroup (row-major tile order keeps them side by side along a tile
+  // row).  Default: up to 4 while at least 2048 workgroups remain (on 16384^2 fp16 in 128x64
+  // tiles, 4 ran 5-15 % faster than 8 or 16 at every depth, and 16 % faster than 1 at depth 4).
+  int32_t tpw = ao->tiles_per_workgroup;
+  if (!tpw) {
+    tpw = 1;
+    while (tpw < 4 && plan->copy.tiles / (2 * tpw) >= 2048) tpw *= 2;
+  }
+  plan->tiles_per_workgroup = tpw;
+  plan->grid = (plan->copy.tiles + tpw - 1) / tpw;
+  return TG_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* tile_last_error(void) { return g_last_error.c_str(); }
 
-int tile_abi_version(void) { return 4; }
+int tile_abi_version(void) { return 5; }
 
 int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D, int64_t M,
                    int64_t N, int64_t K, int transA, int transB, float beta, int dtype,
@@ -445,6 +509,30 @@ int tile_copy(const void* src, void* dst, const int64_t shape[2], int dtype,
   if (plan.tiles == 0) return TG_OK;
   return launch_tile_copy(args, plan.load.vec * args.eb, plan.store.vec * args.eb, plan.lds_bytes,
                           stream);
+}
+
+int tile_copy_async_plan(const void* src, const void* dst, const int64_t shape[2], int dtype,
+                         const tg_layout* src_layout, const tg_layout* dst_layout,
+                         const tg_async_opts* opts, tg_async_plan* out) {
+  clear_error();
+  if (!out) return fail(TG_E_ARG, "out is NULL");
+  CopyArgs args;
+  return plan_async(src, dst, shape, dtype, src_layout, dst_layout, opts, out, &args);
+}
+
+int tile_copy_async(const void* src, void* dst, const int64_t shape[2], int dtype,
+                    const tg_layout* src_layout, const tg_layout* dst_layout,
+                    const tg_async_opts* opts, void* stream) {
+  clear_error();
+  tg_async_plan plan;
+  CopyArgs args;
+  int st = plan_async(src, dst, shape, dtype, src_layout, dst_layout, opts, &plan, &args);
+  if (st || plan.copy.tiles == 0) return st;
+  const hipError_t e = launch_tile_copy_async(args, plan.copy.load.vec * args.eb, plan.copy.load.outer,
+                                              plan.depth, plan.tiles_per_workgroup, plan.grid,
+                                              (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TG_E_HIP, std::string("tile_copy_async launch: ") + hipGetErrorString(e));
+  return TG_OK;
 }
 
 int tile_copy_partition(int64_t rows, int64_t cols, int elem_bits, int threads,

@@ -65,6 +65,12 @@ struct CopyArgs {
 int launch_tile_copy(const CopyArgs& a, int vec_bytes_load, int vec_bytes_store, int lds_bytes,
                      void* stream);
 
+// Asynchronous tile copy: vec_bytes 16 or 4 on both sides, rounds 1/2/4/8 per thread (the same
+// for both sides), depth 1..4 stages, tiles_per_wg consecutive tiles per workgroup.
+constexpr int kAsyncStageBytes = 16384;
+hipError_t launch_tile_copy_async(const CopyArgs& a, int vec_bytes, int rounds, int depth,
+                                  int32_t tiles_per_wg, int64_t grid, hipStream_t s);
+
 struct GemmArgs {
   const uint16_t* A;   // operand base addresses (fp8 kernels read them as bytes)
   const uint16_t* B;
