@@ -342,7 +342,8 @@ int tile_copy_async_plan(const void* src, const void* dst, const int64_t shape[2
  * A register image holds what the wavefront's registers hold: for each tile, in row-major
  * tile order over the matrix, 64 lanes x elems elements, each lane's elements contiguous in
  * register order (tile t, lane l, element e at (t*64 + l)*elems + e).  Every lane's
- * registers are groups of 16 bytes that run along one axis of the tile (a "run").
+ * registers are groups of 16 bytes (8 bytes for the K = 8 / 16 atoms) that run along one axis
+ * of the tile (a "run").
  * ------------------------------------------------------------------------------------- */
 typedef enum tg_frag_kind {
   TG_FRAG_A16_32x32x16 = 1,  /* 32 x 16, 16-bit, 8 per lane: (l%32, 8(l/32) + e)        */
@@ -352,7 +353,11 @@ typedef enum tg_frag_kind {
   TG_FRAG_A8_32x32x64 = 5,   /* 32 x 64, 8-bit, 32 per lane: (l%32, 32(e/16) + 16(l/32) + e%16) */
   TG_FRAG_B8_32x32x64 = 6,   /* 64 x 32, 8-bit, 32 per lane: (32(e/16) + 16(l/32) + e%16, l%32) */
   TG_FRAG_C32_32x32 = 7,     /* 32 x 32 fp32 accumulator, 16 per lane: (8(e/4) + 4(l/32) + e%4, l%32) */
-  TG_FRAG_C32_16x16 = 8      /* 16 x 16 fp32 accumulator, 4 per lane: (4(l/16) + e, l%16) */
+  TG_FRAG_C32_16x16 = 8,     /* 16 x 16 fp32 accumulator, 4 per lane: (4(l/16) + e, l%16) */
+  TG_FRAG_A16_32x32x8 = 9,   /* 32 x 8, 16-bit, 4 per lane: (l%32, 4(l/32) + e)          */
+  TG_FRAG_B16_32x32x8 = 10,  /* 8 x 32, 16-bit, 4 per lane: (4(l/32) + e, l%32)          */
+  TG_FRAG_A16_16x16x16 = 11, /* 16 x 16, 16-bit, 4 per lane: (l%16, 4(l/16) + e)         */
+  TG_FRAG_B16_16x16x16 = 12  /* 16 x 16, 16-bit, 4 per lane: (4(l/16) + e, l%16)         */
 } tg_frag_kind;
 
 typedef enum tg_frag_route {
@@ -417,8 +422,21 @@ int tile_frag_plan(int store, const void* mem, const void* image, const int64_t 
 typedef enum tg_mma_shape {
   TG_MMA_32x32x16 = 1,     /* v_mfma_f32_32x32x16_{f16,bf16}: A16_32x32x16, B16_32x32x16, C32_32x32 */
   TG_MMA_16x16x32 = 2,     /* v_mfma_f32_16x16x32_{f16,bf16}: A16_16x16x32, B16_16x16x32, C32_16x16 */
-  TG_MMA_32x32x64_F8 = 3   /* v_mfma_f32_32x32x64_f8f6f4 (fp8): A8_32x32x64, B8_32x32x64, C32_32x32 */
+  TG_MMA_32x32x64_F8 = 3,  /* v_mfma_f32_32x32x64_f8f6f4 (fp8): A8_32x32x64, B8_32x32x64, C32_32x32 */
+  TG_MMA_32x32x8 = 4,      /* v_mfma_f32_32x32x8_{f16,bf16}: A16_32x32x8, B16_32x32x8, C32_32x32 */
+  TG_MMA_16x16x16 = 5      /* v_mfma_f32_16x16x16_{f16,bf16}: A16_16x16x16, B16_16x16x16, C32_16x16 */
 } tg_mma_shape;
+
+/*
+ * tile_mma_select — host-only: the widest matrix-instruction shape whose atom divides
+ * (M, N, K) exactly, for the operand formats ([TCGEN05-CP] 形状选择: candidates from the widest
+ * down, the first that fits wins; [SYNC-GEMM] 二: the k16 atom when K allows, else k8).  Width is
+ * the multiply-adds of one instruction; 16-bit candidates in order 32x32x16, 16x16x32, 32x32x8,
+ * 16x16x16; fp8: 32x32x64.  *shape receives the choice.  Returns TG_E_SHAPE when no atom
+ * divides the problem (the caller then pads), TG_E_DTYPE for formats no shape takes, TG_E_ARG
+ * for a NULL shape or negative extents.  Needs no GPU.
+ */
+int tile_mma_select(int64_t M, int64_t N, int64_t K, int a_dtype, int b_dtype, int* shape);
 
 /*
  * tile_frag_mma — the register-level gemm over register images ([SYNC-GEMM] 一 and 四 step 3):
@@ -432,7 +450,8 @@ typedef enum tg_mma_shape {
  *   d_image  device fp32, D [M, N] as an image of the accumulator kind; written; must not
  *            overlap a_image or b_image.
  *   M, N, K  whole atoms of the shape (32x32x16: M%32, N%32, K%16; 16x16x32: M%16, N%16,
- *            K%32; 32x32x64: M%32, N%32, K%64), else TG_E_SHAPE; M == 0 or N == 0 is a no-op,
+ *            K%32; 32x32x64: M%32, N%32, K%64; 32x32x8: M%32, N%32, K%8; 16x16x16: M%16, N%16,
+ *            K%16), else TG_E_SHAPE; M == 0 or N == 0 is a no-op,
  *            K == 0 gives D = beta·C.
  *   beta     exactly 0.0 or 1.0 (alpha is 1), else TG_E_BETA.
  *   a_dtype, b_dtype  TG_F16 or TG_BF16 (equal) for the 16-bit shapes; TG_FP8_E4M3 or
@@ -447,9 +466,9 @@ int tile_frag_mma(const void* a_image, const void* b_image, const float* c_image
 /* Reason for the last failure on the calling thread ("" after a success). */
 const char* tile_last_error(void);
 
-/* Library ABI version (this header: 5; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
+/* Library ABI version (this header: 6; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
  * tile_gemm_mx and tile_gemm_mx_plan, 4 the register fragment calls tile_frag_*, 5
- * tile_copy_async and tile_copy_async_plan). */
+ * tile_copy_async and tile_copy_async_plan, 6 the K = 8 / 16 atoms and tile_mma_select). */
 int tile_abi_version(void);
 
 #ifdef __cplusplus

@@ -17,6 +17,10 @@ Readings:
     b16_16x16x32  32 x 16   16-bit  e < 8   (8 (l / 16) + e, l % 16)
     a8_32x32x64   32 x 64   8-bit   e < 32  (l % 32, 32 (e / 16) + 16 (l / 32) + e % 16)
     b8_32x32x64   64 x 32   8-bit   e < 32  (32 (e / 16) + 16 (l / 32) + e % 16, l % 32)
+    a16_32x32x8   32 x 8    16-bit  e < 4   (l % 32, 4 (l / 32) + e)
+    b16_32x32x8   8 x 32    16-bit  e < 4   (4 (l / 32) + e, l % 32)
+    a16_16x16x16  16 x 16   16-bit  e < 4   (l % 16, 4 (l / 16) + e)
+    b16_16x16x16  16 x 16   16-bit  e < 4   (4 (l / 16) + e, l % 16)
     c32_32x32     32 x 32   32-bit  e < 16  (8 (e / 4) + 4 (l / 32) + e % 4, l % 32)
     c32_16x16     16 x 16   32-bit  e < 4   (4 (l / 16) + e, l % 16)
   (the A / B maps pair A row m with B column n over the same K per register element, as the
@@ -25,6 +29,8 @@ Readings:
   power of two dividing E) such that every aligned run of v consecutive register elements of
   every lane of every tile is contiguous in memory and starts on a v-element boundary of the
   absolute address — the page's width rule with the register layout as the driving side.
+* Atom selection: the widest shape (most multiply-adds per instruction) whose atom divides
+  (M, N, K), tried in a fixed candidate order (select_mma).
 
 * The register-level product ([SYNC-GEMM] 一 and 四: A / B fragments and the C / D
   accumulator live in registers, the caller loads the fragments first, and each output tile
@@ -53,6 +59,10 @@ KINDS = {
     "b16_16x16x32": (32, 16, 16, 8),
     "a8_32x32x64": (32, 64, 8, 32),
     "b8_32x32x64": (64, 32, 8, 32),
+    "a16_32x32x8": (32, 8, 16, 4),
+    "b16_32x32x8": (8, 32, 16, 4),
+    "a16_16x16x16": (16, 16, 16, 4),
+    "b16_16x16x16": (16, 16, 16, 4),
     "c32_32x32": (32, 32, 32, 16),
     "c32_16x16": (16, 16, 32, 4),
 }
@@ -77,6 +87,14 @@ def coords(kind):
         r, c = l % 32 + 0 * e, 32 * (e // 16) + 16 * (l // 32) + e % 16
     elif kind == "b8_32x32x64":
         r, c = 32 * (e // 16) + 16 * (l // 32) + e % 16, l % 32 + 0 * e
+    elif kind == "a16_32x32x8":
+        r, c = l % 32 + 0 * e, 4 * (l // 32) + e
+    elif kind == "b16_32x32x8":
+        r, c = 4 * (l // 32) + e, l % 32 + 0 * e
+    elif kind == "a16_16x16x16":
+        r, c = l % 16 + 0 * e, 4 * (l // 16) + e
+    elif kind == "b16_16x16x16":
+        r, c = 4 * (l // 16) + e, l % 16 + 0 * e
     elif kind == "c32_32x32":
         r, c = 8 * (e // 4) + 4 * (l // 32) + e % 4, l % 32 + 0 * e
     elif kind == "c32_16x16":
@@ -151,7 +169,25 @@ SHAPES = {
     "32x32x16": ("a16_32x32x16", "b16_32x32x16", "c32_32x32", (32, 32, 16)),
     "16x16x32": ("a16_16x16x32", "b16_16x16x32", "c32_16x16", (16, 16, 32)),
     "32x32x64_f8": ("a8_32x32x64", "b8_32x32x64", "c32_32x32", (32, 32, 64)),
+    "32x32x8": ("a16_32x32x8", "b16_32x32x8", "c32_32x32", (32, 32, 8)),
+    "16x16x16": ("a16_16x16x16", "b16_16x16x16", "c32_16x16", (16, 16, 16)),
 }
+
+# Widest first ([TCGEN05-CP] 形状选择: candidates are tried from the widest atom down and the
+# first that fits wins; [SYNC-GEMM] 二: the k16 atom when K allows it, else k8).  "Widest" is
+# the multiply-adds one instruction performs; at equal width the longer K comes first (fewer
+# accumulator passes over the same output).  The 8-bit formats have the one shape.
+CANDIDATES_16 = ("32x32x16", "16x16x32", "32x32x8", "16x16x16")
+CANDIDATES_8 = ("32x32x64_f8",)
+
+
+def select_mma(M, N, K, a_fmt, b_fmt):
+    """The widest shape whose atom divides (M, N, K) exactly, or None."""
+    fp8 = a_fmt in ("e4m3", "e5m2")
+    for shape in (CANDIDATES_8 if fp8 else CANDIDATES_16):
+        if accepts_mma(M, N, K, shape, a_fmt, b_fmt, 0.0)[0]:
+            return shape
+    return None
 
 
 def unpack(image, rows, cols, kind, dtype):

@@ -11,7 +11,9 @@ from oracle.layout import Layout
 KIND_CODE = {"a16_32x32x16": tg.TG_FRAG_A16_32x32x16, "b16_32x32x16": tg.TG_FRAG_B16_32x32x16,
              "a16_16x16x32": tg.TG_FRAG_A16_16x16x32, "b16_16x16x32": tg.TG_FRAG_B16_16x16x32,
              "a8_32x32x64": tg.TG_FRAG_A8_32x32x64, "b8_32x32x64": tg.TG_FRAG_B8_32x32x64,
-             "c32_32x32": tg.TG_FRAG_C32_32x32, "c32_16x16": tg.TG_FRAG_C32_16x16}
+             "c32_32x32": tg.TG_FRAG_C32_32x32, "c32_16x16": tg.TG_FRAG_C32_16x16,
+             "a16_32x32x8": tg.TG_FRAG_A16_32x32x8, "b16_32x32x8": tg.TG_FRAG_B16_32x32x8,
+             "a16_16x16x16": tg.TG_FRAG_A16_16x16x16, "b16_16x16x16": tg.TG_FRAG_B16_16x16x16}
 DTYPE_OF_BITS = {8: tg.TG_FP8_E4M3, 16: tg.TG_BF16, 32: tg.TG_F32}
 MEM, IMG = 1 << 32, 1 << 36          # far-apart addresses, only used for alignment
 
@@ -83,7 +85,7 @@ def test_auto_falls_back_to_direct_when_lines_are_not_16_byte_aligned():
 def test_direct_grid_covers_every_tile():
     # 4 waves per workgroup, 4 KiB of registers per wave
     for kind, per_wave in (("a16_32x32x16", 4), ("a8_32x32x64", 2), ("c32_32x32", 1),
-                           ("c32_16x16", 4)):
+                           ("c32_16x16", 4), ("a16_32x32x8", 8), ("b16_16x16x16", 8)):
         tr, tc, _, _ = fr.KINDS[kind]
         p = plan(1, kind, 3 * tr, 5 * tc, "row", route=tg.TG_FRAG_DIRECT)
         assert p.grid == -(-15 // (4 * per_wave))
@@ -143,6 +145,9 @@ def test_rejected_copy_calls_launch_nothing():
     ((32, 32, 64, 0.0, tg.TG_F16, tg.TG_F16, tg.TG_MMA_32x32x64_F8), tg.TG_E_DTYPE),
     ((32, 32, 64, 0.0, tg.TG_FP8_E4M3, tg.TG_U8, tg.TG_MMA_32x32x64_F8), tg.TG_E_DTYPE),
     ((32, 32, 16, 0.5, tg.TG_F16, tg.TG_F16, tg.TG_MMA_32x32x16), tg.TG_E_BETA),
+    ((32, 32, 4, 0.0, tg.TG_F16, tg.TG_F16, tg.TG_MMA_32x32x8), tg.TG_E_SHAPE),
+    ((16, 16, 8, 0.0, tg.TG_BF16, tg.TG_BF16, tg.TG_MMA_16x16x16), tg.TG_E_SHAPE),
+    ((32, 32, 8, 0.0, tg.TG_FP8_E4M3, tg.TG_FP8_E4M3, tg.TG_MMA_32x32x8), tg.TG_E_DTYPE),
 ])
 def test_mma_rejections_match_the_oracle(args, code):
     M, N, K, beta, ad, bd, shape = args
@@ -150,13 +155,41 @@ def test_mma_rejections_match_the_oracle(args, code):
                                          shape))
     assert st == code
     names = {tg.TG_MMA_32x32x16: "32x32x16", tg.TG_MMA_16x16x32: "16x16x32",
-             tg.TG_MMA_32x32x64_F8: "32x32x64_f8"}
+             tg.TG_MMA_32x32x64_F8: "32x32x64_f8", tg.TG_MMA_32x32x8: "32x32x8",
+             tg.TG_MMA_16x16x16: "16x16x16"}
     fmts = {tg.TG_F16: "f16", tg.TG_BF16: "bf16", tg.TG_FP8_E4M3: "e4m3", tg.TG_FP8_E5M2: "e5m2"}
     ok, why = fr.accepts_mma(M, N, K, names.get(shape, "?"), fmts.get(ad, "?"), fmts.get(bd, "?"),
                              beta)
     assert not ok
     assert {"shape": tg.TG_E_ARG, "extent": tg.TG_E_SHAPE, "dtype": tg.TG_E_DTYPE,
             "beta": tg.TG_E_BETA}[why] == code
+
+
+SHAPE_NAME = {tg.TG_MMA_32x32x16: "32x32x16", tg.TG_MMA_16x16x32: "16x16x32",
+              tg.TG_MMA_32x32x64_F8: "32x32x64_f8", tg.TG_MMA_32x32x8: "32x32x8",
+              tg.TG_MMA_16x16x16: "16x16x16"}
+FMT = {tg.TG_F16: "f16", tg.TG_BF16: "bf16", tg.TG_FP8_E4M3: "e4m3", tg.TG_FP8_E5M2: "e5m2"}
+
+
+def test_mma_select_matches_the_oracle():
+    for ad, bd in ((tg.TG_F16, tg.TG_F16), (tg.TG_BF16, tg.TG_BF16), (tg.TG_FP8_E4M3, tg.TG_FP8_E5M2)):
+        for M in (0, 8, 16, 32, 48, 64, 96):
+            for N in (0, 8, 16, 32, 48):
+                for K in (0, 8, 16, 24, 32, 48, 64, 128, 192):
+                    want = fr.select_mma(M, N, K, FMT[ad], FMT[bd])
+                    try:
+                        got = SHAPE_NAME[tg.tile_mma_select(M, N, K, ad, bd)]
+                    except tg.TileError as e:
+                        assert e.status == tg.TG_E_SHAPE
+                        got = None
+                    assert got == want, (M, N, K, ad, bd, got, want)
+
+
+def test_mma_select_rejections():
+    assert status(lambda: tg.tile_mma_select(32, 32, 16, tg.TG_F16, tg.TG_BF16)) == tg.TG_E_DTYPE
+    assert status(lambda: tg.tile_mma_select(32, 32, 16, tg.TG_F32, tg.TG_F32)) == tg.TG_E_DTYPE
+    assert status(lambda: tg.tile_mma_select(-32, 32, 16, tg.TG_F16, tg.TG_F16)) == tg.TG_E_ARG
+    assert status(lambda: tg.tile_mma_select(16, 8, 16, tg.TG_F16, tg.TG_F16)) == tg.TG_E_SHAPE
 
 
 def test_mma_pointer_checks():

@@ -32,13 +32,14 @@ def test_every_declared_symbol_is_exported():
     assert {"tile_gemm", "tile_copy", "tile_copy_ex", "tile_copy_plan", "tile_gemm_plan",
             "tile_gemm_fp8", "tile_gemm_fp8_plan", "tile_gemm_mx", "tile_gemm_mx_plan",
             "tile_copy_partition", "tile_frag_load", "tile_frag_store", "tile_frag_plan",
-            "tile_frag_mma", "tile_copy_async", "tile_copy_async_plan", "tile_last_error",
+            "tile_frag_mma", "tile_copy_async", "tile_copy_async_plan", "tile_mma_select",
+            "tile_last_error",
             "tile_abi_version"} <= set(names)
     lib = tg.lib()
     for n in names:
         assert hasattr(lib, n), n
         assert n in tg._SIGS, n   # the binding marshals every declared entry point
-    assert tg.tile_abi_version() == 5
+    assert tg.tile_abi_version() == 6
 
 
 # ------------------------------------------------------------- planner ----

@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 KIND_CODE = {"a16_32x32x16": tg.TG_FRAG_A16_32x32x16, "b16_32x32x16": tg.TG_FRAG_B16_32x32x16,
              "a16_16x16x32": tg.TG_FRAG_A16_16x16x32, "b16_16x16x32": tg.TG_FRAG_B16_16x16x32,
              "a8_32x32x64": tg.TG_FRAG_A8_32x32x64, "b8_32x32x64": tg.TG_FRAG_B8_32x32x64,
-             "c32_32x32": tg.TG_FRAG_C32_32x32, "c32_16x16": tg.TG_FRAG_C32_16x16}
+             "c32_32x32": tg.TG_FRAG_C32_32x32, "c32_16x16": tg.TG_FRAG_C32_16x16,
+             "a16_32x32x8": tg.TG_FRAG_A16_32x32x8, "b16_32x32x8": tg.TG_FRAG_B16_32x32x8,
+             "a16_16x16x16": tg.TG_FRAG_A16_16x16x16, "b16_16x16x16": tg.TG_FRAG_B16_16x16x16}
 DTYPES = {8: (tg.TG_U8, tg.TG_FP8_E4M3), 16: (tg.TG_F16, tg.TG_BF16), 32: (tg.TG_F32,)}
 UINT = {1: np.uint8, 2: np.uint16, 4: np.uint32}
 LK = {"row": tg.TG_ROW_MAJOR, "col": tg.TG_COL_MAJOR}
@@ -94,6 +96,8 @@ NARROW = [
     ("a8_32x32x64", "row", 4, 4, 4), ("b8_32x32x64", "col", 2, 2, 2), ("b8_32x32x64", "col", 1, 3, 1),
     ("c32_32x32", "col", 2, 0, 2), ("c32_16x16", "col", 1, 1, 1),
     ("a16_32x32x16", "col", 5, 1, 1), ("c32_32x32", "row", 1, 3, 1),
+    ("a16_32x32x8", "row", 4, 0, 4), ("a16_32x32x8", "row", 2, 0, 2),
+    ("b16_16x16x16", "col", 4, 4, 4), ("b16_32x32x8", "col", 1, 0, 1),
 ]
 
 
@@ -188,7 +192,8 @@ def test_empty_shapes_are_no_ops():
 # ---- the register-level product --------------------------------------------------------------
 
 SHAPE_CODE = {"32x32x16": tg.TG_MMA_32x32x16, "16x16x32": tg.TG_MMA_16x16x32,
-              "32x32x64_f8": tg.TG_MMA_32x32x64_F8}
+              "32x32x64_f8": tg.TG_MMA_32x32x64_F8, "32x32x8": tg.TG_MMA_32x32x8,
+              "16x16x16": tg.TG_MMA_16x16x16}
 FMT_CODE = {"f16": tg.TG_F16, "bf16": tg.TG_BF16, "e4m3": tg.TG_FP8_E4M3, "e5m2": tg.TG_FP8_E5M2}
 
 
@@ -211,7 +216,9 @@ def check_d(shape, d, ref, bound, a, b, M, N, K, af, bf):
 MMA_CASES = [("32x32x16", "f16", "f16"), ("32x32x16", "bf16", "bf16"),
              ("16x16x32", "f16", "f16"), ("16x16x32", "bf16", "bf16"),
              ("32x32x64_f8", "e4m3", "e4m3"), ("32x32x64_f8", "e4m3", "e5m2"),
-             ("32x32x64_f8", "e5m2", "e4m3"), ("32x32x64_f8", "e5m2", "e5m2")]
+             ("32x32x64_f8", "e5m2", "e4m3"), ("32x32x64_f8", "e5m2", "e5m2"),
+             ("32x32x8", "f16", "f16"), ("32x32x8", "bf16", "bf16"),
+             ("16x16x16", "f16", "f16"), ("16x16x16", "bf16", "bf16")]
 
 
 @pytest.mark.parametrize("shape,af,bf", MMA_CASES)
@@ -272,7 +279,7 @@ def test_frag_mma_in_place_and_k0(shape, af, bf):
 
 
 @pytest.mark.parametrize("shape,af,bf", [MMA_CASES[1], MMA_CASES[2], MMA_CASES[4],
-                                         MMA_CASES[7]])
+                                         MMA_CASES[7], MMA_CASES[8], MMA_CASES[11]])
 @pytest.mark.parametrize("a_lk,b_lk", [("row", "row"), ("col", "col"), ("col", "row")])
 def test_register_pipeline_equals_the_matrix_product(shape, af, bf, a_lk, b_lk):
     """Load A and B into registers from memory in either orientation, multiply, store D: the
@@ -305,6 +312,36 @@ def test_register_pipeline_equals_the_matrix_product(shape, af, bf, a_lk, b_lk):
     bound = np.abs(al) @ np.abs(bl)
     got = d_out.host(np.float32).reshape(M, N)
     ok, worst = check_d(shape, got, ref, bound, a, b, M, N, K, af, bf)
+    assert d_out.guards_intact() and ok, worst
+
+
+@pytest.mark.parametrize("M,N,K,fmt", [(64, 96, 64, "bf16"), (48, 32, 96, "f16"), (32, 64, 40, "f16"),
+                                       (16, 48, 48, "bf16"), (64, 64, 256, "e4m3")])
+def test_selected_atom_runs_the_product(M, N, K, fmt):
+    """The widest atom tile_mma_select names, through the whole register pipeline."""
+    code = {"f16": tg.TG_F16, "bf16": tg.TG_BF16, "e4m3": tg.TG_FP8_E4M3}[fmt]
+    shape_code = tg.tile_mma_select(M, N, K, code, code)
+    shape = {v: k for k, v in SHAPE_CODE.items()}[shape_code]
+    assert shape == fr.select_mma(M, N, K, fmt, fmt)
+    ka, kb, kc, _ = fr.SHAPES[shape]
+    a, b, c = operands(shape, M, N, K, fmt, fmt, 0.0, 600)
+    eb = a.dtype.itemsize
+    a_img = torch.empty(M * K * eb, dtype=torch.uint8, device="cuda")
+    b_img = torch.empty(K * N * eb, dtype=torch.uint8, device="cuda")
+    d_img = torch.empty(M * N, dtype=torch.float32, device="cuda")
+    d_out = Guarded(M * N * 4)
+    say(f"frag selected {shape} {M}x{N}x{K} {fmt}")
+    tg.tile_frag_load(upload_bits(a.reshape(-1)), a_img, (M, K), code, (tg.TG_ROW_MAJOR, 0),
+                      KIND_CODE[ka])
+    tg.tile_frag_load(upload_bits(b.reshape(-1)), b_img, (K, N), code, (tg.TG_ROW_MAJOR, 0),
+                      KIND_CODE[kb])
+    tg.tile_frag_mma(a_img, b_img, None, d_img, M, N, K, 0.0, code, code, shape_code)
+    tg.tile_frag_store(d_img, d_out.ptr, (M, N), tg.TG_F32, (tg.TG_ROW_MAJOR, 0), KIND_CODE[kc])
+    torch.cuda.synchronize()
+    from oracle.gemm import logical_operands
+    al, bl = logical_operands(a, b, M, N, K, 0, 0, fmt, fmt)
+    ok, worst = check_d(shape, d_out.host(np.float32).reshape(M, N), al @ bl, np.abs(al) @ np.abs(bl),
+                        a, b, M, N, K, fmt, fmt)
     assert d_out.guards_intact() and ok, worst
 
 

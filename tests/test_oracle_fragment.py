@@ -46,10 +46,10 @@ def test_map_is_a_bijection_onto_the_tile(kind):
 
 @pytest.mark.parametrize("kind", KINDS)
 def test_each_lane_holds_one_run_per_register_group(kind):
-    # Every lane's registers are groups of 16 bytes that run along one axis of the tile: the
-    # 128-bit span the vector width rule can reach.
+    # Every lane's registers are runs of 16 bytes (8 for the K = 8 / 16 atoms, whose lanes hold
+    # four 16-bit values) along one axis of the tile: the span the vector width rule can reach.
     tr, tc, bits, e = fr.KINDS[kind]
-    run = 128 // bits
+    run = min(128 // bits, e)
     r, c = fr.coords(kind)
     for lane in range(64):
         for g in range(e // run):
@@ -150,6 +150,29 @@ def test_frag_mma_ref_empty_and_k0():
     assert (b == 0).all()
 
 
+def test_select_mma_widest_first():
+    assert fr.select_mma(64, 64, 64, "f16", "f16") == "32x32x16"
+    assert fr.select_mma(16, 16, 64, "bf16", "bf16") == "16x16x32"     # M, N only 16-divisible
+    assert fr.select_mma(32, 64, 24, "f16", "f16") == "32x32x8"         # K % 16 == 8: the k8 atom
+    assert fr.select_mma(48, 16, 16, "f16", "f16") == "16x16x16"
+    assert fr.select_mma(16, 8, 16, "f16", "f16") is None                # N = 8 fits no atom
+    assert fr.select_mma(32, 32, 8, "f16", "bf16") is None               # mixed 16-bit formats
+    assert fr.select_mma(32, 32, 128, "e4m3", "e5m2") == "32x32x64_f8"
+    assert fr.select_mma(32, 32, 32, "e4m3", "e4m3") is None
+
+
+def test_candidates_are_ordered_by_width_and_the_first_fit_wins():
+    macs = [int(np.prod(fr.SHAPES[s][3])) for s in fr.CANDIDATES_16]
+    assert macs == sorted(macs, reverse=True)
+    for M in (16, 32, 48, 64):
+        for N in (16, 32, 48):
+            for K in (8, 16, 24, 32, 48, 64):
+                got = fr.select_mma(M, N, K, "f16", "f16")
+                fits = [s for s in fr.CANDIDATES_16
+                        if all(x % a == 0 for x, a in zip((M, N, K), fr.SHAPES[s][3]))]
+                assert got == (fits[0] if fits else None)
+
+
 @pytest.mark.parametrize("args,why", [
     ((16, 32, 16, "32x32x16", "f16", "f16", 0.0), "extent"),
     ((32, 32, 8, "32x32x16", "f16", "f16", 0.0), "extent"),
@@ -207,7 +230,7 @@ def _brute_vec(kind, rows, cols, layout, base):
             addr[(i, j)] = base + eb * off
     r, c = fr.coords(kind)
     for vb in (16, 8, 4, 2, 1):
-        if vb < eb:
+        if vb < eb or (vb // eb) > e:       # a transfer never spans more than a lane's registers
             continue
         v = vb // eb
         ok = True
@@ -320,6 +343,7 @@ def _pins_fail(monkeypatch, kind, how):
     ("a16_32x32x16", "k_reversed"), ("b16_16x16x32", "k_reversed"), ("b8_32x32x64", "k_reversed"),
     ("a16_16x16x32", "halves_swapped"), ("b16_32x32x16", "halves_swapped"),
     ("c32_32x32", "transposed"), ("c32_16x16", "transposed"),
+    ("a16_32x32x8", "k_reversed"), ("b16_16x16x16", "halves_swapped"),
     ("a8_32x32x64", "block_order"), ("b8_32x32x64", "block_order"),
     ("c32_32x32", "rows_by_lane_half"),
 ])

@@ -25,9 +25,10 @@ TG_E_ALIGN, TG_E_THREADS, TG_E_LAYOUT, TG_E_HIP, TG_E_ARG = -6, -7, -8, -9, -10
 TG_ROW_MAJOR, TG_COL_MAJOR, TG_XOR_SWIZZLE = 0, 1, 2
 TG_GEMM_NONE, TG_GEMM_ATOM, TG_GEMM_TILED, TG_GEMM_FILL = 0, 1, 2, 3
 (TG_FRAG_A16_32x32x16, TG_FRAG_B16_32x32x16, TG_FRAG_A16_16x16x32, TG_FRAG_B16_16x16x32,
- TG_FRAG_A8_32x32x64, TG_FRAG_B8_32x32x64, TG_FRAG_C32_32x32, TG_FRAG_C32_16x16) = range(1, 9)
+ TG_FRAG_A8_32x32x64, TG_FRAG_B8_32x32x64, TG_FRAG_C32_32x32, TG_FRAG_C32_16x16,
+ TG_FRAG_A16_32x32x8, TG_FRAG_B16_32x32x8, TG_FRAG_A16_16x16x16, TG_FRAG_B16_16x16x16) = range(1, 13)
 TG_FRAG_AUTO, TG_FRAG_DIRECT, TG_FRAG_LDS = 0, 1, 2
-TG_MMA_32x32x16, TG_MMA_16x16x32, TG_MMA_32x32x64_F8 = 1, 2, 3
+TG_MMA_32x32x16, TG_MMA_16x16x32, TG_MMA_32x32x64_F8, TG_MMA_32x32x8, TG_MMA_16x16x16 = 1, 2, 3, 4, 5
 
 STATUS_NAMES = {0: "TG_OK", -1: "TG_E_NULL", -2: "TG_E_SHAPE", -3: "TG_E_DTYPE", -4: "TG_E_BETA",
                 -5: "TG_E_ALIAS", -6: "TG_E_ALIGN", -7: "TG_E_THREADS", -8: "TG_E_LAYOUT",
@@ -130,6 +131,7 @@ _SIGS = {
     "tile_frag_plan": (_INT, [_INT, _VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
                               _INT, _INT, ctypes.POINTER(FragPlan)]),
     "tile_frag_mma": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _INT, _INT, _INT, _VP]),
+    "tile_mma_select": (_INT, [_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(ctypes.c_int)]),
     "tile_copy_async": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
                                ctypes.POINTER(Layout), ctypes.POINTER(AsyncOpts), _VP]),
     "tile_copy_async_plan": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
@@ -358,3 +360,10 @@ def tile_frag_mma(a_image, b_image, c_image, d_image, M, N, K, beta, a_dtype, b_
     _check(lib().tile_frag_mma(_addr(a_image), _addr(b_image), _addr(c_image), _addr(d_image), M,
                                N, K, float(beta), int(a_dtype), int(b_dtype), int(shape),
                                _stream(stream)))
+
+
+def tile_mma_select(M, N, K, a_dtype, b_dtype):
+    """The widest matrix-instruction shape whose atom divides (M, N, K) (a TG_MMA_* code)."""
+    out = ctypes.c_int(0)
+    _check(lib().tile_mma_select(M, N, K, int(a_dtype), int(b_dtype), ctypes.byref(out)))
+    return out.value

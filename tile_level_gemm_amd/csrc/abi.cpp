@@ -368,7 +368,7 @@ extern "C" {
 
 const char* tile_last_error(void) { return g_last_error.c_str(); }
 
-int tile_abi_version(void) { return 5; }
+int tile_abi_version(void) { return 6; }
 
 int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D, int64_t M,
                    int64_t N, int64_t K, int transA, int transB, float beta, int dtype,

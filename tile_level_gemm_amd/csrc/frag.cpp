@@ -25,6 +25,7 @@ struct KindInfo {
   int eb;          // element bytes
   int elems;       // register elements per lane
   bool run_rows;   // every run goes along the tile's rows (else along its columns)
+  int run_bytes() const { return elems * eb < 16 ? elems * eb : 16; }
 };
 
 bool kind_info(int kind, KindInfo* k) {
@@ -37,6 +38,10 @@ bool kind_info(int kind, KindInfo* k) {
     case TG_FRAG_B8_32x32x64: *k = {64, 32, 1, 32, true}; return true;
     case TG_FRAG_C32_32x32: *k = {32, 32, 4, 16, true}; return true;
     case TG_FRAG_C32_16x16: *k = {16, 16, 4, 4, true}; return true;
+    case TG_FRAG_A16_32x32x8: *k = {32, 8, 2, 4, false}; return true;
+    case TG_FRAG_B16_32x32x8: *k = {8, 32, 2, 4, true}; return true;
+    case TG_FRAG_A16_16x16x16: *k = {16, 16, 2, 4, false}; return true;
+    case TG_FRAG_B16_16x16x16: *k = {16, 16, 2, 4, true}; return true;
     default: return false;
   }
 }
@@ -114,7 +119,7 @@ int plan_frag(bool store, const void* mem, const void* image, const int64_t shap
   // Direct-route width: the widest transfer every run keeps contiguous and aligned.
   int vb = k.eb;
   if (!plan->transposed)
-    for (int w = 16; w > k.eb; w /= 2)
+    for (int w = k.run_bytes(); w > k.eb; w /= 2)
       if ((uintptr_t)mem % w == 0 && (ld * k.eb) % w == 0) { vb = w; break; }
   const bool lds_ok = (uintptr_t)mem % 16 == 0 && (ld * k.eb) % 16 == 0;
   int r = route;
@@ -172,13 +177,42 @@ bool mma_info(int shape, int* am, int* an, int* ak, int* eb) {
     case TG_MMA_32x32x16: *am = 32; *an = 32; *ak = 16; *eb = 2; return true;
     case TG_MMA_16x16x32: *am = 16; *an = 16; *ak = 32; *eb = 2; return true;
     case TG_MMA_32x32x64_F8: *am = 32; *an = 32; *ak = 64; *eb = 1; return true;
+    case TG_MMA_32x32x8: *am = 32; *an = 32; *ak = 8; *eb = 2; return true;
+    case TG_MMA_16x16x16: *am = 16; *an = 16; *ak = 16; *eb = 2; return true;
     default: return false;
   }
 }
 
+// Candidates from the widest atom down (multiply-adds per instruction; at equal width the
+// longer K first).
+const int kCandidates16[] = {TG_MMA_32x32x16, TG_MMA_16x16x32, TG_MMA_32x32x8, TG_MMA_16x16x16};
+const int kCandidates8[] = {TG_MMA_32x32x64_F8};
+
 }  // namespace
 
 extern "C" {
+
+int tile_mma_select(int64_t M, int64_t N, int64_t K, int a_dtype, int b_dtype, int* shape) {
+  clear_error();
+  if (!shape) return fail(TG_E_ARG, "shape is NULL");
+  if (M < 0 || N < 0 || K < 0) return fail(TG_E_ARG, "negative extent");
+  const bool f16 = (a_dtype == TG_F16 || a_dtype == TG_BF16) && a_dtype == b_dtype;
+  const bool f8 = (a_dtype == TG_FP8_E4M3 || a_dtype == TG_FP8_E5M2) &&
+                  (b_dtype == TG_FP8_E4M3 || b_dtype == TG_FP8_E5M2);
+  if (!f16 && !f8)
+    return fail(TG_E_DTYPE, "no matrix-instruction shape takes these operand formats");
+  const int* cand = f16 ? kCandidates16 : kCandidates8;
+  const int n = f16 ? 4 : 1;
+  for (int i = 0; i < n; ++i) {
+    int am, an, ak, eb;
+    mma_info(cand[i], &am, &an, &ak, &eb);
+    if (M % am == 0 && N % an == 0 && K % ak == 0) {
+      *shape = cand[i];
+      return TG_OK;
+    }
+  }
+  return fail(TG_E_SHAPE, fmt("no atom divides M=%lld, N=%lld, K=%lld", M, N, K));
+}
 
 int tile_frag_plan(int store, const void* mem, const void* image, const int64_t shape[2],
                    int dtype, const tg_layout* layout, int kind, int route, tg_frag_plan* out) {

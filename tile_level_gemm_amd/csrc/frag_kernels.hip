@@ -6,7 +6,8 @@
 // place; the caller fills the fragments first with a copy of the ldstmatrix kind ([VEC-AUTO]
 // closing reading list: the register path and the warp-collective ldstmatrix copy).
 //
-// Every lane's registers are runs of 16 bytes along one axis of its tile (G runs of R elements).
+// Every lane's registers are runs of RB bytes along one axis of its tile (G runs of R elements):
+// 16 bytes, or 8 for the K = 8 / 16 atoms whose lanes hold four 16-bit values.
 // Memory is seen as lines (row-major: rows; column-major: columns); a run either lies along a
 // memory line or crosses lines ("transposed").
 //
@@ -33,6 +34,7 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -43,25 +45,32 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // Fragment kind traits: tile extent TR x TC, element bytes EB, E elements per lane in G runs
-// of R; RUN_ROWS: runs go along the tile's rows.
+// of R (RB bytes each); RUN_ROWS: runs go along the tile's rows.
 template <int KIND>
 struct FK {
   static constexpr bool k8 = KIND == TG_FRAG_A8_32x32x64 || KIND == TG_FRAG_B8_32x32x64;
   static constexpr bool kAcc = KIND == TG_FRAG_C32_32x32 || KIND == TG_FRAG_C32_16x16;
+  static constexpr bool kShortK = KIND == TG_FRAG_A16_32x32x8 || KIND == TG_FRAG_B16_32x32x8 ||
+                                  KIND == TG_FRAG_A16_16x16x16 || KIND == TG_FRAG_B16_16x16x16;
   static constexpr int EB = k8 ? 1 : kAcc ? 4 : 2;
-  static constexpr int E = k8 ? 32 : KIND == TG_FRAG_C32_32x32 ? 16 : KIND == TG_FRAG_C32_16x16 ? 4 : 8;
-  static constexpr int R = 16 / EB;
+  static constexpr int E = k8 ? 32 : KIND == TG_FRAG_C32_32x32 ? 16
+                         : (KIND == TG_FRAG_C32_16x16 || kShortK) ? 4 : 8;
+  static constexpr int RB = E * EB < 16 ? E * EB : 16;
+  static constexpr int R = RB / EB;
   static constexpr int G = E / R;
   static constexpr bool RUN_ROWS = !(KIND == TG_FRAG_A16_32x32x16 || KIND == TG_FRAG_A16_16x16x32 ||
-                                     KIND == TG_FRAG_A8_32x32x64);
+                                     KIND == TG_FRAG_A8_32x32x64 || KIND == TG_FRAG_A16_32x32x8 ||
+                                     KIND == TG_FRAG_A16_16x16x16);
   static constexpr int TR = KIND == TG_FRAG_A16_32x32x16 ? 32 : KIND == TG_FRAG_B16_32x32x16 ? 16
                           : KIND == TG_FRAG_A16_16x16x32 ? 16 : KIND == TG_FRAG_B16_16x16x32 ? 32
                           : KIND == TG_FRAG_A8_32x32x64 ? 32 : KIND == TG_FRAG_B8_32x32x64 ? 64
-                          : KIND == TG_FRAG_C32_32x32 ? 32 : 16;
+                          : KIND == TG_FRAG_C32_32x32 ? 32 : KIND == TG_FRAG_A16_32x32x8 ? 32
+                          : KIND == TG_FRAG_B16_32x32x8 ? 8 : 16;
   static constexpr int TC = KIND == TG_FRAG_A16_32x32x16 ? 16 : KIND == TG_FRAG_B16_32x32x16 ? 32
                           : KIND == TG_FRAG_A16_16x16x32 ? 32 : KIND == TG_FRAG_B16_16x16x32 ? 16
                           : KIND == TG_FRAG_A8_32x32x64 ? 64 : KIND == TG_FRAG_B8_32x32x64 ? 32
-                          : KIND == TG_FRAG_C32_32x32 ? 32 : 16;
+                          : KIND == TG_FRAG_C32_32x32 ? 32 : KIND == TG_FRAG_A16_32x32x8 ? 8
+                          : KIND == TG_FRAG_B16_32x32x8 ? 32 : 16;
   static_assert(TR * TC == 64 * E, "a fragment tile holds 64 lanes x E elements");
 
   // Tile coordinates of the first element of run g of lane l.
@@ -73,6 +82,10 @@ struct FK {
     else if constexpr (KIND == TG_FRAG_A8_32x32x64) { r = l & 31; c = 32 * g + 16 * (l >> 5); }
     else if constexpr (KIND == TG_FRAG_B8_32x32x64) { r = 32 * g + 16 * (l >> 5); c = l & 31; }
     else if constexpr (KIND == TG_FRAG_C32_32x32) { r = 8 * g + 4 * (l >> 5); c = l & 31; }
+    else if constexpr (KIND == TG_FRAG_A16_32x32x8) { r = l & 31; c = 4 * (l >> 5); }
+    else if constexpr (KIND == TG_FRAG_B16_32x32x8) { r = 4 * (l >> 5); c = l & 31; }
+    else if constexpr (KIND == TG_FRAG_A16_16x16x16) { r = l & 15; c = 4 * (l >> 4); }
+    else if constexpr (KIND == TG_FRAG_B16_16x16x16) { r = 4 * (l >> 4); c = l & 15; }
     else { r = 4 * (l >> 4); c = l & 15; }
   }
 };
@@ -97,37 +110,45 @@ template <> struct Word<4> { typedef uint32_t T; };
 template <> struct Word<2> { typedef uint16_t T; };
 template <> struct Word<1> { typedef uint8_t T; };
 
+// Register type of one run.
+template <int RB>
+struct RunT;
+template <> struct RunT<16> { typedef u32x4 T; };
+template <> struct RunT<8> { typedef u32x2 T; };
+
 // One run between memory and registers.  Along a line: 16 / VB transfers of VB bytes; across
 // lines: R transfers of one element, `pitch` bytes apart.
-template <int VB, bool TRANS, int EB>
-__device__ __forceinline__ u32x4 load_run(const uint8_t* p, int64_t pitch) {
+template <int VB, bool TRANS, int EB, int RB>
+__device__ __forceinline__ typename RunT<RB>::T load_run(const uint8_t* p, int64_t pitch) {
   Run r;
   if constexpr (!TRANS) {
     typedef typename Word<VB>::T T;
 #pragma unroll
-    for (int s = 0; s < 16 / VB; ++s) {
+    for (int s = 0; s < RB / VB; ++s) {
       const T x = ((const T*)p)[s];
       __builtin_memcpy(&r.b[s * VB], &x, VB);
     }
   } else {
     typedef typename Word<EB>::T T;
 #pragma unroll
-    for (int e = 0; e < 16 / EB; ++e) {
+    for (int e = 0; e < RB / EB; ++e) {
       const T x = *(const T*)(p + e * pitch);
       __builtin_memcpy(&r.b[e * EB], &x, EB);
     }
   }
-  return r.v;
+  typename RunT<RB>::T out;
+  __builtin_memcpy(&out, r.b, RB);
+  return out;
 }
 
-template <int VB, bool TRANS, int EB>
-__device__ __forceinline__ void store_run(uint8_t* p, int64_t pitch, u32x4 v) {
+template <int VB, bool TRANS, int EB, int RB>
+__device__ __forceinline__ void store_run(uint8_t* p, int64_t pitch, typename RunT<RB>::T v) {
   Run r;
-  r.v = v;
+  __builtin_memcpy(r.b, &v, RB);
   if constexpr (!TRANS) {
     typedef typename Word<VB>::T T;
 #pragma unroll
-    for (int s = 0; s < 16 / VB; ++s) {
+    for (int s = 0; s < RB / VB; ++s) {
       T x;
       __builtin_memcpy(&x, &r.b[s * VB], VB);
       ((T*)p)[s] = x;
@@ -135,7 +156,7 @@ __device__ __forceinline__ void store_run(uint8_t* p, int64_t pitch, u32x4 v) {
   } else {
     typedef typename Word<EB>::T T;
 #pragma unroll
-    for (int e = 0; e < 16 / EB; ++e) {
+    for (int e = 0; e < RB / EB; ++e) {
       T x;
       __builtin_memcpy(&x, &r.b[e * EB], EB);
       *(T*)(p + e * pitch) = x;
@@ -143,19 +164,19 @@ __device__ __forceinline__ void store_run(uint8_t* p, int64_t pitch, u32x4 v) {
   }
 }
 
-// Image side: a lane's registers are LANE_BYTES contiguous bytes, so with 16 bytes per lane one
-// instruction moves 1 KiB of the image contiguously and streams past the caches; with 32 or 64
-// bytes per lane each instruction covers every second or fourth 16-byte chunk, and plain
-// accesses let the L2 merge the chunks of one line before it is written back.
-template <int LANE_BYTES>
-__device__ __forceinline__ void img_store(uint8_t* p, int g, u32x4 v) {
-  if constexpr (LANE_BYTES == 16) __builtin_nontemporal_store(v, (u32x4*)p + g);
-  else ((u32x4*)p)[g] = v;
+// Image side: a lane's registers are LANE_BYTES contiguous bytes, so with 8 or 16 bytes per
+// lane one instruction moves 512 bytes or 1 KiB of the image contiguously and streams past the
+// caches; with 32 or 64 bytes per lane each instruction covers every second or fourth 16-byte
+// chunk, and plain accesses let the L2 merge the chunks of one line before it is written back.
+template <int LANE_BYTES, class V>
+__device__ __forceinline__ void img_store(uint8_t* p, int g, V v) {
+  if constexpr (LANE_BYTES <= 16) __builtin_nontemporal_store(v, (V*)p + g);
+  else ((V*)p)[g] = v;
 }
-template <int LANE_BYTES>
-__device__ __forceinline__ u32x4 img_load(const uint8_t* p, int g) {
-  if constexpr (LANE_BYTES == 16) return __builtin_nontemporal_load((const u32x4*)p + g);
-  else return ((const u32x4*)p)[g];
+template <int LANE_BYTES, class V>
+__device__ __forceinline__ V img_load(const uint8_t* p, int g) {
+  if constexpr (LANE_BYTES <= 16) return __builtin_nontemporal_load((const V*)p + g);
+  else return ((const V*)p)[g];
 }
 
 // ------------------------------------------------------------------------ direct route ---
@@ -168,6 +189,7 @@ __global__ __launch_bounds__(kFragThreads) void frag_direct(FragArgs a) {
   constexpr bool CM = K::RUN_ROWS != TRANS;   // memory is column-major
   constexpr int TPW = tiles_per_wave<KIND>();
   constexpr int LANE_BYTES = K::E * K::EB;
+  typedef typename RunT<K::RB>::T V;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kFragThreads / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -179,7 +201,7 @@ __global__ __launch_bounds__(kFragThreads) void frag_direct(FragArgs a) {
     K::origin(lane, g, r, c);
     off[g] = (CM ? (int64_t)c * a.ld + r : (int64_t)r * a.ld + c) * K::EB;
   }
-  u32x4 regs[TPW][K::G];
+  V regs[TPW][K::G];
   int64_t mem_at[TPW], img_at[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
@@ -196,26 +218,26 @@ __global__ __launch_bounds__(kFragThreads) void frag_direct(FragArgs a) {
       if (wave * TPW + u < a.ntiles)
 #pragma unroll
         for (int g = 0; g < K::G; ++g)
-          regs[u][g] = load_run<VB, TRANS, K::EB>(a.mem + mem_at[u] + off[g], pitch);
+          regs[u][g] = load_run<VB, TRANS, K::EB, K::RB>(a.mem + mem_at[u] + off[g], pitch);
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
       if (wave * TPW + u < a.ntiles)
 #pragma unroll
         for (int g = 0; g < K::G; ++g)
-          img_store<LANE_BYTES>(a.img + img_at[u], g, regs[u][g]);
+          img_store<LANE_BYTES, V>(a.img + img_at[u], g, regs[u][g]);
   } else {
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
       if (wave * TPW + u < a.ntiles)
 #pragma unroll
         for (int g = 0; g < K::G; ++g)
-          regs[u][g] = img_load<LANE_BYTES>(a.img + img_at[u], g);
+          regs[u][g] = img_load<LANE_BYTES, V>(a.img + img_at[u], g);
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
       if (wave * TPW + u < a.ntiles)
 #pragma unroll
         for (int g = 0; g < K::G; ++g)
-          store_run<VB, TRANS, K::EB>(a.mem + mem_at[u] + off[g], pitch, regs[u][g]);
+          store_run<VB, TRANS, K::EB, K::RB>(a.mem + mem_at[u] + off[g], pitch, regs[u][g]);
   }
 }
 
@@ -228,17 +250,20 @@ __device__ __forceinline__ uint32_t lds_at(uint32_t q, uint32_t byte) {
 }
 
 // Run of a lane whose first element sits at LDS line q, element p (block coordinates).
-template <int EB, bool TRANS>
-__device__ __forceinline__ u32x4 lds_read_run(const uint8_t* lds, int q, int p, int lane) {
+template <int EB, bool TRANS, int RB>
+__device__ __forceinline__ typename RunT<RB>::T lds_read_run(const uint8_t* lds, int q, int p,
+                                                             int lane) {
+  typedef typename RunT<RB>::T V;
   Run r;
   if constexpr (!TRANS) {
-    r.v = *(const u32x4*)(lds + lds_at(q, p * EB));
+    const V v = *(const V*)(lds + lds_at(q, p * EB));
+    __builtin_memcpy(r.b, &v, RB);
   } else if constexpr (EB == 2) {
     // Lanes of a 16-lane group hold consecutive p and the same q: lane i reads 4 elements at
     // line q + 4s + i/4, element p - i + 4(i%4), and receives (q + 4s .. +3, p).
     const int i = lane & 15;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < RB / 8; ++s) {
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(lds + lds_at(q + 4 * s + (i >> 2), 2 * (p - i + 4 * (i & 3)))));
       __builtin_memcpy(&r.b[8 * s], &v, 8);
@@ -247,28 +272,31 @@ __device__ __forceinline__ u32x4 lds_read_run(const uint8_t* lds, int q, int p, 
     // lane i reads 8 bytes at line q + 8s + i/2, element p - i + 8(i%2); receives (q + 8s .. +7, p)
     const int i = lane & 15;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < RB / 8; ++s) {
       const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
           (lds_i32x2*)(lds + lds_at(q + 8 * s + (i >> 1), p - i + 8 * (i & 1))));
       __builtin_memcpy(&r.b[8 * s], &v, 8);
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.w[e] = *(const uint32_t*)(lds + lds_at(q + e, 4 * p));
+    for (int e = 0; e < RB / 4; ++e) r.w[e] = *(const uint32_t*)(lds + lds_at(q + e, 4 * p));
   }
-  return r.v;
+  V out;
+  __builtin_memcpy(&out, r.b, RB);
+  return out;
 }
 
-template <int EB, bool TRANS>
-__device__ __forceinline__ void lds_write_run(uint8_t* lds, int q, int p, u32x4 v) {
+template <int EB, bool TRANS, int RB>
+__device__ __forceinline__ void lds_write_run(uint8_t* lds, int q, int p, typename RunT<RB>::T v) {
+  typedef typename RunT<RB>::T V;
   Run r;
-  r.v = v;
+  __builtin_memcpy(r.b, &v, RB);
   if constexpr (!TRANS) {
-    *(u32x4*)(lds + lds_at(q, p * EB)) = v;
+    *(V*)(lds + lds_at(q, p * EB)) = v;
   } else {
     typedef typename Word<EB>::T T;
 #pragma unroll
-    for (int e = 0; e < 16 / EB; ++e) {
+    for (int e = 0; e < RB / EB; ++e) {
       T x;
       __builtin_memcpy(&x, &r.b[e * EB], EB);
       *(T*)(lds + lds_at(q + e, p * EB)) = x;
@@ -288,6 +316,7 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
   constexpr int NTQ = kFragLdsLines / TQ, NTP = LINE / TP;
   constexpr int CHUNKS = kFragLdsLines * kFragLdsLineBytes / 16 / kFragThreads;
   constexpr int LANE_BYTES = K::E * K::EB;
+  typedef typename RunT<K::RB>::T V;
   static_assert(NTQ * TQ == kFragLdsLines && NTP * TP == LINE, "whole tiles per block");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFragLdsLines * kFragLdsLineBytes];
 
@@ -329,32 +358,33 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
       int tq, tp;
       int64_t img;
       if (!tile_of(b, tq, tp, img)) continue;
-      u32x4 regs[K::G];
+      V regs[K::G];
 #pragma unroll
       for (int g = 0; g < K::G; ++g) {
         int r, c;
         K::origin(lane, g, r, c);
-        regs[g] = lds_read_run<K::EB, TRANS>(lds, tq * TQ + (CM ? c : r), tp * TP + (CM ? r : c),
-                                             lane);
+        regs[g] = lds_read_run<K::EB, TRANS, K::RB>(lds, tq * TQ + (CM ? c : r),
+                                                    tp * TP + (CM ? r : c), lane);
       }
 #pragma unroll
       for (int g = 0; g < K::G; ++g)
-        img_store<LANE_BYTES>(a.img + img, g, regs[g]);
+        img_store<LANE_BYTES, V>(a.img + img, g, regs[g]);
     }
   } else {
     for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
       int tq, tp;
       int64_t img;
       if (!tile_of(b, tq, tp, img)) continue;
-      u32x4 regs[K::G];
+      V regs[K::G];
 #pragma unroll
       for (int g = 0; g < K::G; ++g)
-        regs[g] = img_load<LANE_BYTES>(a.img + img, g);
+        regs[g] = img_load<LANE_BYTES, V>(a.img + img, g);
 #pragma unroll
       for (int g = 0; g < K::G; ++g) {
         int r, c;
         K::origin(lane, g, r, c);
-        lds_write_run<K::EB, TRANS>(lds, tq * TQ + (CM ? c : r), tp * TP + (CM ? r : c), regs[g]);
+        lds_write_run<K::EB, TRANS, K::RB>(lds, tq * TQ + (CM ? c : r), tp * TP + (CM ? r : c),
+                                          regs[g]);
       }
     }
     __syncthreads();
@@ -371,7 +401,31 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
 // ------------------------------------------------------------------ register-level gemm ---
 template <int SHAPE, int ADT, int BDT>
 __device__ __forceinline__ void mma_step(const uint8_t* a, const uint8_t* b, float* acc) {
-  if constexpr (SHAPE == TG_MMA_32x32x16 || SHAPE == TG_MMA_16x16x32) {
+  if constexpr (SHAPE == TG_MMA_32x32x8 || SHAPE == TG_MMA_16x16x16) {
+    // four 16-bit values per lane (the bf16 forms take them as shorts)
+    const u32x2 x = *(const u32x2*)a, y = *(const u32x2*)b;
+    if constexpr (SHAPE == TG_MMA_32x32x8) {
+      f32x16 c;
+      __builtin_memcpy(&c, acc, 64);
+      if constexpr (ADT == TG_F16)
+        c = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, x),
+                                                 __builtin_bit_cast(f16x4, y), c, 0, 0, 0);
+      else
+        c = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, x),
+                                                     __builtin_bit_cast(s16x4, y), c, 0, 0, 0);
+      __builtin_memcpy(acc, &c, 64);
+    } else {
+      f32x4 c;
+      __builtin_memcpy(&c, acc, 16);
+      if constexpr (ADT == TG_F16)
+        c = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, x),
+                                                  __builtin_bit_cast(f16x4, y), c, 0, 0, 0);
+      else
+        c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, x),
+                                                      __builtin_bit_cast(s16x4, y), c, 0, 0, 0);
+      __builtin_memcpy(acc, &c, 16);
+    }
+  } else if constexpr (SHAPE == TG_MMA_32x32x16 || SHAPE == TG_MMA_16x16x32) {
     const u32x4 x = *(const u32x4*)a, y = *(const u32x4*)b;
     if constexpr (SHAPE == TG_MMA_32x32x16) {
       f32x16 c;
@@ -413,8 +467,9 @@ __device__ __forceinline__ void mma_step(const uint8_t* a, const uint8_t* b, flo
 template <int SHAPE, int ADT, int BDT>
 __global__ __launch_bounds__(kFragThreads) void frag_mma(FragMmaArgs g) {
   constexpr bool F8 = SHAPE == TG_MMA_32x32x64_F8;
-  constexpr int AB_BYTES = F8 ? 32 : 16;                       // operand bytes per lane
-  constexpr int ACC = SHAPE == TG_MMA_16x16x32 ? 4 : 16;        // accumulator floats per lane
+  constexpr bool SHORT_K = SHAPE == TG_MMA_32x32x8 || SHAPE == TG_MMA_16x16x16;
+  constexpr int AB_BYTES = F8 ? 32 : SHORT_K ? 8 : 16;         // operand bytes per lane
+  constexpr int ACC = (SHAPE == TG_MMA_16x16x32 || SHAPE == TG_MMA_16x16x16) ? 4 : 16;
   const int lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * (kFragThreads / 64) +
                     __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -450,7 +505,7 @@ hipError_t launch_direct(const FragArgs& a, int vb, int64_t grid, hipStream_t s)
     hipLaunchKernelGGL((frag_direct<KIND, STORE, true, EB>), gd, bd, 0, s, a);
   } else {
     switch (vb) {
-      case 16: hipLaunchKernelGGL((frag_direct<KIND, STORE, false, 16>), gd, bd, 0, s, a); break;
+      case 16: hipLaunchKernelGGL((frag_direct<KIND, STORE, false, (FK<KIND>::RB >= 16 ? 16 : FK<KIND>::RB)>), gd, bd, 0, s, a); break;
       case 8: hipLaunchKernelGGL((frag_direct<KIND, STORE, false, (EB <= 8 ? 8 : 16)>), gd, bd, 0, s, a); break;
       case 4: hipLaunchKernelGGL((frag_direct<KIND, STORE, false, (EB <= 4 ? 4 : 16)>), gd, bd, 0, s, a); break;
       case 2: hipLaunchKernelGGL((frag_direct<KIND, STORE, false, (EB <= 2 ? 2 : 16)>), gd, bd, 0, s, a); break;
@@ -488,6 +543,10 @@ int frag_tiles_per_wave(int kind) {
     case TG_FRAG_A8_32x32x64: return tiles_per_wave<TG_FRAG_A8_32x32x64>();
     case TG_FRAG_B8_32x32x64: return tiles_per_wave<TG_FRAG_B8_32x32x64>();
     case TG_FRAG_C32_32x32: return tiles_per_wave<TG_FRAG_C32_32x32>();
+    case TG_FRAG_A16_32x32x8: return tiles_per_wave<TG_FRAG_A16_32x32x8>();
+    case TG_FRAG_B16_32x32x8: return tiles_per_wave<TG_FRAG_B16_32x32x8>();
+    case TG_FRAG_A16_16x16x16: return tiles_per_wave<TG_FRAG_A16_16x16x16>();
+    case TG_FRAG_B16_16x16x16: return tiles_per_wave<TG_FRAG_B16_16x16x16>();
     default: return tiles_per_wave<TG_FRAG_C32_16x16>();
   }
 }
@@ -503,6 +562,10 @@ hipError_t launch_frag(const FragArgs& a, int kind, bool store, bool transposed,
     case TG_FRAG_B8_32x32x64: return launch_kind<TG_FRAG_B8_32x32x64>(a, store, transposed, route, vec_bytes, grid, s);
     case TG_FRAG_C32_32x32: return launch_kind<TG_FRAG_C32_32x32>(a, store, transposed, route, vec_bytes, grid, s);
     case TG_FRAG_C32_16x16: return launch_kind<TG_FRAG_C32_16x16>(a, store, transposed, route, vec_bytes, grid, s);
+    case TG_FRAG_A16_32x32x8: return launch_kind<TG_FRAG_A16_32x32x8>(a, store, transposed, route, vec_bytes, grid, s);
+    case TG_FRAG_B16_32x32x8: return launch_kind<TG_FRAG_B16_32x32x8>(a, store, transposed, route, vec_bytes, grid, s);
+    case TG_FRAG_A16_16x16x16: return launch_kind<TG_FRAG_A16_16x16x16>(a, store, transposed, route, vec_bytes, grid, s);
+    case TG_FRAG_B16_16x16x16: return launch_kind<TG_FRAG_B16_16x16x16>(a, store, transposed, route, vec_bytes, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -519,6 +582,14 @@ hipError_t launch_frag_mma(const FragMmaArgs& g, int shape, int a_dtype, int b_d
     case TG_MMA_16x16x32:
       if (a_dtype == TG_F16) hipLaunchKernelGGL((frag_mma<TG_MMA_16x16x32, TG_F16, TG_F16>), gd, bd, 0, s, g);
       else hipLaunchKernelGGL((frag_mma<TG_MMA_16x16x32, TG_BF16, TG_BF16>), gd, bd, 0, s, g);
+      break;
+    case TG_MMA_32x32x8:
+      if (a_dtype == TG_F16) hipLaunchKernelGGL((frag_mma<TG_MMA_32x32x8, TG_F16, TG_F16>), gd, bd, 0, s, g);
+      else hipLaunchKernelGGL((frag_mma<TG_MMA_32x32x8, TG_BF16, TG_BF16>), gd, bd, 0, s, g);
+      break;
+    case TG_MMA_16x16x16:
+      if (a_dtype == TG_F16) hipLaunchKernelGGL((frag_mma<TG_MMA_16x16x16, TG_F16, TG_F16>), gd, bd, 0, s, g);
+      else hipLaunchKernelGGL((frag_mma<TG_MMA_16x16x16, TG_BF16, TG_BF16>), gd, bd, 0, s, g);
       break;
     case TG_MMA_32x32x64_F8:
       if (!a5 && !b5) hipLaunchKernelGGL((frag_mma<TG_MMA_32x32x64_F8, TG_FP8_E4M3, TG_FP8_E4M3>), gd, bd, 0, s, g);
