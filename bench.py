@@ -399,6 +399,31 @@ def main():
         "parity": {"bit_exact": bool(torch.equal(S, T))},
     }
 
+    # widest-first atom selection: the register-level product at 4096^3 f16 with each atom that
+    # divides it; tile_mma_select names the first of them
+    print("bench: register-level product per atom", file=sys.stderr, flush=True)
+    n4 = 4096
+    sel = tg.tile_mma_select(n4, n4, n4, tg.TG_F16, tg.TG_F16)
+    img_a = torch.empty(n4 * n4, dtype=torch.int16, device=dev).random_(0, 14000)   # finite f16
+    img_b = torch.empty_like(img_a).random_(0, 14000)
+    img_d = torch.empty(n4 * n4, dtype=torch.float32, device=dev)
+    atoms = {}
+    for name, code in (("32x32x16", tg.TG_MMA_32x32x16), ("16x16x32", tg.TG_MMA_16x16x32),
+                       ("32x32x8", tg.TG_MMA_32x32x8), ("16x16x16", tg.TG_MMA_16x16x16)):
+        ms_, _ = time_call(lambda: tg.tile_frag_mma(img_a, img_b, None, img_d, n4, n4, n4, 0.0,
+                                                    tg.TG_F16, tg.TG_F16, code), 1.0)
+        atoms[name] = {"avg_ms": round(ms_, 5),
+                       "TFLOP/s": round(2.0 * n4 ** 3 / (ms_ * 1e-3) / 1e12, 3)}
+    frag["mma_atoms_4096"] = {
+        "workload": "tile_frag_mma 4096x4096x4096 f16 register images (one wave per output tile, "
+                    "operands streamed from the images); each atom that divides the shape",
+        "selected": {v: k for k, v in {"32x32x16": tg.TG_MMA_32x32x16, "16x16x32": tg.TG_MMA_16x16x32,
+                                       "32x32x8": tg.TG_MMA_32x32x8,
+                                       "16x16x16": tg.TG_MMA_16x16x16}.items()}[sel],
+        "atoms": atoms,
+    }
+    del img_a, img_b, img_d
+
     base = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
