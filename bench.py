@@ -79,7 +79,7 @@ TRAFFIC_KERNELS = {
                                  2 * M * K + M * N * 4),
     "gemm_mx_256x256_e4m3_tn": ("gemm_direct<false, false, 32, 2, 4, false, 0>", "mx",
                                 2 * M * K + 2 * M * (K // 32) + M * N * 4),
-    "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4, 4>", "copy", 2 * ROWS * COLS * 2),
+    "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4, 4, 128>", "copy", 2 * ROWS * COLS * 2),
     "frag_load_a16_32x32x16_col_16384x16384": ("frag_lds<1, false, true>", "frag",
                                                2 * ROWS * COLS * 2),
     "frag_store_c32_32x32_row_8192x16384": ("frag_lds<7, true, true>", "frag",
