@@ -64,13 +64,14 @@ def test_direct_width_matches_the_oracle_rule(kind):
 ])
 def test_auto_route(kind, lk, route):
     tr, tc, _, _ = fr.KINDS[kind]
-    p = plan(0, kind, 2 * tr, 4 * tc, lk)
-    assert p.route == route
-    if route == tg.TG_FRAG_LDS:
-        assert (p.vec_bits, p.lds_bytes, p.threads) == (128, 16384, 256)
-        lines, line_len = (2 * tr, 4 * tc) if lk == "row" else (4 * tc, 2 * tr)
-        per_line = 256 // (fr.KINDS[kind][2] // 8)
-        assert p.grid == -(-lines // 64) * -(-line_len // per_line)
+    for store, line_bytes in ((0, 256), (1, 512)):      # block lines: 256 B loads, 512 B stores
+        p = plan(store, kind, 2 * tr, 4 * tc, lk)
+        assert p.route == route
+        if route == tg.TG_FRAG_LDS:
+            assert (p.vec_bits, p.lds_bytes, p.threads) == (128, 64 * line_bytes, 256)
+            lines, line_len = (2 * tr, 4 * tc) if lk == "row" else (4 * tc, 2 * tr)
+            per_line = line_bytes // (fr.KINDS[kind][2] // 8)
+            assert p.grid == -(-lines // 64) * -(-line_len // per_line)
 
 
 def test_auto_falls_back_to_direct_when_lines_are_not_16_byte_aligned():

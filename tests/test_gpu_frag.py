@@ -123,7 +123,7 @@ def test_direct_narrow_widths(kind, lk, pad, base, vec, store):
                                      ("c32_16x16", "col"), ("b16_16x16x32", "col")])
 @pytest.mark.parametrize("store", [False, True])
 def test_lds_route_padded_lines_and_many_blocks(kind, lk, store):
-    # 16-byte aligned padding and base; several 256-byte blocks along each line and a ragged
+    # 16-byte aligned padding and base; several 512-byte blocks along each line and a ragged
     # last block in both directions.
     tr, tc, bits, _ = fr.KINDS[kind]
     eb = bits // 8

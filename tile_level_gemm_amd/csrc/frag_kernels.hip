@@ -14,13 +14,14 @@
 //  * direct route: each lane moves its runs between memory and its VGPRs itself — VB-byte
 //    transfers along a line (VB from the widest-first width rule), one element per transfer
 //    across lines — and writes / reads its registers to / from the register image.
-//  * LDS route: a workgroup stages a block of 64 memory lines x 256 bytes through LDS with
+//  * LDS route: a workgroup stages a block of 64 memory lines x 256 bytes (loads) or 512 bytes
+//    (stores) through LDS with
 //    128-bit global transfers; lanes then read their runs with ds_read_b128 along a line or
 //    with the transposing reads across lines: ds_read_b64_tr_b16 (within each 16-lane group,
 //    lane j receives element j%4 of the 8-byte reads of lanes 4q + j/4, q = 0..3) and
 //    ds_read_b64_tr_b8 (lane j receives byte j%8 of the reads of lanes 2k + j/8, k = 0..7).
 //    Stores write runs with ds_write_b128 along a line and element by element across lines.
-//    LDS lines are 16 chunks of 16 bytes; chunk x of line q sits at x ^ swz(q), swz(q) =
+//    LDS lines are 16 or 32 chunks of 16 bytes; chunk x of line q sits at x ^ swz(q), swz(q) =
 //    2(q & 7) ^ ((q >> 3) & 1): sixteen consecutive lines reading one logical chunk hit sixteen
 //    distinct chunks, and the two-chunk spans of four (tr_b16) or the chunks of eight (tr_b8)
 //    consecutive lines land apart.
@@ -243,20 +244,20 @@ __global__ __launch_bounds__(kFragThreads) void frag_direct(FragArgs a) {
 
 // --------------------------------------------------------------------------- LDS route ---
 __device__ __forceinline__ uint32_t swz(uint32_t q) { return ((q & 7u) << 1) ^ ((q >> 3) & 1u); }
-
-// LDS byte address of byte `byte` of line q.
+// LDS byte address of byte `byte` of line q of a block with LB-byte lines.
+template <int LB>
 __device__ __forceinline__ uint32_t lds_at(uint32_t q, uint32_t byte) {
-  return q * kFragLdsLineBytes + (((byte >> 4) ^ swz(q)) << 4) + (byte & 15u);
+  return q * LB + (((byte >> 4) ^ swz(q)) << 4) + (byte & 15u);
 }
 
 // Run of a lane whose first element sits at LDS line q, element p (block coordinates).
-template <int EB, bool TRANS, int RB>
+template <int EB, bool TRANS, int RB, int LB>
 __device__ __forceinline__ typename RunT<RB>::T lds_read_run(const uint8_t* lds, int q, int p,
                                                              int lane) {
   typedef typename RunT<RB>::T V;
   Run r;
   if constexpr (!TRANS) {
-    const V v = *(const V*)(lds + lds_at(q, p * EB));
+    const V v = *(const V*)(lds + lds_at<LB>(q, p * EB));
     __builtin_memcpy(r.b, &v, RB);
   } else if constexpr (EB == 2) {
     // Lanes of a 16-lane group hold consecutive p and the same q: lane i reads 4 elements at
@@ -265,7 +266,7 @@ __device__ __forceinline__ typename RunT<RB>::T lds_read_run(const uint8_t* lds,
 #pragma unroll
     for (int s = 0; s < RB / 8; ++s) {
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(lds + lds_at(q + 4 * s + (i >> 2), 2 * (p - i + 4 * (i & 3)))));
+          (lds_s16x4*)(lds + lds_at<LB>(q + 4 * s + (i >> 2), 2 * (p - i + 4 * (i & 3)))));
       __builtin_memcpy(&r.b[8 * s], &v, 8);
     }
   } else if constexpr (EB == 1) {
@@ -274,51 +275,55 @@ __device__ __forceinline__ typename RunT<RB>::T lds_read_run(const uint8_t* lds,
 #pragma unroll
     for (int s = 0; s < RB / 8; ++s) {
       const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_i32x2*)(lds + lds_at(q + 8 * s + (i >> 1), p - i + 8 * (i & 1))));
+          (lds_i32x2*)(lds + lds_at<LB>(q + 8 * s + (i >> 1), p - i + 8 * (i & 1))));
       __builtin_memcpy(&r.b[8 * s], &v, 8);
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < RB / 4; ++e) r.w[e] = *(const uint32_t*)(lds + lds_at(q + e, 4 * p));
+    for (int e = 0; e < RB / 4; ++e) r.w[e] = *(const uint32_t*)(lds + lds_at<LB>(q + e, 4 * p));
   }
   V out;
   __builtin_memcpy(&out, r.b, RB);
   return out;
 }
 
-template <int EB, bool TRANS, int RB>
+template <int EB, bool TRANS, int RB, int LB>
 __device__ __forceinline__ void lds_write_run(uint8_t* lds, int q, int p, typename RunT<RB>::T v) {
   typedef typename RunT<RB>::T V;
   Run r;
   __builtin_memcpy(r.b, &v, RB);
   if constexpr (!TRANS) {
-    *(V*)(lds + lds_at(q, p * EB)) = v;
+    *(V*)(lds + lds_at<LB>(q, p * EB)) = v;
   } else {
     typedef typename Word<EB>::T T;
 #pragma unroll
     for (int e = 0; e < RB / EB; ++e) {
       T x;
       __builtin_memcpy(&x, &r.b[e * EB], EB);
-      *(T*)(lds + lds_at(q + e, p * EB)) = x;
+      *(T*)(lds + lds_at<LB>(q + e, p * EB)) = x;
     }
   }
 }
 
-// One workgroup per block of 64 lines x 256 bytes (blocks walk along the lines first); the
-// block's tiles are shared out over the four waves.
+// One workgroup per block of 64 lines x LB bytes (blocks walk along the lines first); the
+// block's tiles are shared out over the four waves.  Stores use 512-byte lines (each workgroup
+// writes runs of 512 bytes of every line: 5.6-6.2 TB/s against 5.5-6.1 with 256), loads
+// 256-byte ones (3.2-3.8 TB/s with 512 against 5.0-6.0).
 template <int KIND, bool STORE, bool TRANS>
 __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
+  constexpr int LB = frag_lds_line_bytes(STORE);
+  constexpr int kLineChunks = LB / 16;   // 16-byte chunks per block line
   using K = FK<KIND>;
   constexpr bool CM = K::RUN_ROWS != TRANS;
   constexpr int TQ = CM ? K::TC : K::TR;            // tile extent across lines
   constexpr int TP = CM ? K::TR : K::TC;            // tile extent along a line (elements)
-  constexpr int LINE = kFragLdsLineBytes / K::EB;   // elements per block line
+  constexpr int LINE = LB / K::EB;   // elements per block line
   constexpr int NTQ = kFragLdsLines / TQ, NTP = LINE / TP;
-  constexpr int CHUNKS = kFragLdsLines * kFragLdsLineBytes / 16 / kFragThreads;
+  constexpr int CHUNKS = kFragLdsLines * LB / 16 / kFragThreads;
   constexpr int LANE_BYTES = K::E * K::EB;
   typedef typename RunT<K::RB>::T V;
   static_assert(NTQ * TQ == kFragLdsLines && NTP * TP == LINE, "whole tiles per block");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kFragLdsLines * kFragLdsLineBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFragLdsLines * LB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -344,14 +349,14 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
     u32x4 v[CHUNKS];
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + kFragThreads * i, q = c >> 4, x = c & 15;
+      const int c = tid + kFragThreads * i, q = c / kLineChunks, x = c % kLineChunks;
       if (q < qn && 16 * x < pn * K::EB)
         v[i] = __builtin_nontemporal_load((const u32x4*)(gblock + q * pitch + 16 * x));
     }
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + kFragThreads * i, q = c >> 4, x = c & 15;
-      if (q < qn && 16 * x < pn * K::EB) *(u32x4*)(lds + lds_at(q, 16 * x)) = v[i];
+      const int c = tid + kFragThreads * i, q = c / kLineChunks, x = c % kLineChunks;
+      if (q < qn && 16 * x < pn * K::EB) *(u32x4*)(lds + lds_at<LB>(q, 16 * x)) = v[i];
     }
     __syncthreads();
     for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
       for (int g = 0; g < K::G; ++g) {
         int r, c;
         K::origin(lane, g, r, c);
-        regs[g] = lds_read_run<K::EB, TRANS, K::RB>(lds, tq * TQ + (CM ? c : r),
+        regs[g] = lds_read_run<K::EB, TRANS, K::RB, LB>(lds, tq * TQ + (CM ? c : r),
                                                     tp * TP + (CM ? r : c), lane);
       }
 #pragma unroll
@@ -383,16 +388,16 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
       for (int g = 0; g < K::G; ++g) {
         int r, c;
         K::origin(lane, g, r, c);
-        lds_write_run<K::EB, TRANS, K::RB>(lds, tq * TQ + (CM ? c : r), tp * TP + (CM ? r : c),
+        lds_write_run<K::EB, TRANS, K::RB, LB>(lds, tq * TQ + (CM ? c : r), tp * TP + (CM ? r : c),
                                           regs[g]);
       }
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + kFragThreads * i, q = c >> 4, x = c & 15;
+      const int c = tid + kFragThreads * i, q = c / kLineChunks, x = c % kLineChunks;
       if (q < qn && 16 * x < pn * K::EB)
-        __builtin_nontemporal_store(*(const u32x4*)(lds + lds_at(q, 16 * x)),
+        __builtin_nontemporal_store(*(const u32x4*)(lds + lds_at<LB>(q, 16 * x)),
                                     (u32x4*)(gblock + q * pitch + 16 * x));
     }
   }

@@ -122,8 +122,9 @@ struct FragArgs {
 };
 
 constexpr int kFragThreads = 256;          // four waves per workgroup
-constexpr int kFragLdsLines = 64;          // LDS route: a block of 64 lines x 256 bytes
-constexpr int kFragLdsLineBytes = 256;
+constexpr int kFragLdsLines = 64;          // LDS route: a block of 64 lines x line bytes
+// bytes per block line: 256 for loads, 512 for stores (measured per direction)
+constexpr int frag_lds_line_bytes(bool store) { return store ? 512 : 256; }
 
 // Tiles one wave moves per direct-route launch iteration (4 KiB of registers per wave).
 int frag_tiles_per_wave(int kind);
