@@ -77,7 +77,8 @@ typedef enum tg_layout_kind {
 typedef struct tg_layout {
   int32_t kind;      /* tg_layout_kind */
   int32_t reserved;  /* must be 0 */
-  int64_t ld;        /* leading dimension in elements; 0 = packed */
+  int64_t ld;        /* leading dimension in elements; 0 = packed; at most 2^40 (else
+                        TG_E_LAYOUT) */
 } tg_layout;
 
 /* How tile_copy_ex stages a tensor: it is cut into tile_rows x tile_cols

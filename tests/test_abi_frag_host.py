@@ -207,3 +207,15 @@ def test_mma_pointer_checks():
                                            f16, f16, s)) == tg.TG_E_ALIGN
     assert status(lambda: tg.tile_frag_mma(None, None, None, None, 0, 32, 16, 0.0, f16, f16,
                                            s)) == tg.TG_OK
+
+
+def test_huge_leading_dimensions_are_rejected():
+    # offsets must stay far inside 64 bits: ld above 2^40 elements is refused on every call
+    big = (1 << 40) + 1
+    assert status(lambda: plan(0, "a16_32x32x16", 64, 32, "row", ld=big)) == tg.TG_E_LAYOUT
+    assert status(lambda: tg.tile_copy_plan(1 << 20, 1 << 30, (64, 64), tg.TG_F16,
+                                            (tg.TG_ROW_MAJOR, big), None)) == tg.TG_E_LAYOUT
+    assert status(lambda: tg.tile_copy_async_plan(1 << 20, 1 << 30, (64, 64), tg.TG_F16, None,
+                                                  (tg.TG_ROW_MAJOR, big),
+                                                  dict(tile_rows=64, tile_cols=64, threads=256,
+                                                       depth=2))) == tg.TG_E_LAYOUT

@@ -31,6 +31,7 @@ using namespace tg;
 namespace {
 
 const int64_t kMaxDim = (int64_t)1 << 30;
+const int64_t kMaxLd = (int64_t)1 << 40;   // keeps every element offset far inside int64
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
@@ -169,6 +170,8 @@ int plan_copy(const void* src, const void* dst, const int64_t shape[2], int dtyp
   if (!valid_kind(sl->kind) || !valid_kind(dl->kind) || sl->reserved || dl->reserved)
     return fail(TG_E_LAYOUT, "unknown layout kind or nonzero reserved field");
   if (sl->ld < 0 || dl->ld < 0) return fail(TG_E_LAYOUT, "negative leading dimension");
+  if (sl->ld > kMaxLd || dl->ld > kMaxLd)
+    return fail(TG_E_LAYOUT, "leading dimension above 2^40 elements");
   if (opts && opts->flags) return fail(TG_E_ARG, "opts->flags must be 0");
 
   std::memset(plan, 0, sizeof *plan);

@@ -92,6 +92,7 @@ int plan_frag(bool store, const void* mem, const void* image, const int64_t shap
   const int64_t lines = col_major ? cols : rows, line_len = col_major ? rows : cols;
   const int64_t ld = layout->ld ? layout->ld : line_len;
   if (layout->ld < 0 || ld < line_len) return fail(TG_E_LAYOUT, "leading dimension below the line length");
+  if (ld > ((int64_t)1 << 40)) return fail(TG_E_LAYOUT, "leading dimension above 2^40 elements");
 
   std::memset(plan, 0, sizeof *plan);
   std::memset(args, 0, sizeof *args);
