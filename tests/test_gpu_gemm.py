@@ -120,14 +120,48 @@ def test_beta0_ignores_nan_c():
     assert torch.isfinite(D1).all() and torch.equal(D1, D2)
 
 
-def _sampled(M, N, K, fmt, ta, tb, beta, inputs, sample_seed, tag):
+# Shapes the 256x256 direct-load kernel serves without being whole blocks: ragged M and / or
+# N, stage counts (64 K each) odd, even and one, and a partial last stage (K % 64 = 8 .. 56);
+# M or N below one block.  Every case has at least 256 blocks, so the direct kernel runs.
+DIRECT_RAGGED = [(4000, 4008, 8), (4000, 4008, 40), (4112, 4104, 64), (4096, 4096, 192),
+                 (4096, 4096, 200), (4000, 4104, 136), (4016, 4000, 256), (4080, 4096, 312),
+                 (16, 65544, 24), (65552, 8, 88)]
+
+
+@pytest.mark.parametrize("M,N,K", DIRECT_RAGGED)
+@pytest.mark.parametrize("fmt,beta", [("f16", 0.0), ("bf16", 1.0)])
+def test_direct_ragged_shapes(M, N, K, fmt, beta):
+    plan = tg.tile_gemm_plan(0x100000, 0x40000000, 0x80000000 if beta else None, 0xC0000000,
+                             M, N, K, 0, 0, beta, FMT[fmt])
+    assert (plan.block_m, plan.block_n, plan.loader) == (256, 256, 1)
+    assert plan.bounds_checked == int(M % 256 != 0 or N % 256 != 0 or K % 64 != 0)
+    say(f"gemm direct ragged {M}x{N}x{K} {fmt} beta={beta}")
+    full_check(M, N, K, fmt, False, False, beta, (M + 5, N + 6, K + 7))
+
+
+@pytest.mark.parametrize("M,N,K", [(4000, 4008, 40), (4000, 4104, 136), (16, 65544, 24),
+                                   (65552, 8, 88)])
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_direct_ragged_transposes(M, N, K, ta, tb, fmt):
+    say(f"gemm direct ragged {M}x{N}x{K} {fmt} transA={ta} transB={tb}")
+    full_check(M, N, K, fmt, ta, tb, 1.0, (17, 18, 19))
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, True)])
+def test_direct_ragged_in_place(ta, tb):
+    say(f"gemm direct ragged in-place C==D 4000x4008x136 transA={ta} transB={tb}")
+    full_check(4000, 4008, 136, "bf16", ta, tb, 1.0, (21, 22, 23), c_is_d=True)
+
+
+def _sampled(M, N, K, fmt, ta, tb, beta, inputs, sample_seed, tag, bounds=0):
     a_bits, b_bits, c = inputs
     say(f"gemm {tag}: {M}x{N}x{K} {fmt} transA={ta} transB={tb} beta={beta}")
     A, B = upload_bits(a_bits), upload_bits(b_bits)
     Cd = upload_f32(c) if beta == 1.0 else None
     D = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
     plan = tg.tile_gemm_plan(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
-    assert (plan.block_m, plan.block_n, plan.bounds_checked, plan.loader) == (256, 256, 0, 1)
+    assert (plan.block_m, plan.block_n, plan.bounds_checked, plan.loader) == (256, 256, bounds, 1)
     tg.tile_gemm(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
     D2 = torch.empty_like(D)
     tg.tile_gemm(A, B, Cd, D2, M, N, K, ta, tb, beta, FMT[fmt])
@@ -148,3 +182,19 @@ def test_gemm_8192_bf16_beta0_sampled():
 
 def test_gemm_8192_f16_transa_beta1_sampled():
     _sampled(8192, 8192, 8192, "f16", True, False, 1.0, synth.gemm8k_f16_inputs(), 57, "8192 f16")
+
+
+def test_gemm_8000_ragged_sampled():
+    # 8000 = 31 blocks + 64 rows; 8000 K = 125 stages (odd), no partial stage
+    M = N = K = 8000
+    s = float(1.0 / np.sqrt(K))
+    inputs = synth.gemm_inputs(M, N, K, "bf16", False, False, 0.0, (61, 62, 63), a_scale=s, b_scale=s)
+    _sampled(M, N, K, "bf16", False, False, 0.0, inputs, 59, "8000 bf16", bounds=1)
+
+
+def test_gemm_ragged_partial_stage_sampled():
+    # K = 8008: 126 stages, the last holding 8 K; transA, beta 1
+    M, N, K = 8016, 8200, 8008
+    s = float(1.0 / np.sqrt(K))
+    inputs = synth.gemm_inputs(M, N, K, "f16", True, False, 1.0, (64, 65, 66), a_scale=s, b_scale=s)
+    _sampled(M, N, K, "f16", True, False, 1.0, inputs, 67, "ragged partial stage", bounds=1)

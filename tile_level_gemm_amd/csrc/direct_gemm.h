@@ -26,6 +26,12 @@
 //  * the K loop is unrolled by two so each half names its LDS stage at compile time; the
 //    next stage's loads are issued at the top of an iteration and the next K step's
 //    fragments are read while the current step's MFMAs run.
+//  * ragged shapes: the buffer range check compares the whole offset (VGPR + SGPR +
+//    immediate) with num_records and returns zeros past it without touching memory (measured
+//    on gfx950 for the register and the LDS forms), so operand rows past M or N, and k-rows
+//    of an M/N-major operand past K, read as zero.  A K-major operand's last stage when K is
+//    not a whole number of stages would read the next row's K instead: there the lanes whose
+//    chunk lies past K get a VGPR offset of 2^31, out of range whatever else is added.
 //
 // Internal header: included by gemm_direct.hip (16-bit instantiations) and gemm_fp8.hip.
 #pragma once
@@ -135,12 +141,15 @@ constexpr int SKV = 1, SMV = 1;   // swizzle variants in use (see sk / sm)
 // i writes 1 KiB block b = PER·wave + i = rows 8b .. 8b+7.  Lane l fills physical slot l%8
 // of row 8b + l/8 and so fetches logical chunk (l%8) ^ sk(row).  sk(row) depends on the
 // lane and on i's parity only (PER is even), so two byte offsets cover all instructions.
+// kbyte[p]: the byte of the 128-byte K row where that chunk starts (parity p).
 template <int PER, int E>
-__device__ __forceinline__ void km_dma_offsets(int64_t ld, int wave, int lane, uint32_t (&off)[2]) {
+__device__ __forceinline__ void km_dma_offsets(int64_t ld, int wave, int lane, uint32_t (&off)[2],
+                                               uint32_t (&kbyte)[2]) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const uint32_t r = (uint32_t)(8 * PER * wave + 8 * p + (lane >> 3));
     const uint32_t kc = ((uint32_t)lane & 7u) ^ sk<SKV>(r);
+    kbyte[p] = kc * 16u;
     if constexpr (E == 2) off[p] = (r * (uint32_t)ld + kc * 8u) * 2u;   // bytes; < 256·K·2 < 2^32
     else off[p] = r * (uint32_t)ld + kc * 16u;                          // bytes; < 256·K < 2^32
   }
@@ -233,6 +242,7 @@ struct Operand {
   using EL = Elem<DT>;
   using Frag = typename EL::Frag;
   uint32_t dma[2];   // byte offsets of the two DMA parities
+  uint32_t kbyte[2]; // K-major: first byte within the K row of each parity's chunk
   uint32_t frag[4];  // byte offsets: per K-major read slot, or per M/N-major tile
 
   // LDS read instructions per fragment and per K step
@@ -247,7 +257,7 @@ struct Operand {
       mn_dma_offsets<PER>(ld, wave, lane, dma);
       mn_frag_offsets<T>(base, lane, frag);
     } else {
-      km_dma_offsets<PER, EL::kBytes>(ld, wave, lane, dma);
+      km_dma_offsets<PER, EL::kBytes>(ld, wave, lane, dma, kbyte);
       km_frag_offsets<EL::kFp8>(base, lane, frag);
     }
   }
@@ -260,17 +270,22 @@ struct Operand {
   }
   // Issue the PER DMA instructions of one stage (buffer_load_dwordx4 ... lds): per-lane byte
   // offset `dma[i & 1]` (VGPR), stage and instruction offset `soff` (SGPR), LDS block address
-  // in M0 — no per-instruction vector arithmetic.  `wave` is wave-uniform.
-  __device__ __forceinline__ void load(uint32_t stage_off, int64_t ld, uint8_t* stage,
-                                       int wave) const {
+  // in M0 — no per-instruction vector arithmetic.  `wave` is wave-uniform.  TAIL: only the
+  // first `lim` bytes of each K row are valid in this stage; a K-major lane whose chunk
+  // starts at or past them reads zeros (M/N-major k-rows past K are past the operand's end).
+  template <bool TAIL = false>
+  __device__ __forceinline__ void load(uint32_t stage_off, int64_t ld, uint8_t* stage, int wave,
+                                       uint32_t lim = kRowBytes) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      uint32_t v = dma[i & 1];
+      if constexpr (TAIL && !MN) v = kbyte[i & 1] < lim ? v : 0x80000000u;
       // K-major: +8 rows per instruction pair; M/N-major: +2 (16-bit) or +4 (fp8) k-rows
       const uint32_t step = MN ? (EL::kFp8 ? (uint32_t)(4 * (i & ~1)) * (uint32_t)ld
                                            : (uint32_t)(2 * (i & ~1)) * (uint32_t)ld * 2u)
                                : (uint32_t)(8 * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * PER + i) * 1024),
-                                               16, dma[i & 1], stage_off + step, 0, 0);
+                                               16, v, stage_off + step, 0, 0);
     }
   }
   __device__ __forceinline__ void frags(const uint8_t* stage, int s, Frag (&f)[T]) const {
@@ -369,12 +384,15 @@ __device__ __forceinline__ void interleave_inplace() {
 
 // Number of K stages a kernel serves: even, odd and at least 3, or exactly one.  Each shape
 // has its own peeled tail, so every LDS address is a compile-time immediate and no
-// accumulator state merges across branches.
-enum KStages { kEven = 0, kOdd = 1, kSingle = 2 };
+// accumulator state merges across branches.  kTail (added to a shape, 16-bit operands): the
+// last stage may hold fewer than 64 K, stages = ceil(K / 64).
+enum KStages { kEven = 0, kOdd = 1, kSingle = 2, kTail = 4 };
 
 // WGM x WGN waves; wave tile (256/WGM) x (256/WGN).  BOUNDS: M or N is not a whole number of
 // blocks; operand rows past the end read as zero (buffer range check) and the epilogue skips
-// rows and columns past M and N.  KS: the KStages shape of K / (K per stage).
+// rows and columns past M and N.  An operand row past M or N only feeds outputs that are
+// never stored, so the data there need not be zero, only never fetched from outside the
+// operand.  KS: the KStages shape of the stage count, plus kTail.
 template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   using EL = Elem<DT>;
@@ -384,7 +402,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int PER = 32 / NW;   // DMA blocks per operand per wave per stage
   constexpr int E = EL::kBytes, BK = EL::kBK, NS = EL::kSteps;
+  constexpr int KSH = KS & 3;
+  constexpr bool TAIL = (KS & kTail) != 0;
   static_assert(PER % 2 == 0 && TM >= 1 && TN >= 1 && TM <= 4 && TN <= 4, "wave grid");
+  static_assert(!TAIL || !EL::kFp8, "a partial last stage is served for 16-bit operands");
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[BN * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[BM * kRowBytes];
@@ -444,7 +465,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   //   then step NS-1's MFMAs (operands already in registers) overlap the reads of stage
   //   kt+1's first fragments and the DMA of stage kt+2 into `cur`.
   // The last two stages are peeled off the loop so the steady-state body is branch free.
-  const int KT = g.K / BK;   // >= 1, of shape KS
+  const int KT = TAIL ? (g.K + BK - 1) / BK : g.K / BK;   // >= 1, of shape KSH
+  // valid bytes of each K row in stage s: all 128 but in a partial last stage
+  const uint32_t krem = (uint32_t)(g.K - (KT - 1) * BK) * E;
+  auto lim = [&](int s) -> uint32_t { return s == KT - 1 ? krem : (uint32_t)kRowBytes; };
+  auto load_ab = [&](uint32_t s, uint8_t* stage_a, uint8_t* stage_b) {
+    oa.template load<TAIL>(s * adv_a, lda, stage_a, wave, lim((int)s));
+    ob.template load<TAIL>(s * adv_b, ldb, stage_b, wave, lim((int)s));
+  };
 
   // Block scales (scaled fp8): each stage's 4 scale bytes of every row of the block (K/32
   // bytes per row, 4 per 128-K stage) go to LDS by one 4-byte-per-lane DMA per wave: waves
@@ -485,8 +513,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
     }
   };
 
-  oa.load(0u, lda, sa0, wave);
-  ob.load(0u, ldb, sb0, wave);
+  load_ab(0u, sa0, sb0);
   qload(0u, qs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -494,9 +521,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   oa.frags(sa0, 0, a);
   ob.frags(sb0, 0, b);
   qread(qs0);
-  if constexpr (KS != kSingle) {
-    oa.load(adv_a, lda, sa1, wave);
-    ob.load(adv_b, ldb, sb1, wave);
+  if constexpr (KSH != kSingle) {
+    load_ab(1u, sa1, sb1);
     qload(1u, qs1);
   }
 
@@ -556,8 +582,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if constexpr (decltype(dma)::value) {
-        oa.load((uint32_t)(kt + 2) * adv_a, lda, ca, wave);
-        ob.load((uint32_t)(kt + 2) * adv_b, ldb, cb, wave);
+        load_ab((uint32_t)(kt + 2), ca, cb);
         qload((uint32_t)(kt + 2), cq);
       }
       step_inplace(na, nb_, 0, next, dma, std::integral_constant<int, 1>{}, nq);
@@ -581,10 +606,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
       oa.frags(na, 0, an);
       ob.frags(nb_, 0, bn);
     }
-    if constexpr (decltype(dma)::value) {
-      oa.load((uint32_t)(kt + 2) * adv_a, lda, ca, wave);
-      ob.load((uint32_t)(kt + 2) * adv_b, ldb, cb, wave);
-    }
+    if constexpr (decltype(dma)::value) load_ab((uint32_t)(kt + 2), ca, cb);
     mfmas(a, b);
     if constexpr (decltype(dma)::value) interleave<kMfma, kReads, kDma>();
     else if constexpr (decltype(next)::value) interleave<kMfma, kReads, 0>();
@@ -665,16 +687,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   // for an odd count); then the last two (or three, or the only one).
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if constexpr (KS == kSingle) {
+  if constexpr (KSH == kSingle) {
     stage(sa0, sb0, sa1, sb1, qs0, qs1, 0, F_{}, F_{});
   } else {
-    constexpr int odd = KS == kOdd ? 1 : 0;
+    constexpr int odd = KSH == kOdd ? 1 : 0;
     int kt = 0;
     for (; kt + 2 + odd < KT; kt += 2) {
       stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, T_{}, T_{});
       stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, T_{}, T_{});
     }
-    if constexpr (KS == kEven) {
+    if constexpr (KSH == kEven) {
       stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, F_{}, T_{});
       stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, F_{}, F_{});
     } else {

@@ -1,6 +1,7 @@
 // Large-tile GEMM on gfx950 with direct global -> LDS operand loads: the f16 / bf16
-// instantiations of the kernel template in direct_gemm.h and their host dispatch.
-#include "direct_gemm.h"
+// instantiations of the kernel template in direct_gemm.h for whole 256x256 blocks and K a
+// multiple of 128, and the host dispatch (ragged shapes: gemm_direct_*.hip).
+#include "gemm_direct_launch.h"
 
 namespace tg {
 namespace {
@@ -17,18 +18,25 @@ hipError_t launch_direct_dt(const GemmArgs& g, int64_t grid, hipStream_t s) {
 
 }  // namespace
 
-// Whole 256x256 tiles, K a multiple of 128, and each operand under 2 GiB so that every
-// buffer offset (per-lane plus per-stage) fits the 32-bit offset fields.
+// Each operand under 2 GiB, so that every buffer offset (per-lane plus per-stage, and the
+// out-of-range 2^31 of a partial last stage plus the stage offset) fits the 32-bit fields.
 bool direct_gemm_fits(int64_t M, int64_t N, int64_t K) {
   const int64_t lim = (int64_t)1 << 31;
-  return M % BM == 0 && N % BN == 0 && K % (2 * Elem<TG_F16>::kBK) == 0 && K > 0 && M * K * 2 < lim &&
-         K * N * 2 < lim;
+  return M > 0 && N > 0 && K > 0 && M * K * 2 < lim && K * N * 2 < lim;
 }
 
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
                               hipStream_t s) {
   // A is M/N-major when stored [K][M] (transA); B is M/N-major when stored [K][N] (!transB).
   const bool amn = trans_a != 0, bmn = trans_b == 0;
+  const bool exact = g.M % BM == 0 && g.N % BN == 0 && g.K % (2 * Elem<TG_F16>::kBK) == 0;
+  if (!exact) {
+    const bool bounds = g.M % BM != 0 || g.N % BN != 0;
+    if (amn && bmn) return launch_direct16_mm(g, grid, dtype, bounds, s);
+    if (amn) return launch_direct16_mk(g, grid, dtype, bounds, s);
+    if (bmn) return launch_direct16_km(g, grid, dtype, bounds, s);
+    return launch_direct16_kk(g, grid, dtype, bounds, s);
+  }
   if (dtype == TG_F16) {
     if (amn && bmn) return launch_direct_dt<true, true, TG_F16>(g, grid, s);
     if (amn) return launch_direct_dt<true, false, TG_F16>(g, grid, s);

@@ -1,0 +1,12 @@
+// 16-bit GEMM instantiations of the direct-load kernel template for ragged shapes, A stored
+// [M,K] and B stored [K,N].
+#include "gemm_direct_launch.h"
+
+namespace tg {
+
+hipError_t launch_direct16_km(const GemmArgs& g, int64_t grid, int dtype, bool bounds,
+                              hipStream_t s) {
+  return launch_direct16_layout<false, true>(g, grid, dtype, bounds, s);
+}
+
+}  // namespace tg
