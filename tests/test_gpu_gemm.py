@@ -154,14 +154,14 @@ def test_direct_ragged_in_place(ta, tb):
     full_check(4000, 4008, 136, "bf16", ta, tb, 1.0, (21, 22, 23), c_is_d=True)
 
 
-def _sampled(M, N, K, fmt, ta, tb, beta, inputs, sample_seed, tag, bounds=0):
+def _sampled(M, N, K, fmt, ta, tb, beta, inputs, sample_seed, tag, bounds=0, loader=1):
     a_bits, b_bits, c = inputs
     say(f"gemm {tag}: {M}x{N}x{K} {fmt} transA={ta} transB={tb} beta={beta}")
     A, B = upload_bits(a_bits), upload_bits(b_bits)
     Cd = upload_f32(c) if beta == 1.0 else None
     D = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
     plan = tg.tile_gemm_plan(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
-    assert (plan.block_m, plan.block_n, plan.bounds_checked, plan.loader) == (256, 256, bounds, 1)
+    assert (plan.block_m, plan.block_n, plan.bounds_checked, plan.loader) == (256, 256, bounds, loader)
     tg.tile_gemm(A, B, Cd, D, M, N, K, ta, tb, beta, FMT[fmt])
     D2 = torch.empty_like(D)
     tg.tile_gemm(A, B, Cd, D2, M, N, K, ta, tb, beta, FMT[fmt])
@@ -198,3 +198,23 @@ def test_gemm_ragged_partial_stage_sampled():
     s = float(1.0 / np.sqrt(K))
     inputs = synth.gemm_inputs(M, N, K, "f16", True, False, 1.0, (64, 65, 66), a_scale=s, b_scale=s)
     _sampled(M, N, K, "f16", True, False, 1.0, inputs, 67, "ragged partial stage", bounds=1)
+
+
+# Operands at the direct kernel's limit: its buffer offsets are 32-bit, so it serves operands
+# under 2 GiB; from 2 GiB on the 64-bit-indexed tiled kernel takes over.
+@pytest.mark.parametrize("ta", [False, True])
+def test_gemm_operand_just_under_2gib_sampled(ta):
+    # A = 130928 x 8200 f16 = 2 GiB - 256 KiB; ragged M, and a last stage of 8 K
+    M, N, K = 130928, 256, 8200
+    assert M * K * 2 < 1 << 31
+    s = float(1.0 / np.sqrt(K))
+    inputs = synth.gemm_inputs(M, N, K, "f16", ta, False, 1.0, (71, 72, 73), a_scale=s, b_scale=s)
+    _sampled(M, N, K, "f16", ta, False, 1.0, inputs, 74, "A just under 2 GiB", bounds=1)
+
+
+def test_gemm_operand_of_2gib_sampled():
+    # A = 131072 x 8192 f16 = 2 GiB: the tiled kernel, element offsets past 2^31 bytes
+    M, N, K = 131072, 256, 8192
+    s = float(1.0 / np.sqrt(K))
+    inputs = synth.gemm_inputs(M, N, K, "f16", False, True, 0.0, (75, 76, 0), a_scale=s, b_scale=s)
+    _sampled(M, N, K, "f16", False, True, 0.0, inputs, 77, "A of 2 GiB", bounds=0, loader=0)
