@@ -248,8 +248,9 @@ def test_gemm_kernel_choice():
     assert (p.kernel, p.block_m, p.block_n, p.grid, p.bounds_checked) == (tg.TG_GEMM_TILED, 256, 256, 1024, 0)
     p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 528, 520, 264, 1, 0, 0.0, tg.TG_F16)
     assert p.kernel == tg.TG_GEMM_TILED and p.bounds_checked
-    # the direct-load kernel serves every shape with at least 256 blocks of 256x256, ragged ones
-    # with range-checked operand loads and a masked epilogue; fewer blocks take smaller tiles
+    # the direct-load kernel serves every shape with at least 256 blocks of 256x256, or else 128
+    # of 128x128, ragged ones with range-checked operand loads and a masked epilogue; fewer
+    # blocks take the VGPR-staged kernel on 64x64 tiles
     p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 8192, 8192, 8192, 0, 0, 0.0, tg.TG_BF16)
     assert (p.threads, p.bounds_checked, p.loader) == (512, 0, 1)
     p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 8000, 8000, 8000, 0, 0, 0.0, tg.TG_BF16)
@@ -257,7 +258,11 @@ def test_gemm_kernel_choice():
     p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 16, 65544, 24, 0, 0, 0.0, tg.TG_F16)
     assert (p.block_m, p.grid, p.bounds_checked, p.loader) == (256, 257, 1, 1)
     p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 2048, 2048, 2048, 0, 0, 0.0, tg.TG_F16)
-    assert (p.block_m, p.loader) == (128, 0)
+    assert (p.block_m, p.grid, p.wave_m, p.wave_n, p.threads, p.loader) == (128, 256, 64, 32, 512, 1)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 1552, 2056, 200, 0, 0, 0.0, tg.TG_F16)
+    assert (p.block_m, p.grid, p.bounds_checked, p.loader) == (128, 221, 1, 1)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 1024, 1024, 1024, 0, 0, 0.0, tg.TG_F16)
+    assert (p.block_m, p.grid, p.loader) == (64, 256, 0)
     p = tg.tile_gemm_plan(None, None, None, D_ADDR, 16, 8, 0, 0, 0, 0.0, tg.TG_F16)
     assert p.kernel == tg.TG_GEMM_FILL
     p = tg.tile_gemm_plan(None, None, None, None, 0, 8, 16, 0, 0, 0.0, tg.TG_F16)

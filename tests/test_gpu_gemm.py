@@ -148,6 +148,30 @@ def test_direct_ragged_transposes(M, N, K, ta, tb, fmt):
     full_check(M, N, K, fmt, ta, tb, 1.0, (17, 18, 19))
 
 
+# 128x128 direct-load blocks: problems with fewer than 256 blocks of 256x256 but at least 128
+# of 128x128; whole and ragged blocks, every stage-count shape, a partial last stage.
+DIRECT_128 = [(2048, 2048, 512), (1552, 2056, 200), (128, 16384, 64), (1040, 2064, 8),
+              (2048, 1024, 1032), (1536, 1536, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", DIRECT_128)
+@pytest.mark.parametrize("fmt,beta", [("f16", 1.0), ("bf16", 0.0)])
+def test_direct128_shapes(M, N, K, fmt, beta):
+    plan = tg.tile_gemm_plan(0x100000, 0x40000000, 0x80000000 if beta else None, 0xC0000000,
+                             M, N, K, 0, 0, beta, FMT[fmt])
+    assert (plan.block_m, plan.block_n, plan.loader) == (128, 128, 1)
+    say(f"gemm direct 128 {M}x{N}x{K} {fmt} beta={beta}")
+    full_check(M, N, K, fmt, False, False, beta, (M + 8, N + 9, K + 10))
+
+
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_direct128_transposes(ta, tb, fmt):
+    M, N, K = 1552, 2056, 200
+    say(f"gemm direct 128 {M}x{N}x{K} {fmt} transA={ta} transB={tb}")
+    full_check(M, N, K, fmt, ta, tb, 1.0, (24, 25, 26))
+
+
 @pytest.mark.parametrize("ta,tb", [(False, False), (True, True)])
 def test_direct_ragged_in_place(ta, tb):
     say(f"gemm direct ragged in-place C==D 4000x4008x136 transA={ta} transB={tb}")

@@ -115,8 +115,9 @@ __device__ __forceinline__ uint32_t sk(uint32_t r) {
   if constexpr (SK == 0) return r & 7u;
   else return (r & 7u) ^ ((r >> 3) & 1u);
 }
-// M/N-major stage: 64 k-rows x 512 bytes (32 chunks); physical chunk = c ^ sm(k).  A
-// transposing read touches 32 bytes (2 chunks) in each of 4 consecutive k-rows per 16 lanes.
+// M/N-major stage: 64 k-rows x 512 bytes (32 chunks) for 256-wide blocks, x 256 bytes (16
+// chunks) for 128-wide ones; physical chunk = c ^ sm(k).  A transposing read touches 32
+// bytes (2 chunks) in each of 4 consecutive k-rows per 16 lanes.
 //   SM 0: 2(k & 3) — the four rows land in four distinct 32-byte bank slots of 128 bytes;
 //   SM 1: 2(k & 3) ^ 8(k & 1) — additionally, two adjacent 16-lane groups (mn + 16) land
 //         in eight distinct slots of 256 bytes.
@@ -154,15 +155,17 @@ __device__ __forceinline__ void km_dma_offsets(int64_t ld, int wave, int lane, u
     else off[p] = r * (uint32_t)ld + kc * 16u;                          // bytes; < 256·K < 2^32
   }
 }
-// DMA for an M/N-major 16-bit operand: instruction i writes block b = PER·wave + i = k-rows
-// 2b, 2b+1; lane l fills slot l%32 of k-row 2b + l/32, logical chunk (l%32) ^ sm(k); sm
-// depends on k & 3, i.e. on the lane and i's parity.
-template <int PER>
+// DMA for an M/N-major 16-bit operand with ROWB-byte k-rows (CH = ROWB/16 chunks, RPB =
+// 1024/ROWB k-rows per 1 KiB block): instruction i writes block b = PER·wave + i = k-rows
+// RPB·b .. RPB·b + RPB-1; lane l fills slot l%CH of k-row RPB·b + l/CH, logical chunk
+// (l%CH) ^ sm(k); sm depends on k & 3, i.e. on the lane and i's parity.
+template <int PER, int ROWB>
 __device__ __forceinline__ void mn_dma_offsets(int64_t ld, int wave, int lane, uint32_t (&off)[2]) {
+  constexpr uint32_t CH = ROWB / 16, RPB = 1024 / ROWB;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const uint32_t k = (uint32_t)(2 * PER * wave + 2 * p + (lane >> 5));
-    const uint32_t c = ((uint32_t)lane & 31u) ^ sm<SMV>(k);
+    const uint32_t k = RPB * (uint32_t)(PER * wave + p) + (uint32_t)lane / CH;
+    const uint32_t c = ((uint32_t)lane % CH) ^ sm<SMV>(k);
     off[p] = (k * (uint32_t)ld + c * 8u) * 2u;    // bytes; < 64·N·2 < 2^32
   }
 }
@@ -200,8 +203,8 @@ __device__ __forceinline__ void km_frag_offsets(int row_base, int lane, uint32_t
 // M/N-major fragment of 32-column tile t, K step s, half h (two ds_read_b64_tr_b16): lane
 // l = 16g + j supplies k-row 16s + 8(g/2) + 4h + j/4 and columns mn_base + 32t + 16(g&1) +
 // 4(j&3) .. +3.  sm(k) depends on j only; its bits 2-3 XOR with the tile index, so one byte
-// offset per tile t; s and h are immediates (16s + 4h rows of 512 bytes).
-template <int T>
+// offset per tile t; s and h are immediates (16s + 4h rows of ROWB bytes).
+template <int T, int ROWB>
 __device__ __forceinline__ void mn_frag_offsets(int mn_base, int lane, uint32_t (&off)[4]) {
   const uint32_t g = (uint32_t)lane >> 4, j = (uint32_t)lane & 15u;
   const uint32_t krow = 8u * (g >> 1) + (j >> 2);
@@ -211,7 +214,7 @@ __device__ __forceinline__ void mn_frag_offsets(int mn_base, int lane, uint32_t 
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint32_t c = ((uint32_t)mn_base + 32u * (uint32_t)(t < T ? t : 0) + mn_lane) >> 3;
-    off[t] = krow * 512u + ((c ^ x) << 4) + byte;
+    off[t] = krow * (uint32_t)ROWB + ((c ^ x) << 4) + byte;
   }
 }
 
@@ -236,11 +239,13 @@ __device__ __forceinline__ void mn8_frag_offsets(int mn_base, int lane, uint32_t
 }
 
 // One operand of one wave: T fragments of 32 rows/columns per K step, PER DMA instructions
-// per stage.
-template <bool MN, int T, int PER, int DT>
+// per stage; BS rows (K-major) or columns (M/N-major) per block.
+template <bool MN, int T, int PER, int DT, int BS>
 struct Operand {
   using EL = Elem<DT>;
   using Frag = typename EL::Frag;
+  static constexpr int kRowB = BS * EL::kBytes;   // M/N-major 16-bit: bytes per k-row
+  static_assert(!(MN && EL::kFp8) || BS == 256, "fp8 M/N-major stages are 128 k x 256 bytes");
   uint32_t dma[2];   // byte offsets of the two DMA parities
   uint32_t kbyte[2]; // K-major: first byte within the K row of each parity's chunk
   uint32_t frag[4];  // byte offsets: per K-major read slot, or per M/N-major tile
@@ -254,8 +259,8 @@ struct Operand {
       mn8_dma_offsets<PER>(ld, wave, lane, dma);
       mn8_frag_offsets<T>(base, lane, frag);
     } else if constexpr (MN) {
-      mn_dma_offsets<PER>(ld, wave, lane, dma);
-      mn_frag_offsets<T>(base, lane, frag);
+      mn_dma_offsets<PER, kRowB>(ld, wave, lane, dma);
+      mn_frag_offsets<T, kRowB>(base, lane, frag);
     } else {
       km_dma_offsets<PER, EL::kBytes>(ld, wave, lane, dma, kbyte);
       km_frag_offsets<EL::kFp8>(base, lane, frag);
@@ -280,9 +285,10 @@ struct Operand {
     for (int i = 0; i < PER; ++i) {
       uint32_t v = dma[i & 1];
       if constexpr (TAIL && !MN) v = kbyte[i & 1] < lim ? v : 0x80000000u;
-      // K-major: +8 rows per instruction pair; M/N-major: +2 (16-bit) or +4 (fp8) k-rows
+      // K-major: +8 rows per instruction pair; M/N-major: +1024/kRowB k-rows (16-bit) or +4
+      // (fp8)
       const uint32_t step = MN ? (EL::kFp8 ? (uint32_t)(4 * (i & ~1)) * (uint32_t)ld
-                                           : (uint32_t)(2 * (i & ~1)) * (uint32_t)ld * 2u)
+                                           : (uint32_t)((1024 / kRowB) * (i & ~1)) * (uint32_t)ld * 2u)
                                : (uint32_t)(8 * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * PER + i) * 1024),
                                                16, v, stage_off + step, 0, 0);
@@ -298,7 +304,7 @@ struct Operand {
         u32x4 out;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint8_t* p = stage + frag[t] + (16 * s + 4 * h) * 512;
+          const uint8_t* p = stage + frag[t] + (16 * s + 4 * h) * kRowB;
           const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
           out[2 * h] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
           out[2 * h + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
@@ -388,28 +394,29 @@ __device__ __forceinline__ void interleave_inplace() {
 // last stage may hold fewer than 64 K, stages = ceil(K / 64).
 enum KStages { kEven = 0, kOdd = 1, kSingle = 2, kTail = 4 };
 
-// WGM x WGN waves; wave tile (256/WGM) x (256/WGN).  BOUNDS: M or N is not a whole number of
-// blocks; operand rows past the end read as zero (buffer range check) and the epilogue skips
+// WGM x WGN waves on a BS x BS block (256, or 128 for 16-bit operands); wave tile
+// (BS/WGM) x (BS/WGN).  BOUNDS: M or N is not a whole number of blocks; operand rows past the end read as zero (buffer range check) and the epilogue skips
 // rows and columns past M and N.  An operand row past M or N only feeds outputs that are
 // never stored, so the data there need not be zero, only never fetched from outside the
 // operand.  KS: the KStages shape of the stage count, plus kTail.
-template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
+template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS, int BS>
+__device__ __forceinline__ void direct_body(const GemmArgs& g) {
   using EL = Elem<DT>;
   using Frag = typename EL::Frag;
   constexpr int NW = WGM * WGN;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int WM = BS / WGM, WN = BS / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int PER = 32 / NW;   // DMA blocks per operand per wave per stage
+  constexpr int PER = BS / 8 / NW;   // DMA blocks (1 KiB) per operand per wave per stage
   constexpr int E = EL::kBytes, BK = EL::kBK, NS = EL::kSteps;
   constexpr int KSH = KS & 3;
   constexpr bool TAIL = (KS & kTail) != 0;
   static_assert(PER % 2 == 0 && TM >= 1 && TN >= 1 && TM <= 4 && TN <= 4, "wave grid");
   static_assert(!TAIL || !EL::kFp8, "a partial last stage is served for 16-bit operands");
-  __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb0[BN * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sa1[BM * kRowBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb1[BN * kRowBytes];
+  static_assert(BS == 256 || (BS == 128 && !EL::kFp8), "128-wide blocks are served for 16-bit operands");
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[BS * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[BS * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[BS * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[BS * kRowBytes];
   // block scales of one stage (scaled fp8 only): A's 256 rows x 4 bytes, then B's
   __shared__ __attribute__((aligned(1024))) uint8_t qs0[EL::kScaled ? 2048 : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t qs1[EL::kScaled ? 2048 : 1];
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   const int gsz = min(g.tiles_m - first_m, kGroupM);
   const int tm = first_m + (bid % group) % gsz;
   const int tn = (bid % group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BS, n0 = tn * BS;
 
   const int tid = (int)threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -431,8 +438,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
 
   const int64_t lda = A_MN ? g.M : g.K;
   const int64_t ldb = B_MN ? g.N : g.K;
-  using OA = Operand<A_MN, TM, PER, DT>;
-  using OB = Operand<B_MN, TN, PER, DT>;
+  using OA = Operand<A_MN, TM, PER, DT, BS>;
+  using OB = Operand<B_MN, TN, PER, DT, BS>;
   OA oa;
   OB ob;
   oa.init(lda, wm, wave, lane);
@@ -706,6 +713,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
     }
   }
   epilogue();
+}
+
+// 256x256 blocks (fp8, block-scaled fp8 and 16-bit operands)
+template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
+  direct_body<A_MN, B_MN, DT, WGM, WGN, BOUNDS, KS, 256>(g);
+}
+
+// 128x128 blocks (16-bit operands): 64 KiB of LDS stages, so two workgroups share a CU; for
+// problems with too few 256x256 blocks to fill the chip.
+template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct128(GemmArgs g) {
+  direct_body<A_MN, B_MN, DT, WGM, WGN, BOUNDS, KS, 128>(g);
 }
 
 }  // namespace

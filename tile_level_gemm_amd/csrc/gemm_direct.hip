@@ -26,16 +26,17 @@ bool direct_gemm_fits(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
-                              hipStream_t s) {
+                              int bs, hipStream_t s) {
   // A is M/N-major when stored [K][M] (transA); B is M/N-major when stored [K][N] (!transB).
   const bool amn = trans_a != 0, bmn = trans_b == 0;
-  const bool exact = g.M % BM == 0 && g.N % BN == 0 && g.K % (2 * Elem<TG_F16>::kBK) == 0;
+  const bool exact = bs == 256 && g.M % bs == 0 && g.N % bs == 0 &&
+                     g.K % (2 * Elem<TG_F16>::kBK) == 0;
   if (!exact) {
-    const bool bounds = g.M % BM != 0 || g.N % BN != 0;
-    if (amn && bmn) return launch_direct16_mm(g, grid, dtype, bounds, s);
-    if (amn) return launch_direct16_mk(g, grid, dtype, bounds, s);
-    if (bmn) return launch_direct16_km(g, grid, dtype, bounds, s);
-    return launch_direct16_kk(g, grid, dtype, bounds, s);
+    const bool bounds = g.M % bs != 0 || g.N % bs != 0;
+    if (amn && bmn) return launch_direct16_mm(g, grid, dtype, bounds, bs, s);
+    if (amn) return launch_direct16_mk(g, grid, dtype, bounds, bs, s);
+    if (bmn) return launch_direct16_km(g, grid, dtype, bounds, bs, s);
+    return launch_direct16_kk(g, grid, dtype, bounds, bs, s);
   }
   if (dtype == TG_F16) {
     if (amn && bmn) return launch_direct_dt<true, true, TG_F16>(g, grid, s);

@@ -1,12 +1,12 @@
-// 16-bit GEMM instantiations of the direct-load kernel template for ragged shapes, A stored
+// 16-bit GEMM instantiations of the direct-load kernel template for ragged shapes and 128x128 blocks, A stored
 // [K,M] and B stored [K,N].
 #include "gemm_direct_launch.h"
 
 namespace tg {
 
-hipError_t launch_direct16_mm(const GemmArgs& g, int64_t grid, int dtype, bool bounds,
+hipError_t launch_direct16_mm(const GemmArgs& g, int64_t grid, int dtype, bool bounds, int bs,
                               hipStream_t s) {
-  return launch_direct16_layout<true, true>(g, grid, dtype, bounds, s);
+  return launch_direct16_layout<true, true>(g, grid, dtype, bounds, bs, s);
 }
 
 }  // namespace tg

@@ -376,7 +376,7 @@ int launch_gemm(const GemmArgs& g, const GemmConfig& c, int trans_a, int trans_b
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (c.kernel == TG_GEMM_TILED && c.direct) {
-    e = launch_gemm_direct(g, c.grid, trans_a, trans_b, dtype, s);
+    e = launch_gemm_direct(g, c.grid, trans_a, trans_b, dtype, c.bm, s);
   } else if (c.kernel == TG_GEMM_FILL) {
     hipLaunchKernelGGL(gemm_fill, dim3((unsigned)c.grid), dim3(256), 0, s, g);
     e = hipGetLastError();

@@ -151,7 +151,11 @@ bool tile_steps_aligned(const Side& s, int64_t tile_rows, int64_t tile_cols, int
 // step, accumulated in place ([SYNC-GEMM] 四 step 3); on gfx950 a workgroup
 // owns a block of output tiles so that operands staged once in LDS feed many
 // MFMAs.  The block size is the largest that still gives the chip enough
-// workgroups (256 CUs); tiny problems use the register kernel.
+// workgroups (256 CUs); tiny problems use the register kernel.  256- and 128-wide
+// blocks take the direct-load kernel when each operand is under 2 GiB.  Smaller
+// blocks only where the larger ones are too few: measured, 128-wide blocks lose to
+// 256-wide ones once there are 256 of those (8192^3 bf16: 1082 against 890 us,
+// 6000^3: 554 against 435 us).
 GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   GemmConfig c{};
   if (M == 0 || N == 0) {
@@ -191,10 +195,11 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   c.bounds = (M % c.bm) != 0 || (N % c.bn) != 0 || (K % c.bk) != 0;
   c.lds_bytes = 2 * (c.bm + c.bn) * 128;
   c.grid = blocks(c.bm, c.bn);
-  c.direct = c.bm == 256 && direct_gemm_fits(M, N, K);
-  if (c.direct) {   // gemm_direct: 8 waves of 128 x 64
-    c.wm = 128;
-    c.wn = 64;
+  // gemm_direct (256x256) and gemm_direct128 (128x128): 8 waves, a 2 x 4 wave grid
+  c.direct = c.bm >= 128 && direct_gemm_fits(M, N, K);
+  if (c.direct) {
+    c.wm = c.bm / 2;
+    c.wn = c.bn / 4;
     c.threads = 512;
   }
   return c;

@@ -106,8 +106,9 @@ GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K);
 // scaled: block-scaled fp8 (E8M0 scales in g.SA, g.SB).
 hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int a_dtype,
                            int b_dtype, bool bounds, bool scaled, hipStream_t s);
+// 16-bit direct-load GEMM on bs x bs blocks (256 or 128).
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
-                              hipStream_t s);
+                              int bs, hipStream_t s);
 
 // ------------------------------------------------------------ fragments ---
 // Register fragment copies (tile_frag_load / tile_frag_store).  Memory is seen as lines: Q
