@@ -38,7 +38,8 @@ METRIC = "GEMM TFLOP/s + % MFMA peak (bf16 8192³); tile-copy GB/s + % HBM peak"
 
 
 KERNEL_SOURCES = {
-    "gemm": ("gemm_direct.hip", "direct_gemm.h", "gemm_kernels.hip", "lds_layout.h", "tg_internal.h"),
+    "gemm": ("gemm_direct.hip", "gemm_direct_launch.h", "direct_gemm.h", "gemm_kernels.hip", "lds_layout.h",
+             "tg_internal.h"),
     "fp8": ("gemm_fp8.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "mx": ("gemm_mx_kk.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
