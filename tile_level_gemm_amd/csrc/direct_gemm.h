@@ -61,6 +61,7 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 constexpr int BM = 256, BN = 256;
 constexpr int kRowBytes = 128;   // bytes of K per operand row and stage
 constexpr int kGroupM = 8;       // tile-rows per scheduling group (measured: 8 beats 2, 4, 16)
+constexpr uint32_t kQGroup = 8192;   // block-scaled fp8: LDS bytes of one group of 4 stages' scales
 
 // Format codes of the template's DT parameter: TG_F16 / TG_BF16, an fp8 pair kF8 + 2·a + b,
 // or a block-scaled fp8 pair kMX + 2·a + b, with a, b the MFMA's operand format codes
@@ -417,9 +418,9 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sb1[BS * kRowBytes];
-  // block scales of one stage (scaled fp8 only): A's 256 rows x 4 bytes, then B's
-  __shared__ __attribute__((aligned(1024))) uint8_t qs0[EL::kScaled ? 2048 : 1];
-  __shared__ __attribute__((aligned(1024))) uint8_t qs1[EL::kScaled ? 2048 : 1];
+  // block scales (scaled fp8 only): a ring of three groups of four stages, each A's 256 rows
+  // x 16 bytes, then B's
+  __shared__ __attribute__((aligned(1024))) uint8_t qg[EL::kScaled ? 3 * kQGroup : 1];
 
   // tile scheduler: XCD-contiguous ranges, grouped tile-rows (as gemm_tiled)
   const int nb = (int)gridDim.x;
@@ -481,35 +482,48 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
     ob.template load<TAIL>(s * adv_b, ldb, stage_b, wave, lim((int)s));
   };
 
-  // Block scales (scaled fp8): each stage's 4 scale bytes of every row of the block (K/32
-  // bytes per row, 4 per 128-K stage) go to LDS by one 4-byte-per-lane DMA per wave: waves
-  // 0-3 carry A's 256 rows, 64 each, waves 4-7 B's.  Rows past M or N read as zero.
+  // Block scales (scaled fp8): K/32 bytes per row, 4 per 128-K stage.  They travel in groups
+  // of four stages, 16 bytes per row, into a ring of three LDS group buffers ([row][16 bytes],
+  // A's 256 rows then B's).  Stage kt loads quarter kt % 4 of group kt/4 + 2: rows 64q ..
+  // 64q + 63 of A (waves 0-3, 16 rows each) and of B (waves 4-7), four lanes per row with 4
+  // bytes each, so the lanes of a row share one cache line — 128 lines per stage, where one
+  // 4-byte load per row and stage took 512.  Group G is complete four stages before its
+  // first read, and its buffer last held group G - 3, read out two stages before.  Groups 0
+  // and 1 load before the K loop.  Rows past M or N read as zero.
   __amdgpu_buffer_rsrc_t qrsrc;
-  uint32_t qvoff = 0, qlds = 0;
+  uint32_t qvoff = 0, qlds = 0, qkb = 0;
   if constexpr (EL::kScaled) {
     const int kb = g.K / 32;
     const bool is_a = wave < 4;
     const int row0 = is_a ? m0 : n0, rows = is_a ? g.M : g.N;
     const uint8_t* qbase = (is_a ? g.SA : g.SB) + (int64_t)row0 * kb;
     qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, (rows - row0) * kb, 0x00020000);
-    qvoff = (uint32_t)(64 * (wave & 3) + lane) * (uint32_t)kb;
-    qlds = (is_a ? 0u : 1024u) + 256u * (uint32_t)(wave & 3);
+    qvoff = (uint32_t)(16 * (wave & 3) + (lane >> 2)) * (uint32_t)kb + 4u * (uint32_t)(lane & 3);
+    qlds = (is_a ? 0u : kQGroup / 2) + 256u * (uint32_t)(wave & 3);
+    qkb = (uint32_t)kb;
   }
-  auto qload = [&](uint32_t kt, uint8_t* q) {
+  // quarter q of group G (G % 3 is the ring slot)
+  auto qload_part = [&](uint32_t G, uint32_t q) {
     if constexpr (EL::kScaled)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(q + qlds), 4, qvoff, 4u * kt, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(qg + (G % 3u) * kQGroup + qlds + 1024u * q),
+                                               4, qvoff, 64u * q * qkb + 16u * G, 0, 0);
+  };
+  auto qroll = [&](int kt) { qload_part((uint32_t)(kt >> 2) + 2u, (uint32_t)(kt & 3)); };
+  // stage kt's 4 scale bytes of row 0 in the ring
+  auto qstage = [&](int kt) -> const uint8_t* {
+    return qg + ((uint32_t)(kt >> 2) % 3u) * kQGroup + 4u * (uint32_t)(kt & 3);
   };
   // This lane's scales of one stage for A tile i / B tile j, shifted so that byte 2s holds
   // the block of K step s this lane supplies (K half lane / 32).  One per-lane LDS offset per
   // operand; tiles are immediates.
   uint32_t qa[TM], qb[TN], qbn[TN];
   const uint32_t qsh = 8u * (uint32_t)(lane >> 5);
-  const uint32_t qoa = 4u * (uint32_t)(wm + (lane & 31)), qob = 1024u + 4u * (uint32_t)(wn + (lane & 31));
+  const uint32_t qoa = 16u * (uint32_t)(wm + (lane & 31)), qob = kQGroup / 2 + 16u * (uint32_t)(wn + (lane & 31));
   auto qread_a = [&](const uint8_t* q, int i) -> uint32_t {
-    return *(const uint32_t*)(q + qoa + 128 * i) >> qsh;
+    return *(const uint32_t*)(q + qoa + 512 * i) >> qsh;
   };
   auto qread_b = [&](const uint8_t* q, int j) -> uint32_t {
-    return *(const uint32_t*)(q + qob + 128 * j) >> qsh;
+    return *(const uint32_t*)(q + qob + 512 * j) >> qsh;
   };
   auto qread = [&](const uint8_t* q) {
     if constexpr (EL::kScaled) {
@@ -521,17 +535,19 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   };
 
   load_ab(0u, sa0, sb0);
-  qload(0u, qs0);
+  if constexpr (EL::kScaled) {
+#pragma unroll
+    for (uint32_t G = 0; G < 2; ++G)
+#pragma unroll
+      for (uint32_t q = 0; q < 4; ++q) qload_part(G, q);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frag a[TM], b[TN], an[TM], bn[TN];
   oa.frags(sa0, 0, a);
   ob.frags(sb0, 0, b);
-  qread(qs0);
-  if constexpr (KSH != kSingle) {
-    load_ab(1u, sa1, sb1);
-    qload(1u, qs1);
-  }
+  qread(qstage(0));
+  if constexpr (KSH != kSingle) load_ab(1u, sa1, sb1);
 
   constexpr int kMfma = TM * TN;
   constexpr int kReads = OA::kReads + OB::kReads;
@@ -579,8 +595,8 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
 
   // One K stage.  DMA: also load stage kt+2 into the buffer this stage frees; NEXT: read
   // the next stage's first fragments (false only for the last stage).
-  auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, uint8_t* cq,
-                   const uint8_t* nq, int kt, auto dma, auto next) {
+  auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, int kt, auto dma,
+                   auto next) {
     if constexpr (EL::kFp8) {
       static_assert(NS == 2, "fp8 stages are two 64-K steps");
       step_inplace(ca, cb, 1, std::true_type{}, std::false_type{}, std::integral_constant<int, 0>{},
@@ -590,9 +606,10 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
       __syncthreads();
       if constexpr (decltype(dma)::value) {
         load_ab((uint32_t)(kt + 2), ca, cb);
-        qload((uint32_t)(kt + 2), cq);
+        qroll(kt);
       }
-      step_inplace(na, nb_, 0, next, dma, std::integral_constant<int, 1>{}, nq);
+      step_inplace(na, nb_, 0, next, dma, std::integral_constant<int, 1>{},
+                   EL::kScaled ? qstage(kt + 1) : nullptr);
       return;
     }
 #pragma unroll
@@ -695,21 +712,21 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   using T_ = std::true_type;
   using F_ = std::false_type;
   if constexpr (KSH == kSingle) {
-    stage(sa0, sb0, sa1, sb1, qs0, qs1, 0, F_{}, F_{});
+    stage(sa0, sb0, sa1, sb1, 0, F_{}, F_{});
   } else {
     constexpr int odd = KSH == kOdd ? 1 : 0;
     int kt = 0;
     for (; kt + 2 + odd < KT; kt += 2) {
-      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, T_{}, T_{});
-      stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, T_{}, T_{});
+      stage(sa0, sb0, sa1, sb1, kt, T_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, kt + 1, T_{}, T_{});
     }
     if constexpr (KSH == kEven) {
-      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, F_{}, T_{});
-      stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, F_{}, F_{});
+      stage(sa0, sb0, sa1, sb1, kt, F_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, kt + 1, F_{}, F_{});
     } else {
-      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt, T_{}, T_{});
-      stage(sa1, sb1, sa0, sb0, qs1, qs0, kt + 1, F_{}, T_{});
-      stage(sa0, sb0, sa1, sb1, qs0, qs1, kt + 2, F_{}, F_{});
+      stage(sa0, sb0, sa1, sb1, kt, T_{}, T_{});
+      stage(sa1, sb1, sa0, sb0, kt + 1, F_{}, T_{});
+      stage(sa0, sb0, sa1, sb1, kt + 2, F_{}, F_{});
     }
   }
   epilogue();
