@@ -42,8 +42,11 @@ def full_check(M, N, K, af, bf, ta, tb, beta, seed, c_is_d=False):
     assert ok, f"worst |D-D_ref|/tol = {worst}"
 
 
+# K in stages of 128: one, two, three, five, 11 and 25 (the scales travel in groups of four
+# stages through a three-slot ring: partial last groups and several turns of the ring).
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (48, 32, 128), (256, 256, 256), (272, 528, 384),
-                                   (784, 1040, 640), (1024, 1024, 2048)])
+                                   (784, 1040, 640), (1024, 1024, 2048), (528, 784, 1408),
+                                   (1040, 272, 3200)])
 @pytest.mark.parametrize("beta", [0.0, 1.0])
 def test_shapes(M, N, K, beta):
     say(f"gemm_mx {M}x{N}x{K} e4m3 x e4m3 beta={beta}")
