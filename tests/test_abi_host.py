@@ -299,7 +299,7 @@ def test_fp8_layouts_and_errors_need_no_gpu():
         for tb in (0, 1):
             p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 256, 512, 384, ta, tb, 0.0, e4, e4)
             plans.add((p.kernel, p.block_m, p.block_n, p.block_k, p.grid, p.bounds_checked, p.loader))
-    assert plans == {(tg.TG_GEMM_TILED, 256, 256, 128, 2, 0, 1)}
+    assert plans == {(tg.TG_GEMM_TILED, 128, 128, 128, 8, 0, 1)}
     with pytest.raises(tg.TileError) as e:
         tg.tile_gemm_fp8(A_ADDR, B_ADDR, None, D_ADDR, 256, 256, 256, 0, 2, 0.0, e4, e4)
     assert e.value.status == tg.TG_E_ARG
@@ -324,8 +324,18 @@ def test_fp8_kernel_choice():
     p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 8192, 8192, 8192, 0, 1, 0.0, e4, e4)
     assert (p.kernel, p.block_m, p.block_n, p.block_k, p.threads, p.grid, p.bounds_checked,
             p.loader) == (tg.TG_GEMM_TILED, 256, 256, 128, 512, 1024, 0, 1)
+    # fewer than 256 blocks of 256x256: 128x128 blocks (3 x 5 of them here)
     p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, C_ADDR, D_ADDR, 272, 528, 384, 0, 1, 1.0, e5, e4)
-    assert (p.kernel, p.grid, p.bounds_checked) == (tg.TG_GEMM_TILED, 6, 1)
+    assert (p.kernel, p.block_m, p.grid, p.bounds_checked, p.loader) == (tg.TG_GEMM_TILED, 128, 15, 1, 1)
+    p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 2048, 2048, 8192, 0, 1, 0.0, e4, e4)
+    assert (p.block_m, p.wave_m, p.wave_n, p.threads, p.grid, p.bounds_checked, p.lds_bytes) == \
+        (128, 64, 32, 512, 256, 0, 65536)
+    p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 4096, 4096, 4096, 0, 1, 0.0, e4, e4)
+    assert (p.block_m, p.grid) == (256, 256)
+    # block-scaled fp8 keeps 256x256 blocks at every size (its scale ring is laid out for them)
+    p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, 1 << 36, 1 << 37, None, D_ADDR, 272, 528, 384, 0, 1, 0.0,
+                             e5, e4)
+    assert (p.block_m, p.grid, p.bounds_checked, p.lds_bytes) == (256, 6, 1, 4 * 256 * 128 + 3 * 8192)
     p = tg.tile_gemm_fp8_plan(None, None, C_ADDR, D_ADDR, 16, 16, 0, 0, 1, 1.0, e4, e5)
     assert p.kernel == tg.TG_GEMM_FILL
     p = tg.tile_gemm_fp8_plan(None, None, None, None, 0, 16, 128, 0, 1, 0.0, e4, e4)

@@ -42,8 +42,9 @@ def full_check(M, N, K, af, bf, beta, seeds, scale=1.0, c_is_d=False, ta=False, 
     return worst
 
 
-# Whole blocks and ragged edges (M, N not multiples of 256), with every shape of the stage
-# count K/128: one stage, even, odd >= 3.
+# Whole blocks and ragged edges, with every shape of the stage count K/128: one stage, even,
+# odd >= 3.  These problems have fewer than 256 blocks of 256x256, so they run on 128x128
+# blocks; test_ragged_256_sampled covers the 256-wide ones.
 SHAPES = [(16, 16, 128), (48, 32, 128), (256, 256, 128), (256, 256, 256), (256, 256, 384),
           (272, 528, 384), (512, 512, 1152), (784, 1040, 640), (1024, 1024, 2048),
           (1296, 1040, 1280)]
@@ -224,3 +225,44 @@ def test_unit_groups_of_eight():
         assert guards and np.array_equal(d[:, 0], want.astype(np.float32)), small
         assert np.all(d == d[:, :1])
     assert same_group.any() and (~same_group).any()
+
+
+# 256x256 blocks on ragged problems (at least 256 of them): M, N past a block edge, stage
+# counts one, odd and even, every orientation; sampled outputs plus every block edge.
+@pytest.mark.parametrize("M,N,K,ta,tb", [(4000, 4112, 384, False, True), (4112, 4000, 128, True, False),
+                                         (4016, 4096, 1024, True, True), (4096, 4016, 640, False, False)])
+def test_ragged_256_sampled(M, N, K, ta, tb):
+    say(f"gemm_fp8 ragged 256 {M}x{N}x{K} e5m2 x e4m3 transA={ta} transB={tb} beta=1 sampled")
+    a_bits, b_bits, c = synth.gemm_fp8_inputs(M, N, K, "e5m2", "e4m3", ta, tb, 1.0, (81, 82, 83))
+    A, B = upload_bits(a_bits), upload_bits(b_bits)
+    Cd = upload_f32(c)
+    D = torch.empty((M, N), device="cuda:0")
+    plan = tg.tile_gemm_fp8_plan(A, B, Cd, D, M, N, K, int(ta), int(tb), 1.0, FMT["e5m2"], FMT["e4m3"])
+    assert (plan.block_m, plan.bounds_checked, plan.loader) == (256, 1, 1)
+    tg.tile_gemm_fp8(A, B, Cd, D, M, N, K, int(ta), int(tb), 1.0, FMT["e5m2"], FMT["e4m3"])
+    torch.cuda.synchronize()
+    rows, cols = synth.sample_points(M, N, 84)
+    got = D[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    ref, bound = og.gemm_fp8_ref_at(a_bits, b_bits, c, M, N, K, ta, tb, 1.0, "e5m2", "e4m3", rows, cols)
+    ok, worst = og.check_fp8(got, ref, bound, a_bits, b_bits, M, N, K, ta, tb, "e5m2", "e4m3", rows, cols)
+    assert ok, worst
+    assert torch.isfinite(D).all()
+
+
+# 128x128 blocks at the size where they replace the 256-wide ones: 2048^2 outputs, long K.
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False)])
+def test_128_blocks_long_k_sampled(ta, tb):
+    M, N, K = 2048, 2064, 8192
+    say(f"gemm_fp8 128 blocks {M}x{N}x{K} e4m3 transA={ta} transB={tb} sampled")
+    a_bits, b_bits, c = synth.gemm_fp8_inputs(M, N, K, "e4m3", "e4m3", ta, tb, 0.0, (85, 86, 87))
+    A, B = upload_bits(a_bits), upload_bits(b_bits)
+    D = torch.empty((M, N), device="cuda:0")
+    plan = tg.tile_gemm_fp8_plan(A, B, None, D, M, N, K, int(ta), int(tb), 0.0, FMT["e4m3"], FMT["e4m3"])
+    assert (plan.block_m, plan.bounds_checked, plan.loader) == (128, 1, 1)
+    tg.tile_gemm_fp8(A, B, None, D, M, N, K, int(ta), int(tb), 0.0, FMT["e4m3"], FMT["e4m3"])
+    torch.cuda.synchronize()
+    rows, cols = synth.sample_points(M, N, 88, tile=(128, 128))
+    got = D[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    ref, bound = og.gemm_fp8_ref_at(a_bits, b_bits, c, M, N, K, ta, tb, 0.0, "e4m3", "e4m3", rows, cols)
+    ok, worst = og.check_fp8(got, ref, bound, a_bits, b_bits, M, N, K, ta, tb, "e4m3", "e4m3", rows, cols)
+    assert ok, worst

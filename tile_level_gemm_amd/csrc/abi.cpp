@@ -415,7 +415,7 @@ int tile_gemm_fp8_plan(const void* A, const void* B, const float* C, const float
   if (!out) return fail(TG_E_ARG, "out is NULL");
   int st = validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
   if (st) return st;
-  fill_plan(choose_gemm_fp8(M, N, K), out);
+  fill_plan(choose_gemm_fp8(M, N, K, false), out);
   return TG_OK;
 }
 
@@ -423,7 +423,7 @@ static int run_gemm_fp8(const void* A, const void* B, const uint8_t* SA, const u
                         const float* C, float* D, int64_t M, int64_t N, int64_t K, int transA,
                         int transB, float beta, int a_dtype, int b_dtype, bool scaled,
                         void* stream) {
-  const GemmConfig cfg = choose_gemm_fp8(M, N, K);
+  const GemmConfig cfg = choose_gemm_fp8(M, N, K, scaled);
   if (cfg.kernel == TG_GEMM_NONE) return TG_OK;
   if (cfg.kernel == TG_GEMM_FILL && beta == 1.0f && C == D) return TG_OK;
   GemmArgs g{};
@@ -436,12 +436,12 @@ static int run_gemm_fp8(const void* A, const void* B, const uint8_t* SA, const u
   g.K = (int32_t)K;
   g.use_c = beta == 1.0f;
   if (cfg.kernel == TG_GEMM_FILL) return launch_gemm(g, cfg, 0, 0, TG_BF16, stream);
-  g.tiles_m = (int32_t)((M + 255) / 256);
-  g.tiles_n = (int32_t)((N + 255) / 256);
+  g.tiles_m = (int32_t)((M + cfg.bm - 1) / cfg.bm);
+  g.tiles_n = (int32_t)((N + cfg.bn - 1) / cfg.bn);
   g.SA = SA;
   g.SB = SB;
   const hipError_t e = launch_gemm_fp8(g, cfg.grid, transA, transB, a_dtype, b_dtype,
-                                       cfg.bounds != 0, scaled, (hipStream_t)stream);
+                                       cfg.bounds != 0, scaled, cfg.bm, (hipStream_t)stream);
   if (e != hipSuccess)
     return fail(TG_E_HIP, std::string(scaled ? "tile_gemm_mx launch: " : "tile_gemm_fp8 launch: ") +
                               hipGetErrorString(e));
@@ -465,7 +465,7 @@ int tile_gemm_mx_plan(const void* A, const void* B, const uint8_t* SA, const uin
   if (!out) return fail(TG_E_ARG, "out is NULL");
   int st = validate_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
   if (st) return st;
-  fill_plan(choose_gemm_fp8(M, N, K), out);
+  fill_plan(choose_gemm_fp8(M, N, K, true), out);
   return TG_OK;
 }
 

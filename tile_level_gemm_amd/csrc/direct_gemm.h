@@ -128,11 +128,18 @@ __device__ __forceinline__ uint32_t sm(uint32_t k) {
   else return ((k & 3u) << 1) ^ ((k & 1u) << 3);
 }
 
-// M/N-major fp8 stage: 128 k-rows x 256 bytes (16 chunks); physical chunk = c ^ s8(k).  A
-// transposing read (ds_read_b64_tr_b8) of 32 lanes touches two adjacent chunks (an even one
-// and the next) in each of 8 consecutive k-rows; 2(k & 7) sends the 16 of them to 16 distinct
-// 16-byte bank slots.
-__device__ __forceinline__ uint32_t s8(uint32_t k) { return (k & 7u) << 1; }
+// M/N-major fp8 stage: 128 k-rows x ROWB bytes (256: 16 chunks, 128: 8 chunks); physical
+// chunk = c ^ s8(k).  A transposing read (ds_read_b64_tr_b8) of 32 lanes touches two adjacent
+// chunks (an even one and the next) in each of 8 consecutive k-rows; the swizzle sends the 16
+// of them to 16 distinct 16-byte bank slots of 256 bytes: 2(k & 7) with 256-byte rows; with
+// 128-byte rows a row pair fills 256 bytes, so the four even (odd) rows need four distinct
+// chunk pairs, 2((k >> 1) & 3).
+template <int ROWB>
+__device__ __forceinline__ uint32_t s8(uint32_t k) {
+  static_assert(ROWB == 256 || ROWB == 128, "fp8 M/N-major rows");
+  if constexpr (ROWB == 256) return (k & 7u) << 1;
+  else return ((k >> 1) & 3u) << 1;
+}
 
 // ---- per-lane offsets, computed once ---------------------------------------------------
 // Every address below is a per-lane offset computed before the K loop plus compile-time
@@ -171,15 +178,17 @@ __device__ __forceinline__ void mn_dma_offsets(int64_t ld, int wave, int lane, u
   }
 }
 
-// DMA for an M/N-major fp8 operand: instruction i writes block b = PER·wave + i = k-rows 4b ..
-// 4b+3; lane l fills slot l%16 of k-row 4b + l/16, logical chunk (l%16) ^ s8(k); s8 depends on
-// the lane and i's parity.
-template <int PER>
+// DMA for an M/N-major fp8 operand with ROWB-byte k-rows (CH = ROWB/16 chunks, RPB =
+// 1024/ROWB k-rows per 1 KiB block): instruction i writes block b = PER·wave + i = k-rows RPB·b
+// .. RPB·b + RPB-1; lane l fills slot l%CH of k-row RPB·b + l/CH, logical chunk (l%CH) ^ s8(k);
+// s8 depends on the lane and i's parity.
+template <int PER, int ROWB>
 __device__ __forceinline__ void mn8_dma_offsets(int64_t ld, int wave, int lane, uint32_t (&off)[2]) {
+  constexpr uint32_t CH = ROWB / 16, RPB = 1024 / ROWB;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const uint32_t k = (uint32_t)(4 * PER * wave + 4 * p + (lane >> 4));
-    const uint32_t c = ((uint32_t)lane & 15u) ^ s8(k);
+    const uint32_t k = RPB * (uint32_t)(PER * wave + p) + (uint32_t)lane / CH;
+    const uint32_t c = ((uint32_t)lane % CH) ^ s8<ROWB>(k);
     off[p] = k * (uint32_t)ld + c * 16u;   // bytes; < 128·M < 2^32
   }
 }
@@ -226,16 +235,16 @@ __device__ __forceinline__ void mn_frag_offsets(int mn_base, int lane, uint32_t 
 // receives its bytes 8u .. 8u+7 = k kr(u) + 16(g/2) .. +7 of column mn_base + 32t + l%32 —
 // the K order of the K-major fp8 fragment.  s8 depends on j only (s, u and g/2 add multiples
 // of 8 rows); the chunk of tile t is kept per t (2t carries into the swizzled bits), s and u
-// are immediates.
-template <int T>
+// are immediates (rows of ROWB bytes).
+template <int T, int ROWB>
 __device__ __forceinline__ void mn8_frag_offsets(int mn_base, int lane, uint32_t (&off)[4]) {
   const uint32_t g = (uint32_t)lane >> 4, j = (uint32_t)lane & 15u;
   const uint32_t krow = 16u * (g >> 1) + (j >> 1);
-  const uint32_t x = s8(krow);
+  const uint32_t x = s8<ROWB>(krow);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint32_t c = ((uint32_t)mn_base + 32u * (uint32_t)(t < T ? t : 0)) / 16u + (g & 1u);
-    off[t] = krow * 256u + ((c ^ x) << 4) + 8u * (j & 1u);
+    off[t] = krow * (uint32_t)ROWB + ((c ^ x) << 4) + 8u * (j & 1u);
   }
 }
 
@@ -245,8 +254,7 @@ template <bool MN, int T, int PER, int DT, int BS>
 struct Operand {
   using EL = Elem<DT>;
   using Frag = typename EL::Frag;
-  static constexpr int kRowB = BS * EL::kBytes;   // M/N-major 16-bit: bytes per k-row
-  static_assert(!(MN && EL::kFp8) || BS == 256, "fp8 M/N-major stages are 128 k x 256 bytes");
+  static constexpr int kRowB = BS * EL::kBytes;   // M/N-major: bytes per k-row
   uint32_t dma[2];   // byte offsets of the two DMA parities
   uint32_t kbyte[2]; // K-major: first byte within the K row of each parity's chunk
   uint32_t frag[4];  // byte offsets: per K-major read slot, or per M/N-major tile
@@ -257,8 +265,8 @@ struct Operand {
 
   __device__ __forceinline__ void init(int64_t ld, int base, int wave, int lane) {
     if constexpr (MN && EL::kFp8) {
-      mn8_dma_offsets<PER>(ld, wave, lane, dma);
-      mn8_frag_offsets<T>(base, lane, frag);
+      mn8_dma_offsets<PER, kRowB>(ld, wave, lane, dma);
+      mn8_frag_offsets<T, kRowB>(base, lane, frag);
     } else if constexpr (MN) {
       mn_dma_offsets<PER, kRowB>(ld, wave, lane, dma);
       mn_frag_offsets<T, kRowB>(base, lane, frag);
@@ -286,10 +294,8 @@ struct Operand {
     for (int i = 0; i < PER; ++i) {
       uint32_t v = dma[i & 1];
       if constexpr (TAIL && !MN) v = kbyte[i & 1] < lim ? v : 0x80000000u;
-      // K-major: +8 rows per instruction pair; M/N-major: +1024/kRowB k-rows (16-bit) or +4
-      // (fp8)
-      const uint32_t step = MN ? (EL::kFp8 ? (uint32_t)(4 * (i & ~1)) * (uint32_t)ld
-                                           : (uint32_t)((1024 / kRowB) * (i & ~1)) * (uint32_t)ld * 2u)
+      // K-major: +8 rows per instruction pair; M/N-major: +1024/kRowB k-rows
+      const uint32_t step = MN ? (uint32_t)((1024 / kRowB) * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes
                                : (uint32_t)(8 * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (wave * PER + i) * 1024),
                                                16, v, stage_off + step, 0, 0);
@@ -332,7 +338,7 @@ struct Operand {
       u32x8 out;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint8_t* p = stage + frag[t] + (64 * s + 32 * (u >> 1) + 8 * (u & 1)) * 256;
+        const uint8_t* p = stage + frag[t] + (64 * s + 32 * (u >> 1) + 8 * (u & 1)) * kRowB;
         const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
         out[2 * u] = (uint32_t)v[0];
         out[2 * u + 1] = (uint32_t)v[1];
@@ -395,7 +401,7 @@ __device__ __forceinline__ void interleave_inplace() {
 // last stage may hold fewer than 64 K, stages = ceil(K / 64).
 enum KStages { kEven = 0, kOdd = 1, kSingle = 2, kTail = 4 };
 
-// WGM x WGN waves on a BS x BS block (256, or 128 for 16-bit operands); wave tile
+// WGM x WGN waves on a BS x BS block (256, or 128 without block scales); wave tile
 // (BS/WGM) x (BS/WGN).  BOUNDS: M or N is not a whole number of blocks; operand rows past the end read as zero (buffer range check) and the epilogue skips
 // rows and columns past M and N.  An operand row past M or N only feeds outputs that are
 // never stored, so the data there need not be zero, only never fetched from outside the
@@ -413,7 +419,7 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   constexpr bool TAIL = (KS & kTail) != 0;
   static_assert(PER % 2 == 0 && TM >= 1 && TN >= 1 && TM <= 4 && TN <= 4, "wave grid");
   static_assert(!TAIL || !EL::kFp8, "a partial last stage is served for 16-bit operands");
-  static_assert(BS == 256 || (BS == 128 && !EL::kFp8), "128-wide blocks are served for 16-bit operands");
+  static_assert(BS == 256 || (BS == 128 && !EL::kScaled), "block-scaled fp8 takes 256-wide blocks");
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[BS * kRowBytes];
@@ -738,8 +744,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   direct_body<A_MN, B_MN, DT, WGM, WGN, BOUNDS, KS, 256>(g);
 }
 
-// 128x128 blocks (16-bit operands): 64 KiB of LDS stages, so two workgroups share a CU; for
-// problems with too few 256x256 blocks to fill the chip.
+// 128x128 blocks (16-bit and unscaled fp8 operands): 64 KiB of LDS stages, so two workgroups
+// share a CU; for problems with too few 256x256 blocks to fill the chip.
 template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct128(GemmArgs g) {
   direct_body<A_MN, B_MN, DT, WGM, WGN, BOUNDS, KS, 128>(g);

@@ -9,15 +9,26 @@ namespace tg {
 
 // A_MN: A stored [K][M]; B_MN: B stored [K][N].  af / bf: the MFMA format codes (0 = e4m3,
 // 1 = e5m2).  The stage-count shape (K / 128 even, odd, or one) is fixed at compile time.
-// SCALED: block-scaled fp8 (g.SA, g.SB hold the E8M0 scales).
+// SCALED: block-scaled fp8 (g.SA, g.SB hold the E8M0 scales; 256-wide blocks only).  bs: block
+// size, 256 or 128 (8 waves in a 2 x 4 grid either way).
 template <bool A_MN, bool B_MN, bool SCALED = false>
-hipError_t launch_fp8_layout(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds,
+hipError_t launch_fp8_layout(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
                              hipStream_t s) {
   auto go = [&](auto AF, auto BF, auto BOUNDS, auto KS) {
     constexpr int dt = SCALED ? mx_code(decltype(AF)::value, decltype(BF)::value)
                               : fp8_code(decltype(AF)::value, decltype(BF)::value);
-    hipLaunchKernelGGL((gemm_direct<A_MN, B_MN, dt, 2, 4, decltype(BOUNDS)::value, decltype(KS)::value>),
-                       dim3((unsigned)grid), dim3(512), 0, s, g);
+    constexpr bool b = decltype(BOUNDS)::value;
+    constexpr int ks = decltype(KS)::value;
+    if constexpr (!SCALED) {
+      if (bs == 128) {
+        hipLaunchKernelGGL((gemm_direct128<A_MN, B_MN, dt, 2, 4, b, ks>), dim3((unsigned)grid),
+                           dim3(512), 0, s, g);
+        return hipGetLastError();
+      }
+    }
+    if (bs != 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_direct<A_MN, B_MN, dt, 2, 4, b, ks>), dim3((unsigned)grid), dim3(512), 0,
+                       s, g);
     return hipGetLastError();
   };
   using Z = std::integral_constant<int, 0>;
@@ -37,13 +48,21 @@ hipError_t launch_fp8_layout(const GemmArgs& g, int64_t grid, int af, int bf, bo
   return bounds ? fmt(std::true_type{}) : fmt(std::false_type{});
 }
 
-hipError_t launch_fp8_kk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
-hipError_t launch_fp8_km(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
-hipError_t launch_fp8_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
-hipError_t launch_fp8_mm(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
-hipError_t launch_mx_kk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
-hipError_t launch_mx_km(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
-hipError_t launch_mx_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
-hipError_t launch_mx_mm(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, hipStream_t s);
+hipError_t launch_fp8_kk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
+hipError_t launch_fp8_km(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
+hipError_t launch_fp8_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
+hipError_t launch_fp8_mm(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
+hipError_t launch_mx_kk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
+hipError_t launch_mx_km(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
+hipError_t launch_mx_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
+hipError_t launch_mx_mm(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                         hipStream_t s);
 
 }  // namespace tg

@@ -3,9 +3,9 @@
 
 namespace tg {
 
-hipError_t launch_fp8_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds,
+hipError_t launch_fp8_mk(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
                          hipStream_t s) {
-  return launch_fp8_layout<true, false>(g, grid, af, bf, bounds, s);
+  return launch_fp8_layout<true, false>(g, grid, af, bf, bounds, bs, s);
 }
 
 }  // namespace tg

@@ -100,12 +100,13 @@ int launch_gemm(const GemmArgs& g, const GemmConfig& cfg, int trans_a, int trans
 
 bool direct_gemm_fits(int64_t M, int64_t N, int64_t K);
 
-// fp8 GEMM (any operand orientation): 256x256 blocks, 512 threads, grid =
-// ceil(M/256)·ceil(N/256); bounds = M or N not a multiple of 256.
-GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K);
-// scaled: block-scaled fp8 (E8M0 scales in g.SA, g.SB).
+// fp8 GEMM (any operand orientation): 256x256 blocks (128x128 for unscaled fp8 when there are
+// fewer than 256 of the larger), 512 threads, grid = ceil(M/bm)·ceil(N/bn); bounds = M or N
+// not a multiple of the block.  scaled: block-scaled fp8.
+GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K, bool scaled);
+// scaled: block-scaled fp8 (E8M0 scales in g.SA, g.SB).  bs: block size (cfg.bm).
 hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int a_dtype,
-                           int b_dtype, bool bounds, bool scaled, hipStream_t s);
+                           int b_dtype, bool bounds, bool scaled, int bs, hipStream_t s);
 // 16-bit direct-load GEMM on bs x bs blocks (256 or 128).
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
                               int bs, hipStream_t s);
