@@ -357,8 +357,8 @@ hipError_t launch_dt(const GemmArgs& g, const GemmConfig& c, hipStream_t s) {
     return hipGetLastError();
   }
   if (c.bm == 256) return launch_tiled<256, 256, 128, 128, TA, TB, DT>(g, c, s);
-  if (c.bm == 128) return launch_tiled<128, 128, 64, 64, TA, TB, DT>(g, c, s);
-  return launch_tiled<64, 64, 32, 32, TA, TB, DT>(g, c, s);
+  if (c.bm == 64) return launch_tiled<64, 64, 32, 32, TA, TB, DT>(g, c, s);
+  return hipErrorInvalidValue;   // 128-wide blocks run on the direct-load kernel only
 }
 
 template <int DT>

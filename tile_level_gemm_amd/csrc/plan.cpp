@@ -181,13 +181,15 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   }
   c.kernel = TG_GEMM_TILED;
   c.bk = 64;
-  // 128-wide blocks only while they fit one round of two per CU: with more, a CU runs three
-  // or more of them one after the other, slower than the one 256-wide block it would get
-  // (fp8 3072^3: 41.7 against 35.6 us)
-  if (blocks(256, 256) >= 256 || blocks(128, 128) > 512) {
+  // 128-wide blocks (direct-load kernel only) while they fit one round of two per CU: with
+  // more, a CU runs three or more of them one after the other, slower than the one 256-wide
+  // block it would get (fp8 3072^3: 41.7 against 35.6 us).  Operands of 2 GiB or more take
+  // the VGPR-staged kernel on 256- or 64-wide tiles.
+  const bool fits = direct_gemm_fits(M, N, K);
+  if (blocks(256, 256) >= 256 || (fits && blocks(128, 128) > 512)) {
     c.bm = c.bn = 256;
     c.wm = c.wn = 128;
-  } else if (blocks(128, 128) >= 128) {
+  } else if (fits && blocks(128, 128) >= 128) {
     c.bm = c.bn = 128;
     c.wm = c.wn = 64;
   } else {
@@ -199,7 +201,7 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   c.lds_bytes = 2 * (c.bm + c.bn) * 128;
   c.grid = blocks(c.bm, c.bn);
   // gemm_direct (256x256) and gemm_direct128 (128x128): 8 waves, a 2 x 4 wave grid
-  c.direct = c.bm >= 128 && direct_gemm_fits(M, N, K);
+  c.direct = c.bm >= 128 && fits;
   if (c.direct) {
     c.wm = c.bm / 2;
     c.wn = c.bn / 4;
