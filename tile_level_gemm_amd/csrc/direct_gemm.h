@@ -1,10 +1,10 @@
 // Large-tile GEMM on gfx950 with direct global -> LDS operand loads (kernel template).
 //
 // Same contract as gemm_tiled ([SYNC-GEMM] "TVM TIRx 同步 GEMM 深度解析…": D = A·B (+C),
-// fp32 accumulation in place over K, 二 / 四 step 3), for 256x256 blocks.  The template
-// serves the 16-bit operands of the synchronous GEMM and the fp8 operands of the
+// fp32 accumulation in place over K, 二 / 四 step 3), for 256x256 or 128x128 blocks.  The
+// template serves the 16-bit operands of the synchronous GEMM and the fp8 operands of the
 // asynchronous GEMM's precision family (七: A and B staged in shared memory, fp8 among the
-// operand formats).  What the kernel does:
+// operand formats), with or without block scales.  What the kernel does:
 //
 //  * global -> LDS with buffer_load_dwordx4 ... lds: each instruction moves 64 lanes x 16 bytes
 //    and lane i's bytes land at LDS base + 16·i, so no VGPR staging and no ds_write.  The
@@ -18,7 +18,8 @@
 //    (chunk XOR row bits) and are read as fragments with ds_read_b128: one per 16-bit
 //    fragment, two per fp8 fragment (32 bytes of K per lane).
 //  * M/N-contiguous 16-bit operands (A with transA, B without transB) keep the global
-//    orientation, [64 k][256 mn] stages of 512-byte rows, and are read with
+//    orientation, [64 k][256 mn] stages of 512-byte rows (256 bytes on 128-wide blocks), and
+//    are read with
 //    ds_read_b64_tr_b16: within each 16-lane group, lane j receives element j%4 of the 8-byte
 //    reads of lanes 4q + j/4 (q = 0..3), so if lane i reads 4 consecutive mn at k-row
 //    k0 + i/4 and column block i%4, lane j receives k0..k0+3 at mn0 + j — four K-consecutive
@@ -33,7 +34,8 @@
 //    not a whole number of stages would read the next row's K instead: there the lanes whose
 //    chunk lies past K get a VGPR offset of 2^31, out of range whatever else is added.
 //
-// Internal header: included by gemm_direct.hip (16-bit instantiations) and gemm_fp8.hip.
+// Internal header: included through gemm_direct_launch.h (16-bit instantiations) and
+// gemm_fp8_launch.h (fp8 and block-scaled fp8).
 #pragma once
 
 #include <hip/hip_runtime.h>
