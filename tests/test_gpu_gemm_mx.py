@@ -128,3 +128,47 @@ def test_large_sampled():
     ok, worst = og.check_fp8(got, ref, bound, a, b, M, N, K, False, True, "e4m3", "e4m3", rows, cols,
                              sa_bits=sa, sb_bits=sb)
     assert ok, worst
+
+
+# 256x256 blocks on ragged problems (the shape tests above run on 128x128 blocks): M, N past a
+# block edge, stage counts one, odd (with a partial scale group) and even, every orientation.
+@pytest.mark.parametrize("M,N,K,ta,tb", [(4000, 4112, 384, False, True), (4112, 4000, 128, True, False),
+                                         (4016, 4096, 1408, True, True), (4096, 4016, 1024, False, False)])
+def test_ragged_256_sampled(M, N, K, ta, tb):
+    say(f"gemm_mx ragged 256 {M}x{N}x{K} e4m3 x e5m2 transA={ta} transB={tb} beta=1 sampled")
+    a, b, sa, sb, c = mx_case(M, N, K, "e4m3", "e5m2", ta, tb, 1.0, 91)
+    A, B, SA, SB = upload_bits(a), upload_bits(b), upload_bits(sa), upload_bits(sb)
+    Cd = upload_f32(c)
+    D = torch.empty((M, N), device="cuda:0")
+    plan = tg.tile_gemm_mx_plan(A, B, SA, SB, Cd, D, M, N, K, int(ta), int(tb), 1.0, FMT["e4m3"],
+                                FMT["e5m2"])
+    assert (plan.block_m, plan.bounds_checked) == (256, 1)
+    tg.tile_gemm_mx(A, B, SA, SB, Cd, D, M, N, K, int(ta), int(tb), 1.0, FMT["e4m3"], FMT["e5m2"])
+    torch.cuda.synchronize()
+    rows, cols = synth.sample_points(M, N, 92)
+    got = D[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    ref, bound = og.gemm_mx_ref_at(a, b, sa, sb, c, M, N, K, ta, tb, 1.0, "e4m3", "e5m2", rows, cols)
+    ok, worst = og.check_fp8(got, ref, bound, a, b, M, N, K, ta, tb, "e4m3", "e5m2", rows, cols,
+                             sa_bits=sa, sb_bits=sb)
+    assert ok, worst
+    assert torch.isfinite(D).all()
+
+
+def test_128_blocks_long_k_sampled():
+    # 2048 x 2064 outputs on 128x128 blocks, 64 stages (16 turns of the scale ring's groups)
+    M, N, K = 2048, 2064, 8192
+    say(f"gemm_mx 128 blocks {M}x{N}x{K} e4m3 sampled")
+    a, b, sa, sb, _ = mx_case(M, N, K, "e4m3", "e4m3", False, True, 0.0, 93)
+    A, B, SA, SB = upload_bits(a), upload_bits(b), upload_bits(sa), upload_bits(sb)
+    D = torch.empty((M, N), device="cuda:0")
+    plan = tg.tile_gemm_mx_plan(A, B, SA, SB, None, D, M, N, K, 0, 1, 0.0, FMT["e4m3"], FMT["e4m3"])
+    assert (plan.block_m, plan.bounds_checked) == (128, 1)
+    tg.tile_gemm_mx(A, B, SA, SB, None, D, M, N, K, 0, 1, 0.0, FMT["e4m3"], FMT["e4m3"])
+    torch.cuda.synchronize()
+    rows, cols = synth.sample_points(M, N, 94, tile=(128, 128))
+    got = D[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    ref, bound = og.gemm_mx_ref_at(a, b, sa, sb, None, M, N, K, False, True, 0.0, "e4m3", "e4m3",
+                                   rows, cols)
+    ok, worst = og.check_fp8(got, ref, bound, a, b, M, N, K, False, True, "e4m3", "e4m3", rows, cols,
+                             sa_bits=sa, sb_bits=sb)
+    assert ok, worst

@@ -63,7 +63,6 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 constexpr int BM = 256, BN = 256;
 constexpr int kRowBytes = 128;   // bytes of K per operand row and stage
 constexpr int kGroupM = 8;       // tile-rows per scheduling group (measured: 8 beats 2, 4, 16)
-constexpr uint32_t kQGroup = 8192;   // block-scaled fp8: LDS bytes of one group of 4 stages' scales
 
 // Format codes of the template's DT parameter: TG_F16 / TG_BF16, an fp8 pair kF8 + 2·a + b,
 // or a block-scaled fp8 pair kMX + 2·a + b, with a, b the MFMA's operand format codes
@@ -403,7 +402,7 @@ __device__ __forceinline__ void interleave_inplace() {
 // last stage may hold fewer than 64 K, stages = ceil(K / 64).
 enum KStages { kEven = 0, kOdd = 1, kSingle = 2, kTail = 4 };
 
-// WGM x WGN waves on a BS x BS block (256, or 128 without block scales); wave tile
+// WGM x WGN waves on a BS x BS block (256 or 128); wave tile
 // (BS/WGM) x (BS/WGN).  BOUNDS: M or N is not a whole number of blocks; operand rows past the end read as zero (buffer range check) and the epilogue skips
 // rows and columns past M and N.  An operand row past M or N only feeds outputs that are
 // never stored, so the data there need not be zero, only never fetched from outside the
@@ -421,14 +420,17 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   constexpr bool TAIL = (KS & kTail) != 0;
   static_assert(PER % 2 == 0 && TM >= 1 && TN >= 1 && TM <= 4 && TN <= 4, "wave grid");
   static_assert(!TAIL || !EL::kFp8, "a partial last stage is served for 16-bit operands");
-  static_assert(BS == 256 || (BS == 128 && !EL::kScaled), "block-scaled fp8 takes 256-wide blocks");
+  static_assert(BS == 256 || BS == 128, "block size");
+  // block-scaled fp8: LDS bytes of one group of four stages' scales (BS rows x 16 bytes per
+  // operand), B's offset in it, and rows per operand in a quarter of a group
+  constexpr uint32_t QG = 32u * BS, QH = 16u * BS, QR = BS / 4;
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sb1[BS * kRowBytes];
-  // block scales (scaled fp8 only): a ring of three groups of four stages, each A's 256 rows
+  // block scales (scaled fp8 only): a ring of three groups of four stages, each A's BS rows
   // x 16 bytes, then B's
-  __shared__ __attribute__((aligned(1024))) uint8_t qg[EL::kScaled ? 3 * kQGroup : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t qg[EL::kScaled ? 3 * QG : 1];
 
   // tile scheduler: XCD-contiguous ranges, grouped tile-rows (as gemm_tiled)
   const int nb = (int)gridDim.x;
@@ -492,12 +494,14 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
 
   // Block scales (scaled fp8): K/32 bytes per row, 4 per 128-K stage.  They travel in groups
   // of four stages, 16 bytes per row, into a ring of three LDS group buffers ([row][16 bytes],
-  // A's 256 rows then B's).  Stage kt loads quarter kt % 4 of group kt/4 + 2: rows 64q ..
-  // 64q + 63 of A (waves 0-3, 16 rows each) and of B (waves 4-7), four lanes per row with 4
-  // bytes each, so the lanes of a row share one cache line — 128 lines per stage, where one
-  // 4-byte load per row and stage took 512.  Group G is complete four stages before its
-  // first read, and its buffer last held group G - 3, read out two stages before.  Groups 0
-  // and 1 load before the K loop.  Rows past M or N read as zero.
+  // A's BS rows then B's).  Stage kt loads quarter kt % 4 of group kt/4 + 2: rows QR·q ..
+  // QR·q + QR-1 of A (waves 0-3, 16 rows each) and of B (waves 4-7), four lanes per row with
+  // 4 bytes each, so the lanes of a row share one cache line — 128 lines per stage on 256-wide
+  // blocks, where one 4-byte load per row and stage took 512.  On 128-wide blocks a quarter
+  // is 32 rows, and waves 2-3 (6-7) repeat the transfers of waves 0-1 (4-5): the same bytes
+  // to the same place, which keeps the loop free of branches.  Group G is complete four
+  // stages before its first read, and its buffer last held group G - 3, read out two stages
+  // before.  Groups 0 and 1 load before the K loop.  Rows past M or N read as zero.
   __amdgpu_buffer_rsrc_t qrsrc;
   uint32_t qvoff = 0, qlds = 0, qkb = 0;
   if constexpr (EL::kScaled) {
@@ -506,27 +510,28 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
     const int row0 = is_a ? m0 : n0, rows = is_a ? g.M : g.N;
     const uint8_t* qbase = (is_a ? g.SA : g.SB) + (int64_t)row0 * kb;
     qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, (rows - row0) * kb, 0x00020000);
-    qvoff = (uint32_t)(16 * (wave & 3) + (lane >> 2)) * (uint32_t)kb + 4u * (uint32_t)(lane & 3);
-    qlds = (is_a ? 0u : kQGroup / 2) + 256u * (uint32_t)(wave & 3);
+    const uint32_t wq = (uint32_t)(wave & 3) % (QR / 16);   // this wave's 16 rows of a quarter
+    qvoff = (16u * wq + (uint32_t)(lane >> 2)) * (uint32_t)kb + 4u * (uint32_t)(lane & 3);
+    qlds = (is_a ? 0u : QH) + 256u * wq;
     qkb = (uint32_t)kb;
   }
   // quarter q of group G (G % 3 is the ring slot)
   auto qload_part = [&](uint32_t G, uint32_t q) {
     if constexpr (EL::kScaled)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(qg + (G % 3u) * kQGroup + qlds + 1024u * q),
-                                               4, qvoff, 64u * q * qkb + 16u * G, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(qg + (G % 3u) * QG + qlds + 16u * QR * q),
+                                               4, qvoff, QR * q * qkb + 16u * G, 0, 0);
   };
   auto qroll = [&](int kt) { qload_part((uint32_t)(kt >> 2) + 2u, (uint32_t)(kt & 3)); };
   // stage kt's 4 scale bytes of row 0 in the ring
   auto qstage = [&](int kt) -> const uint8_t* {
-    return qg + ((uint32_t)(kt >> 2) % 3u) * kQGroup + 4u * (uint32_t)(kt & 3);
+    return qg + ((uint32_t)(kt >> 2) % 3u) * QG + 4u * (uint32_t)(kt & 3);
   };
   // This lane's scales of one stage for A tile i / B tile j, shifted so that byte 2s holds
   // the block of K step s this lane supplies (K half lane / 32).  One per-lane LDS offset per
   // operand; tiles are immediates.
   uint32_t qa[TM], qb[TN], qbn[TN];
   const uint32_t qsh = 8u * (uint32_t)(lane >> 5);
-  const uint32_t qoa = 16u * (uint32_t)(wm + (lane & 31)), qob = kQGroup / 2 + 16u * (uint32_t)(wn + (lane & 31));
+  const uint32_t qoa = 16u * (uint32_t)(wm + (lane & 31)), qob = QH + 16u * (uint32_t)(wn + (lane & 31));
   auto qread_a = [&](const uint8_t* q, int i) -> uint32_t {
     return *(const uint32_t*)(q + qoa + 512 * i) >> qsh;
   };
@@ -746,8 +751,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct(GemmArgs g) {
   direct_body<A_MN, B_MN, DT, WGM, WGN, BOUNDS, KS, 256>(g);
 }
 
-// 128x128 blocks (16-bit and unscaled fp8 operands): 64 KiB of LDS stages, so two workgroups
-// share a CU; for problems with too few 256x256 blocks to fill the chip.
+// 128x128 blocks: 64 KiB of LDS stages (76 KiB with block scales), so two workgroups share a
+// CU; for problems with too few 256x256 blocks to fill the chip.
 template <bool A_MN, bool B_MN, int DT, int WGM, int WGN, bool BOUNDS, int KS>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_direct128(GemmArgs g) {
   direct_body<A_MN, B_MN, DT, WGM, WGN, BOUNDS, KS, 128>(g);

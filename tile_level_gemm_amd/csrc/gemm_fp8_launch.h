@@ -9,8 +9,8 @@ namespace tg {
 
 // A_MN: A stored [K][M]; B_MN: B stored [K][N].  af / bf: the MFMA format codes (0 = e4m3,
 // 1 = e5m2).  The stage-count shape (K / 128 even, odd, or one) is fixed at compile time.
-// SCALED: block-scaled fp8 (g.SA, g.SB hold the E8M0 scales; 256-wide blocks only).  bs: block
-// size, 256 or 128 (8 waves in a 2 x 4 grid either way).
+// SCALED: block-scaled fp8 (g.SA, g.SB hold the E8M0 scales).  bs: block size, 256 or 128 (8
+// waves in a 2 x 4 grid either way).
 template <bool A_MN, bool B_MN, bool SCALED = false>
 hipError_t launch_fp8_layout(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
                              hipStream_t s) {
@@ -19,12 +19,10 @@ hipError_t launch_fp8_layout(const GemmArgs& g, int64_t grid, int af, int bf, bo
                               : fp8_code(decltype(AF)::value, decltype(BF)::value);
     constexpr bool b = decltype(BOUNDS)::value;
     constexpr int ks = decltype(KS)::value;
-    if constexpr (!SCALED) {
-      if (bs == 128) {
-        hipLaunchKernelGGL((gemm_direct128<A_MN, B_MN, dt, 2, 4, b, ks>), dim3((unsigned)grid),
-                           dim3(512), 0, s, g);
-        return hipGetLastError();
-      }
+    if (bs == 128) {
+      hipLaunchKernelGGL((gemm_direct128<A_MN, B_MN, dt, 2, 4, b, ks>), dim3((unsigned)grid),
+                         dim3(512), 0, s, g);
+      return hipGetLastError();
     }
     if (bs != 256) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_direct<A_MN, B_MN, dt, 2, 4, b, ks>), dim3((unsigned)grid), dim3(512), 0,

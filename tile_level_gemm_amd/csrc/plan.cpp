@@ -222,10 +222,10 @@ GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K, bool scaled) {
     c.grid = std::min<int64_t>((M * N + 1023) / 1024, 65536);
     return c;
   }
-  // 256x256 blocks; 128x128 (unscaled only) when there are fewer than 256 of the larger and
-  // at most 512 of the smaller, as for the 16-bit kernel
+  // 256x256 blocks; 128x128 when there are fewer than 256 of the larger and at most 512 of the
+  // smaller, as for the 16-bit kernel
   auto blocks = [&](int64_t b) { return ((M + b - 1) / b) * ((N + b - 1) / b); };
-  const int bs = (!scaled && blocks(256) < 256 && blocks(128) <= 512) ? 128 : 256;
+  const int bs = (blocks(256) < 256 && blocks(128) <= 512) ? 128 : 256;
   c.kernel = TG_GEMM_TILED;
   c.bm = c.bn = bs;
   c.bk = 128;
@@ -233,7 +233,7 @@ GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K, bool scaled) {
   c.wn = bs / 4;
   c.threads = 512;
   c.bounds = (M % bs) != 0 || (N % bs) != 0;
-  c.lds_bytes = 4 * bs * 128 + (scaled ? 3 * 8192 : 0);
+  c.lds_bytes = 4 * bs * 128 + (scaled ? 3 * 32 * bs : 0);
   c.grid = blocks(bs);
   c.direct = 1;
   return c;

@@ -100,9 +100,9 @@ int launch_gemm(const GemmArgs& g, const GemmConfig& cfg, int trans_a, int trans
 
 bool direct_gemm_fits(int64_t M, int64_t N, int64_t K);
 
-// fp8 GEMM (any operand orientation): 256x256 blocks (128x128 for unscaled fp8 when there are
-// fewer than 256 of the larger), 512 threads, grid = ceil(M/bm)·ceil(N/bn); bounds = M or N
-// not a multiple of the block.  scaled: block-scaled fp8.
+// fp8 GEMM (any operand orientation): 256x256 blocks (128x128 when there are fewer than 256 of
+// the larger and at most 512 of the smaller), 512 threads, grid = ceil(M/bm)·ceil(N/bn);
+// bounds = M or N not a multiple of the block.  scaled: block-scaled fp8.
 GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K, bool scaled);
 // scaled: block-scaled fp8 (E8M0 scales in g.SA, g.SB).  bs: block size (cfg.bm).
 hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int a_dtype,
