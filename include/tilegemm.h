@@ -18,7 +18,9 @@
  *     dereference them; they need no GPU.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *     stream).  Launches are asynchronous on that stream; the library creates
- *     no stream and never synchronises.
+ *     no stream and never synchronises.  A call issues kernel launches only (no
+ *     allocation, memset or copy), so it may be recorded into a HIP graph; each
+ *     replay reads the buffers' contents at that time.
  *   - Errors: every argument is validated before anything is launched, so a
  *     rejected call writes nothing.  The return value is a tg_status; the
  *     reason of the last failure on the calling thread is tile_last_error().
