@@ -332,13 +332,14 @@ def test_fp8_kernel_choice():
         (128, 64, 32, 512, 256, 0, 65536)
     p = tg.tile_gemm_fp8_plan(A_ADDR, B_ADDR, None, D_ADDR, 4096, 4096, 4096, 0, 1, 0.0, e4, e4)
     assert (p.block_m, p.grid) == (256, 256)
-    # block-scaled fp8: the same block choice; its scale ring adds three groups of BS x 32 bytes
+    # block-scaled fp8: the same block choice; its scale ring adds three groups of 2 x BS/16
+    # blocks of 260 bytes
     p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, 1 << 36, 1 << 37, None, D_ADDR, 272, 528, 384, 0, 1, 0.0,
                              e5, e4)
-    assert (p.block_m, p.grid, p.bounds_checked, p.lds_bytes) == (128, 15, 1, 4 * 128 * 128 + 3 * 32 * 128)
+    assert (p.block_m, p.grid, p.bounds_checked, p.lds_bytes) == (128, 15, 1, 4 * 128 * 128 + 3 * 2 * 260 * 8)
     p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, 1 << 36, 1 << 37, None, D_ADDR, 8192, 8192, 8192, 0, 1, 0.0,
                              e4, e4)
-    assert (p.block_m, p.grid, p.bounds_checked, p.lds_bytes) == (256, 1024, 0, 4 * 256 * 128 + 3 * 32 * 256)
+    assert (p.block_m, p.grid, p.bounds_checked, p.lds_bytes) == (256, 1024, 0, 4 * 256 * 128 + 3 * 2 * 260 * 16)
     p = tg.tile_gemm_fp8_plan(None, None, C_ADDR, D_ADDR, 16, 16, 0, 0, 1, 1.0, e4, e5)
     assert p.kernel == tg.TG_GEMM_FILL
     p = tg.tile_gemm_fp8_plan(None, None, None, None, 0, 16, 128, 0, 1, 0.0, e4, e4)

@@ -421,9 +421,11 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   static_assert(PER % 2 == 0 && TM >= 1 && TN >= 1 && TM <= 4 && TN <= 4, "wave grid");
   static_assert(!TAIL || !EL::kFp8, "a partial last stage is served for 16-bit operands");
   static_assert(BS == 256 || BS == 128, "block size");
-  // block-scaled fp8: LDS bytes of one group of four stages' scales (BS rows x 16 bytes per
-  // operand), B's offset in it, and rows per operand in a quarter of a group
-  constexpr uint32_t QG = 32u * BS, QH = 16u * BS, QR = BS / 4;
+  // block-scaled fp8: a group of four stages' scales holds BS rows x 16 bytes per operand in
+  // blocks of 16 rows, each block 4 bytes longer than its 256 bytes (QB), so that rows r and
+  // r + 16 start in different banks; QH: B's offset in a group; QG: a group's bytes; QR: rows
+  // per operand in a quarter of a group
+  constexpr uint32_t QB = 260u, QH = QB * (BS / 16), QG = 2u * QH, QR = BS / 4;
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[BS * kRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[BS * kRowBytes];
@@ -512,13 +514,13 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
     qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, (rows - row0) * kb, 0x00020000);
     const uint32_t wq = (uint32_t)(wave & 3) % (QR / 16);   // this wave's 16 rows of a quarter
     qvoff = (16u * wq + (uint32_t)(lane >> 2)) * (uint32_t)kb + 4u * (uint32_t)(lane & 3);
-    qlds = (is_a ? 0u : QH) + 256u * wq;
+    qlds = (is_a ? 0u : QH) + QB * wq;
     qkb = (uint32_t)kb;
   }
   // quarter q of group G (G % 3 is the ring slot)
   auto qload_part = [&](uint32_t G, uint32_t q) {
     if constexpr (EL::kScaled)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(qg + (G % 3u) * QG + qlds + 16u * QR * q),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(qg + (G % 3u) * QG + qlds + QB * (QR / 16) * q),
                                                4, qvoff, QR * q * qkb + 16u * G, 0, 0);
   };
   auto qroll = [&](int kt) { qload_part((uint32_t)(kt >> 2) + 2u, (uint32_t)(kt & 3)); };
@@ -531,12 +533,15 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   // operand; tiles are immediates.
   uint32_t qa[TM], qb[TN], qbn[TN];
   const uint32_t qsh = 8u * (uint32_t)(lane >> 5);
-  const uint32_t qoa = 16u * (uint32_t)(wm + (lane & 31)), qob = QH + 16u * (uint32_t)(wn + (lane & 31));
+  // row r of an operand's group: block r / 16, 16 bytes per row within it; tiles are 32 rows
+  // (two blocks) apart
+  auto qrow = [&](uint32_t r) -> uint32_t { return QB * (r >> 4) + 16u * (r & 15u); };
+  const uint32_t qoa = qrow((uint32_t)(wm + (lane & 31))), qob = QH + qrow((uint32_t)(wn + (lane & 31)));
   auto qread_a = [&](const uint8_t* q, int i) -> uint32_t {
-    return *(const uint32_t*)(q + qoa + 512 * i) >> qsh;
+    return *(const uint32_t*)(q + qoa + 2 * QB * i) >> qsh;
   };
   auto qread_b = [&](const uint8_t* q, int j) -> uint32_t {
-    return *(const uint32_t*)(q + qob + 512 * j) >> qsh;
+    return *(const uint32_t*)(q + qob + 2 * QB * j) >> qsh;
   };
   auto qread = [&](const uint8_t* q) {
     if constexpr (EL::kScaled) {

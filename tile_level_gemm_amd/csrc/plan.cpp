@@ -233,7 +233,7 @@ GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K, bool scaled) {
   c.wn = bs / 4;
   c.threads = 512;
   c.bounds = (M % bs) != 0 || (N % bs) != 0;
-  c.lds_bytes = 4 * bs * 128 + (scaled ? 3 * 32 * bs : 0);
+  c.lds_bytes = 4 * bs * 128 + (scaled ? 3 * 2 * 260 * (bs / 16) : 0);   // + the scale ring
   c.grid = blocks(bs);
   c.direct = 1;
   return c;
