@@ -12,7 +12,10 @@ after the steps and reported as an extra field, and so is the fp8 (e4m3 x e4m3, 
 GEMM of the same size against the dense fp8 peak, the block-scaled fp8 GEMM, and two register
 fragment copies: the 16384 x 16384 fp16 matrix stored column-major loaded into 32x32x16 A
 fragments (runs across memory lines: transposing LDS reads), and 8192 x 16384 fp32 32x32
-accumulator fragments stored to a row-major matrix, both against the HBM peak.
+accumulator fragments stored to a row-major matrix, both against the HBM peak; the
+asynchronous copy (4 tiles in flight) of the same 16384 x 16384 tensor; and the register-level
+product at 4096^3 with each matrix-instruction shape that divides it.  A CPU baseline times
+the oracle on bounded samples of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 60] [--no-cpu-baseline]
 
