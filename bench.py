@@ -463,6 +463,62 @@ def main():
     }
     del img_a, img_b, img_d
 
+    # the block-size choice on problems other than the headline: ragged 8000^3 and mid-size
+    # 2048^3 (128x128 blocks), bf16 and fp8, each with sampled outputs against the oracle
+    print("bench: other sizes", file=sys.stderr, flush=True)
+    sizes = {}
+    for tag, (m_, n_, k_), kind in (("bf16_8000", (8000, 8000, 8000), "bf16"),
+                                    ("bf16_2048", (2048, 2048, 2048), "bf16"),
+                                    ("fp8_2048", (2048, 2048, 2048), "fp8")):
+        sd = {"bf16_8000": (91, 92), "bf16_2048": (93, 94), "fp8_2048": (95, 96)}[tag]
+        if kind == "bf16":
+            sc = float(1.0 / np.sqrt(k_))
+            ab, bb, _ = synth.gemm_inputs(m_, n_, k_, "bf16", False, False, 0.0, (sd[0], sd[1], 0),
+                                          a_scale=sc, b_scale=sc)
+        else:
+            ab, bb, _ = synth.gemm_fp8_inputs(m_, n_, k_, "e4m3", "e4m3", False, True, 0.0,
+                                              (sd[0], sd[1], 0))
+        Ax, Bx = up(ab), up(bb)
+        Dx = torch.empty((m_, n_), dtype=torch.float32, device=dev)
+        if kind == "bf16":
+            plan = tg.tile_gemm_plan(Ax, Bx, None, Dx, m_, n_, k_, 0, 0, 0.0, tg.TG_BF16)
+            call = lambda: tg.tile_gemm(Ax, Bx, None, Dx, m_, n_, k_, 0, 0, 0.0, tg.TG_BF16)  # noqa: E731
+        else:
+            plan = tg.tile_gemm_fp8_plan(Ax, Bx, None, Dx, m_, n_, k_, 0, 1, 0.0, e4, e4)
+            call = lambda: tg.tile_gemm_fp8(Ax, Bx, None, Dx, m_, n_, k_, 0, 1, 0.0, e4, e4)  # noqa: E731
+        # launched back to back between one pair of events: at 2048^3 a kernel takes about as
+        # long as a launch from Python, and events around each launch would time the gaps too
+        for _ in range(leg_warmup):
+            call()
+        bev2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        bev2[0].record()
+        for _ in range(reps):
+            call()
+        bev2[1].record()
+        torch.cuda.synchronize()
+        ms_ = bev2[0].elapsed_time(bev2[1]) / reps
+        rs, cs = synth.sample_points(m_, n_, sd[0] + 100, count=256, tile=(plan.block_m, plan.block_n))
+        got = Dx.cpu().numpy()[rs, cs]
+        if kind == "bf16":
+            ref_, bnd_ = og.gemm_ref_at(ab, bb, None, m_, n_, k_, False, False, 0.0, "bf16", rs, cs)
+            ok_, worst_ = og.check(got, ref_, bnd_)
+        else:
+            ref_, bnd_ = og.gemm_fp8_ref_at(ab, bb, None, m_, n_, k_, False, True, 0.0, "e4m3", "e4m3",
+                                            rs, cs)
+            ok_, worst_ = og.check_fp8(got, ref_, bnd_, ab, bb, m_, n_, k_, False, True, "e4m3", "e4m3",
+                                       rs, cs)
+        sizes[tag] = {"shape": [m_, n_, k_], "block": plan.block_m, "avg_ms": round(ms_, 5),
+                      "TFLOP/s": round(2.0 * m_ * n_ * k_ / (ms_ * 1e-3) / 1e12, 3),
+                      "parity": {"sampled_ok": bool(ok_), "worst_err_over_tol": round(float(worst_), 5)}}
+        del Ax, Bx, Dx
+    frag["gemm_other_sizes"] = {
+        "workload": "tile_gemm / tile_gemm_fp8 beyond the headline: 8000^3 bf16 (ragged 256x256 "
+                    "blocks, 125 K stages) and 2048^3 bf16 / e4m3 (128x128 blocks); A [M,K], "
+                    "B [K,N] (bf16) or [N,K] (fp8), beta 0; launches back to back, averaged",
+        "sizes": sizes,
+    }
+
     base = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
