@@ -14,8 +14,9 @@ fragment copies: the 16384 x 16384 fp16 matrix stored column-major loaded into 3
 fragments (runs across memory lines: transposing LDS reads), and 8192 x 16384 fp32 32x32
 accumulator fragments stored to a row-major matrix, both against the HBM peak; the
 asynchronous copy (4 tiles in flight) of the same 16384 x 16384 tensor; and the register-level
-product at 4096^3 with each matrix-instruction shape that divides it.  A CPU baseline times
-the oracle on bounded samples of the same workload.
+product at 4096^3 with each matrix-instruction shape that divides it; and the GEMM at other
+sizes (8000^3 bf16, 2048^3 bf16 and e4m3).  A CPU baseline times the oracle on bounded samples
+of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 60] [--no-cpu-baseline]
 
