@@ -64,14 +64,16 @@ def test_direct_width_matches_the_oracle_rule(kind):
 ])
 def test_auto_route(kind, lk, route):
     tr, tc, _, _ = fr.KINDS[kind]
-    for store, line_bytes in ((0, 256), (1, 512)):      # block lines: 256 B loads, 512 B stores
+    # blocks of 64 lines: loads 256-byte lines, four blocks per workgroup along the lines;
+    # stores 512-byte lines, one block per workgroup
+    for store, line_bytes, nb in ((0, 256, 4), (1, 512, 1)):
         p = plan(store, kind, 2 * tr, 4 * tc, lk)
         assert p.route == route
         if route == tg.TG_FRAG_LDS:
-            assert (p.vec_bits, p.lds_bytes, p.threads) == (128, 64 * line_bytes, 256)
+            assert (p.vec_bits, p.lds_bytes, p.threads) == (128, 64 * line_bytes * nb, 256)
             lines, line_len = (2 * tr, 4 * tc) if lk == "row" else (4 * tc, 2 * tr)
             per_line = line_bytes // (fr.KINDS[kind][2] // 8)
-            assert p.grid == -(-lines // 64) * -(-line_len // per_line)
+            assert p.grid == -(-lines // 64) * -(-(-(-line_len // per_line)) // nb)
 
 
 def test_auto_falls_back_to_direct_when_lines_are_not_16_byte_aligned():

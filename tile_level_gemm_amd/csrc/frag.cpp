@@ -136,9 +136,11 @@ int plan_frag(bool store, const void* mem, const void* image, const int64_t shap
   if (r == TG_FRAG_LDS) {
     plan->vec = 16 / k.eb;
     plan->vec_bits = 128;
-    plan->lds_bytes = kFragLdsLines * frag_lds_line_bytes(store);
+    const int nb = frag_lds_blocks(store);
+    plan->lds_bytes = kFragLdsLines * frag_lds_line_bytes(store) * nb;
     const int64_t per_line = frag_lds_line_bytes(store) / k.eb;
-    plan->grid = ((lines + kFragLdsLines - 1) / kFragLdsLines) * ((line_len + per_line - 1) / per_line);
+    const int64_t nbp = (line_len + per_line - 1) / per_line;   // blocks along a line
+    plan->grid = ((lines + kFragLdsLines - 1) / kFragLdsLines) * ((nbp + nb - 1) / nb);
   } else {
     plan->vec = vb / k.eb;
     plan->vec_bits = 8 * vb;

@@ -305,13 +305,17 @@ __device__ __forceinline__ void lds_write_run(uint8_t* lds, int q, int p, typena
   }
 }
 
-// One workgroup per block of 64 lines x LB bytes (blocks walk along the lines first); the
-// block's tiles are shared out over the four waves.  Stores use 512-byte lines (each workgroup
-// writes runs of 512 bytes of every line: 5.6-6.2 TB/s against 5.5-6.1 with 256), loads
-// 256-byte ones (3.2-3.8 TB/s with 512 against 5.0-6.0).
+// One workgroup per NB blocks of 64 lines x LB bytes, adjacent along the lines (groups walk
+// along the lines first); each block's tiles are shared out over the four waves.  Stores use
+// one block of 512-byte lines (each workgroup writes runs of 512 bytes of every line: 5.6-6.2
+// TB/s against 5.5-6.1 with 256), loads four blocks of 256-byte lines (with one block, 512-byte
+// lines read at 3.2-3.8 TB/s against 5.0-6.0 with 256): every load of all four blocks is in
+// flight before the first LDS write, so a workgroup reads 1 KiB runs of each line.
 template <int KIND, bool STORE, bool TRANS>
 __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
   constexpr int LB = frag_lds_line_bytes(STORE);
+  constexpr int NB = frag_lds_blocks(STORE);
+  constexpr int BLK = kFragLdsLines * LB;   // LDS bytes of one block
   constexpr int kLineChunks = LB / 16;   // 16-byte chunks per block line
   using K = FK<KIND>;
   constexpr bool CM = K::RUN_ROWS != TRANS;
@@ -323,63 +327,82 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
   constexpr int LANE_BYTES = K::E * K::EB;
   typedef typename RunT<K::RB>::T V;
   static_assert(NTQ * TQ == kFragLdsLines && NTP * TP == LINE, "whole tiles per block");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kFragLdsLines * LB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NB * BLK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t nbp = (a.line_len + LINE - 1) / LINE;
-  const int64_t q0 = (int64_t)(blockIdx.x / nbp) * kFragLdsLines;
-  const int64_t p0 = (int64_t)(blockIdx.x % nbp) * LINE;
+  const int64_t nbp = (a.line_len + LINE - 1) / LINE;   // blocks along a line
+  const int64_t ngp = (nbp + NB - 1) / NB;               // groups of NB blocks along a line
+  const int64_t q0 = (int64_t)(blockIdx.x / ngp) * kFragLdsLines;
+  const int64_t p0 = (int64_t)(blockIdx.x % ngp) * NB * LINE;   // the group's first element
   const int qn = (int)(a.lines - q0 < kFragLdsLines ? a.lines - q0 : kFragLdsLines);
-  const int pn = (int)(a.line_len - p0 < LINE ? a.line_len - p0 : LINE);   // multiple of TP
+  // elements of block k along the line: a multiple of TP, 0 past the end
+  auto pn_of = [&](int k) -> int {
+    const int64_t left = a.line_len - p0 - (int64_t)k * LINE;
+    return (int)(left <= 0 ? 0 : (left < LINE ? left : LINE));
+  };
   const int64_t pitch = a.ld * K::EB;
   uint8_t* gblock = a.mem + (q0 * a.ld + p0) * K::EB;
 
-  auto tile_of = [&](int b, int& tq, int& tp, int64_t& img) -> bool {
+  // tile b of block k
+  auto tile_of = [&](int k, int b, int& tq, int& tp, int64_t& img) -> bool {
     tq = b / NTP;
     tp = b % NTP;
+    const int pn = pn_of(k);
     if (tq * TQ >= qn || tp * TP >= pn) return false;
-    const int64_t qt = q0 + tq * TQ, pt = p0 + tp * TP;
+    const int64_t qt = q0 + tq * TQ, pt = p0 + (int64_t)k * LINE + tp * TP;
     const int64_t ti = CM ? pt / K::TR : qt / K::TR, tj = CM ? qt / K::TC : pt / K::TC;
     img = ((ti * a.tiles_c + tj) * 64 + lane) * LANE_BYTES;
     return true;
   };
 
   if constexpr (!STORE) {
-    u32x4 v[CHUNKS];
+    int pnb[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) pnb[k] = pn_of(k) * K::EB;   // bytes of block k's lines
+    u32x4 v[CHUNKS][NB];
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
       const int c = tid + kFragThreads * i, q = c / kLineChunks, x = c % kLineChunks;
-      if (q < qn && 16 * x < pn * K::EB)
-        v[i] = __builtin_nontemporal_load((const u32x4*)(gblock + q * pitch + 16 * x));
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (q < qn && 16 * x < pnb[k])
+          v[i][k] = __builtin_nontemporal_load((const u32x4*)(gblock + q * pitch + k * LB + 16 * x));
     }
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
       const int c = tid + kFragThreads * i, q = c / kLineChunks, x = c % kLineChunks;
-      if (q < qn && 16 * x < pn * K::EB) *(u32x4*)(lds + lds_at<LB>(q, 16 * x)) = v[i];
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (q < qn && 16 * x < pnb[k]) *(u32x4*)(lds + k * BLK + lds_at<LB>(q, 16 * x)) = v[i][k];
     }
     __syncthreads();
-    for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
-      int tq, tp;
-      int64_t img;
-      if (!tile_of(b, tq, tp, img)) continue;
-      V regs[K::G];
 #pragma unroll
-      for (int g = 0; g < K::G; ++g) {
-        int r, c;
-        K::origin(lane, g, r, c);
-        regs[g] = lds_read_run<K::EB, TRANS, K::RB, LB>(lds, tq * TQ + (CM ? c : r),
-                                                    tp * TP + (CM ? r : c), lane);
+    for (int k = 0; k < NB; ++k) {
+      for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
+        int tq, tp;
+        int64_t img;
+        if (!tile_of(k, b, tq, tp, img)) continue;
+        V regs[K::G];
+#pragma unroll
+        for (int g = 0; g < K::G; ++g) {
+          int r, c;
+          K::origin(lane, g, r, c);
+          regs[g] = lds_read_run<K::EB, TRANS, K::RB, LB>(lds + k * BLK, tq * TQ + (CM ? c : r),
+                                                      tp * TP + (CM ? r : c), lane);
+        }
+#pragma unroll
+        for (int g = 0; g < K::G; ++g)
+          img_store<LANE_BYTES, V>(a.img + img, g, regs[g]);
       }
-#pragma unroll
-      for (int g = 0; g < K::G; ++g)
-        img_store<LANE_BYTES, V>(a.img + img, g, regs[g]);
     }
   } else {
+    static_assert(NB == 1, "stores move one block per workgroup");
+    const int pn = pn_of(0);
     for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
       int tq, tp;
       int64_t img;
-      if (!tile_of(b, tq, tp, img)) continue;
+      if (!tile_of(0, b, tq, tp, img)) continue;
       V regs[K::G];
 #pragma unroll
       for (int g = 0; g < K::G; ++g)

@@ -127,6 +127,9 @@ constexpr int kFragThreads = 256;          // four waves per workgroup
 constexpr int kFragLdsLines = 64;          // LDS route: a block of 64 lines x line bytes
 // bytes per block line: 256 for loads, 512 for stores (measured per direction)
 constexpr int frag_lds_line_bytes(bool store) { return store ? 512 : 256; }
+// LDS route: blocks per workgroup, adjacent along the lines (loads: 4, so that a workgroup
+// reads 1 KiB runs of every line while each block keeps its 256-byte lines)
+constexpr int frag_lds_blocks(bool store) { return store ? 1 : 4; }
 
 // Tiles one wave moves per direct-route launch iteration (4 KiB of registers per wave).
 int frag_tiles_per_wave(int kind);
