@@ -397,31 +397,37 @@ __global__ __launch_bounds__(kFragThreads) void frag_lds(FragArgs a) {
       }
     }
   } else {
-    static_assert(NB == 1, "stores move one block per workgroup");
-    const int pn = pn_of(0);
-    for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
-      int tq, tp;
-      int64_t img;
-      if (!tile_of(0, b, tq, tp, img)) continue;
-      V regs[K::G];
+    int pnb[NB];
 #pragma unroll
-      for (int g = 0; g < K::G; ++g)
-        regs[g] = img_load<LANE_BYTES, V>(a.img + img, g);
+    for (int k = 0; k < NB; ++k) pnb[k] = pn_of(k) * K::EB;   // bytes of block k's lines
 #pragma unroll
-      for (int g = 0; g < K::G; ++g) {
-        int r, c;
-        K::origin(lane, g, r, c);
-        lds_write_run<K::EB, TRANS, K::RB, LB>(lds, tq * TQ + (CM ? c : r), tp * TP + (CM ? r : c),
-                                          regs[g]);
+    for (int k = 0; k < NB; ++k) {
+      for (int b = wave; b < NTQ * NTP; b += kFragThreads / 64) {
+        int tq, tp;
+        int64_t img;
+        if (!tile_of(k, b, tq, tp, img)) continue;
+        V regs[K::G];
+#pragma unroll
+        for (int g = 0; g < K::G; ++g)
+          regs[g] = img_load<LANE_BYTES, V>(a.img + img, g);
+#pragma unroll
+        for (int g = 0; g < K::G; ++g) {
+          int r, c;
+          K::origin(lane, g, r, c);
+          lds_write_run<K::EB, TRANS, K::RB, LB>(lds + k * BLK, tq * TQ + (CM ? c : r),
+                                            tp * TP + (CM ? r : c), regs[g]);
+        }
       }
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
       const int c = tid + kFragThreads * i, q = c / kLineChunks, x = c % kLineChunks;
-      if (q < qn && 16 * x < pn * K::EB)
-        __builtin_nontemporal_store(*(const u32x4*)(lds + lds_at<LB>(q, 16 * x)),
-                                    (u32x4*)(gblock + q * pitch + 16 * x));
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (q < qn && 16 * x < pnb[k])
+          __builtin_nontemporal_store(*(const u32x4*)(lds + k * BLK + lds_at<LB>(q, 16 * x)),
+                                      (u32x4*)(gblock + q * pitch + k * LB + 16 * x));
     }
   }
 }
