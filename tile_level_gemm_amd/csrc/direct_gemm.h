@@ -108,7 +108,7 @@ __device__ __forceinline__ f32x16 mfma32s(F a, F b, f32x16 c, uint32_t sa, uint3
 }
 
 // ---- LDS layouts --------------------------------------------------------------------
-// K-major stage: 256 rows x 128 bytes; physical chunk = kc ^ sk(row).
+// K-major stage: BS rows (256 or 128) x 128 bytes; physical chunk = kc ^ sk(row).
 //   SK 0: row & 7 — eight consecutive rows hit eight chunks (32 four-byte banks);
 //   SK 1: (row & 7) ^ ((row >> 3) & 1) — also sixteen consecutive rows hit sixteen distinct
 //         (row parity, chunk) pairs, i.e. distinct banks if the LDS has 64 banks.
