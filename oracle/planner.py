@@ -11,11 +11,15 @@ Restates [VEC-AUTO]:
   consecutive fused-index slots.  The generated IR of the demo shows the fused
   index of round f, thread t as f·(threads·vec) + t·vec (生成的 TIRx IR).
 * step 2: vector widths of 128, 64, 32, 16 and 8 bits are tried widest first; a
-  width is taken when (a) the contiguous tail divides by it and (b) every
+  width is taken when every transfer moves one aligned vector on both sides.  The
+  page states this as (a) the contiguous tail divides by the width and (b) every
   non-vector stride on both sides, the thread iteration included, and both base
-  offsets are multiples of it.
+  offsets are multiples of it.  The oracle does not restate that rule: it lists
+  the element offsets of every transfer on both sides and checks the plain
+  property the rule stands for (_width_ok): the offsets are consecutive and the
+  first is a multiple of the width.
 * 输入如何改变算法 / swizzled shared 布局: with a swizzled shared side the vector
-  may not leave one 16-byte swizzle chunk.
+  may not leave one 16-byte swizzle chunk (checked transfer by transfer as well).
 * 对齐约束的兜底: misaligned strides or a region starting at an odd column narrow
   the width, down to one element.
 
@@ -23,22 +27,22 @@ Readings (the page is silent):
 
 * widths narrower than the element, or not a multiple of it, are skipped;
 * the width must also divide elements/threads, so that elements = outer·threads·vec;
-* a vector is contiguous on a side when that side stores the fused order's inner
-  dimension contiguously and the vector does not cross a row, or when the whole
-  region is packed on that side; a side stored in the other order only admits
-  one-element vectors;
 * "misaligned" is measured in elements from the side's base: base offset (pointer
-  address / element size plus region offset) and leading dimension.
+  address / element size plus region offset) and leading dimension; an element
+  offset of a side therefore counts from that side's base.
 
 Pinned by tests/test_oracle_planner.py: the page's worked example (32 threads,
 32x32 float32 -> vec 4 = 128 bits, outer 8, fused index f·128 + t·4), the
 per-dtype rounds of the same tile, the 64-elements-on-1024-threads rejection,
 and the two narrowing examples (fp16 row stride 20; a region starting at
-column 3); plus brute force that every planned chunk is contiguous and aligned
-on both sides.
+column 3); plus a re-derivation, thread by thread and round by round, that every
+planned chunk is contiguous and aligned on both sides and that the next wider width
+is not.
 """
 
-from .layout import ROW, COL, XOR, CHUNK_BYTES, xor_defined
+import numpy as np
+
+from .layout import ROW, COL, XOR, CHUNK_BYTES, offsets, xor_defined
 
 WIDTHS_BITS = (128, 64, 32, 16, 8)
 
@@ -70,47 +74,38 @@ def fused_order(drive):
     return COL if drive.kind == COL else ROW
 
 
-def _strides(side, rows, cols):
-    """(row stride, column stride) of a side, in elements."""
-    ld = side.eff_ld(rows, cols)
-    if side.kind == COL:
-        return 1, ld
-    return ld, 1
+def _transfers(side, rows, cols, order, v, elem_bytes):
+    """Element offsets on `side` of every v-element transfer: an (n / v, v) array.
 
-
-def _side_ok(side, rows, cols, order, v, elem_bytes):
-    """Is every v-element chunk of the fused order contiguous and v-aligned on this side?
-
-    A chunk is the run of fused positions [x, x+v) with x a multiple of v; the
-    fused position x is (outer, inner) = divmod(x, inner extent) in `order`.
+    Transfer k covers the fused positions [k·v, k·v + v) of the region in `order`
+    (算法核心 step 1: the vec iteration is the innermost, contiguous part of the fused
+    index); position x is (outer, inner) = divmod(x, inner extent).
     """
-    if side.kind == XOR:
-        if side.ld not in (0, cols) or not xor_defined(cols, elem_bytes):
-            return False
-        if v * elem_bytes > CHUNK_BYTES:
-            return False
-    if v == 1:
-        return True
-    s_r, s_c = _strides(side, rows, cols)
-    inner, outer_ext = (cols, rows) if order == ROW else (rows, cols)
-    s_in, s_out = (s_c, s_r) if order == ROW else (s_r, s_c)
-    if side.kind == XOR and order != ROW:
+    off = offsets(side, rows, cols, elem_bytes)          # [r, c]
+    fused = off.reshape(-1) if order == ROW else off.T.reshape(-1)
+    return fused.reshape(-1, v)
+
+
+def _width_ok(side, rows, cols, order, v, elem_bytes):
+    """Does every transfer of v elements land as one aligned vector on this side?
+
+    The plain definition of 算法核心 step 2 and 对齐约束的兜底, checked transfer by
+    transfer: the v offsets are consecutive, the first is a multiple of v (an element
+    offset counts from the side's base, so the base enters here), and on a swizzled
+    side the transfer's bytes stay inside one 16-byte swizzle chunk
+    (输入如何改变算法).
+    """
+    t = _transfers(side, rows, cols, order, v, elem_bytes)
+    if not (t == t[:, :1] + np.arange(v, dtype=np.int64)).all():
         return False
-    if inner % v == 0:
-        # chunks stay inside one row of the fused order
-        if s_in != 1:
+    if (t[:, 0] % v).any():
+        return False
+    if side.kind == XOR:
+        first = (t[:, 0] * elem_bytes) // CHUNK_BYTES
+        last = ((t[:, -1] + 1) * elem_bytes - 1) // CHUNK_BYTES
+        if (first != last).any():
             return False
-        if outer_ext > 1 and s_out % v:
-            return False
-    else:
-        # chunks cross rows: the region must be one contiguous run on this side
-        if side.kind == XOR:
-            return False
-        if inner > 1 and s_in != 1:
-            return False
-        if s_out != inner:
-            return False
-    return side.base % v == 0
+    return True
 
 
 def plan_region(rows, cols, elem_bits, threads, drive, other):
@@ -124,6 +119,8 @@ def plan_region(rows, cols, elem_bits, threads, drive, other):
     for side in (drive, other):
         if side.kind == XOR and not xor_defined(cols, eb):
             return Reject("layout", "xor layout needs rows of a power-of-two count of 16-byte chunks")
+        if side.kind == XOR and side.ld not in (0, cols):
+            return Reject("layout", "the xor layout is a packed tile")
     order = fused_order(drive)
     if n == 0:
         return Plan(0, threads, 1, elem_bits)
@@ -133,7 +130,7 @@ def plan_region(rows, cols, elem_bits, threads, drive, other):
         v = bits // elem_bits
         if (n // threads) % v:
             continue
-        if all(_side_ok(s, rows, cols, order, v, eb) for s in (drive, other)):
+        if all(_width_ok(s, rows, cols, order, v, eb) for s in (drive, other)):
             return Plan(n // (threads * v), threads, v, bits)
     return Reject("layout", "no vector width keeps every transfer contiguous")
 

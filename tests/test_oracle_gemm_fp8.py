@@ -190,3 +190,59 @@ def test_check_fp8_uses_allowance_only_where_needed():
     assert ok
     ok, worst = G.check_fp8(ref, ref, bound, a, b, M, N, K, False, True, "e5m2", "e5m2")
     assert ok and worst == 0.0
+
+
+def _fp8_codes_in(fmt, lo, hi):
+    """Every finite fp8 code of `fmt` whose magnitude lies in [lo, hi)."""
+    from oracle.numerics import fp8_bits_to_f64
+    codes = np.arange(256, dtype=np.uint8)
+    v = np.abs(fp8_bits_to_f64(codes, fmt))
+    return codes[np.isfinite(v) & (v >= lo) & (v < hi)]
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e5m2", "e5m2")])
+def test_fp8_bar_is_the_16bit_bar_within_six_binades(fa, fb):
+    # An fp8 product carries at most 8 significant bits, so a product within 2^6 of its group's
+    # largest lies on the group's 2^-13 grid: the allowance is exactly zero and the fp8 bar is
+    # north_star's 16-bit bar.  Operands drawn from [1, 2) and [2^-2, 2^1) keep every product in
+    # [2^-2, 2^2), inside six binades of any group maximum.
+    rs = np.random.default_rng(8)
+    M, N, K = 32, 48, 256
+    ca, cb = _fp8_codes_in(fa, 1.0, 2.0), _fp8_codes_in(fb, 0.25, 2.0)
+    a = rs.choice(ca, size=(M, K)) ^ (rs.integers(0, 2, (M, K), dtype=np.uint8) << 7)
+    b = rs.choice(cb, size=(K, N)) ^ (rs.integers(0, 2, (K, N), dtype=np.uint8) << 7)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    t = G.fp8_unit_allowance_at(a, b, M, N, K, False, False, fa, fb, rows.ravel(), cols.ravel())
+    assert np.all(t == 0.0)
+    d = G.gemm_fp8_ref(a, b, None, M, N, K, False, False, 0.0, fa, fb)
+    bound = G.abs_bound_fp8(a, b, M, N, K, False, False, fa, fb)
+    perturbed = d + 0.9 * G.tolerance(bound)
+    assert G.check_fp8(perturbed, d, bound, a, b, M, N, K, False, False, fa, fb) == \
+        G.check(perturbed, d, bound)
+    over = d + 1.1 * G.tolerance(bound)
+    assert not G.check_fp8(over, d, bound, a, b, M, N, K, False, False, fa, fb)[0]
+
+
+def test_fp8_allowance_appears_only_far_below_the_group_max():
+    # One group of 8 products: seven at 1 and one with low bits set 2^-10 below; the low
+    # product is off the 2^-13 grid of a group whose largest is 1 (q = 2^-13) only when it has
+    # bits below 2^-13.  e4m3 1.125·2^-6 times 1.125·2^-4 = 1.265625·2^-10 = 0b1.010001·2^-10:
+    # its last bit is 2^-16, off the grid, so the allowance is min(|p|, 2^-13) = 2^-13.
+    from oracle.numerics import fp8_bits_to_f64
+    codes = np.arange(256, dtype=np.uint8)
+    val = fp8_bits_to_f64(codes, "e4m3")
+    one = int(np.nonzero(val == 1.0)[0][0])
+    x = int(np.nonzero(val == 1.125 * 2.0 ** -6)[0][0])
+    y = int(np.nonzero(val == 1.125 * 2.0 ** -4)[0][0])
+    a = np.full((1, 8), one, np.uint8)
+    b = np.full((8, 1), one, np.uint8)
+    a[0, 7], b[7, 0] = x, y
+    t = G.fp8_unit_allowance_at(a, b, 1, 1, 8, False, False, "e4m3", "e4m3", [0], [0])
+    assert t[0] == 2.0 ** -13
+    # the same low product alone in its group is on its own grid: no allowance
+    a2 = np.full((1, 16), x, np.uint8)
+    b2 = np.full((16, 1), y, np.uint8)
+    a2[0, :8], b2[:8, 0] = one, one
+    a2[0, 8:15], b2[8:15, 0] = 0, 0
+    t2 = G.fp8_unit_allowance_at(a2, b2, 1, 1, 16, False, False, "e4m3", "e4m3", [0], [0])
+    assert t2[0] == 0.0

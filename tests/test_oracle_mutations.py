@@ -102,16 +102,16 @@ def _planner_pins():
 @pytest.mark.parametrize("kind", ["no_base", "no_ld", "narrow_first", "no_thread_check",
                                   "no_vec_divides"])
 def test_planner_mutant_is_caught(kind, monkeypatch):
-    orig_side_ok = P._side_ok
+    orig_width_ok = P._width_ok
     orig_plan = P.plan_region
 
-    def side_ok(side, rows, cols, order, v, eb):
+    def width_ok(side, rows, cols, order, v, eb):
         if kind == "no_base":
             side = L.Layout(side.kind, side.ld, 0)
         if kind == "no_ld" and side.kind != L.XOR:
             ld = side.eff_ld(rows, cols)
             side = L.Layout(side.kind, ld - ld % v if ld % v and ld > v else ld, side.base)
-        return orig_side_ok(side, rows, cols, order, v, eb)
+        return orig_width_ok(side, rows, cols, order, v, eb)
 
     def plan_region(rows, cols, elem_bits, threads, drive, other):
         if kind == "no_thread_check":
@@ -127,12 +127,12 @@ def test_planner_mutant_is_caught(kind, monkeypatch):
                 if bits < elem_bits:
                     continue
                 v = bits // elem_bits
-                if all(orig_side_ok(s, rows, cols, P.fused_order(drive), v, elem_bits // 8) for s in (drive, other)) \
+                if all(orig_width_ok(s, rows, cols, P.fused_order(drive), v, elem_bits // 8) for s in (drive, other)) \
                         and threads > 0 and n % threads == 0:
                     return P.Plan(max(1, n // (threads * v)), threads, v, bits)
         return orig_plan(rows, cols, elem_bits, threads, drive, other)
 
-    monkeypatch.setattr(P, "_side_ok", side_ok)
+    monkeypatch.setattr(P, "_width_ok", width_ok)
     monkeypatch.setattr(P, "plan_region", plan_region)
     import tests.test_oracle_planner as T
     monkeypatch.setattr(T, "plan_region", plan_region)

@@ -63,6 +63,9 @@ void strides(const Side& s, int64_t cols, int64_t* sr, int64_t* sc) {
 bool side_takes(const Side& s, int64_t rows, int64_t cols, bool row_order, int64_t v, int eb) {
   if (s.kind == TG_XOR_SWIZZLE && v * eb > 16) return false;  // one swizzle chunk at most
   if (v == 1) return true;
+  // A fused order whose inner extent is 1 visits the region in the other order's sequence
+  // (one row in column order is that row, left to right).
+  if ((row_order ? cols : rows) == 1) row_order = !row_order;
   int64_t sr, sc;
   strides(s, cols, &sr, &sc);
   const int64_t inner = row_order ? cols : rows;
