@@ -265,6 +265,15 @@ def test_gemm_kernel_choice():
     assert (p.block_m, p.grid, p.loader) == (64, 256, 0)
     p = tg.tile_gemm_plan(None, None, None, D_ADDR, 16, 8, 0, 0, 0, 0.0, tg.TG_F16)
     assert p.kernel == tg.TG_GEMM_FILL
+    # the direct kernel's 32-bit DMA offsets address whole 64-K stages: an M/N-major A with
+    # M = 2^26 and K = 8 is 1 GiB, but 64 k-rows of it are 8 GiB, so it takes the 64-bit tiled
+    # kernel; just under 2 GiB of whole stages it stays on the direct kernel
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 1 << 26, 8, 8, 1, 0, 0.0, tg.TG_BF16)
+    assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 0)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 16, 1 << 26, 8, 0, 0, 0.0, tg.TG_BF16)
+    assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 0)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, (1 << 24) - 256, 8, 8, 1, 0, 0.0, tg.TG_BF16)
+    assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 1)
     p = tg.tile_gemm_plan(None, None, None, None, 0, 8, 16, 0, 0, 0.0, tg.TG_F16)
     assert p.kernel == tg.TG_GEMM_NONE
 

@@ -8,6 +8,13 @@ every call raises.
 
 `torch` is imported before the library is loaded so that the library binds to the
 HIP runtime torch already loaded (one runtime per process).
+
+Tensor arguments are checked here before the library is called, because the library
+only sees addresses: every tensor must live on a GPU, all tensors of one call on the same
+GPU, with the element size the call's format implies and at least the bytes its sizes
+imply (a shorter buffer would be read or written past its end).  A failed check raises
+TileError and launches nothing.  Integer addresses are passed through unchecked: a caller
+who passes raw addresses vouches for them.
 """
 
 import ctypes
@@ -183,6 +190,59 @@ def _addr(x):
     raise TypeError(f"expected a tensor, an int address or None, got {type(x)}")
 
 
+ELEM_BYTES = {TG_F16: 2, TG_BF16: 2, TG_F32: 4, TG_U8: 1, TG_I8: 1, TG_FP8_E4M3: 1, TG_FP8_E5M2: 1}
+
+
+def _on_gpu(t):
+    """True for a tensor in GPU memory (the library dereferences device addresses only)."""
+    return t.is_cuda
+
+
+def _checked(*args):
+    """Validate the tensor arguments of one call: (name, value, element bytes or None, bytes).
+
+    value None or an int address is not checked.  A tensor must be on a GPU, on the same GPU
+    as the call's other tensors, have the given element size and hold at least `bytes`."""
+    dev = None
+    for name, x, esize, nbytes in args:
+        if not isinstance(x, torch.Tensor):
+            continue
+        if not _on_gpu(x):
+            raise TileError(TG_E_ARG, f"{name} is on {x.device}, not on a GPU")
+        if dev is None:
+            dev = x.device
+        elif x.device != dev:
+            raise TileError(TG_E_ARG, f"{name} is on {x.device}, the call's other tensors on {dev}")
+        if esize is not None and x.element_size() != esize:
+            raise TileError(TG_E_DTYPE, f"{name} has {x.element_size()}-byte elements, the call "
+                                        f"expects {esize}-byte elements")
+        have = x.numel() * x.element_size()
+        if have < nbytes:
+            raise TileError(TG_E_SHAPE, f"{name} holds {have} bytes, the sizes need {nbytes}")
+
+
+def _extent(shape, layout, esize):
+    """Bytes a layout of `shape` spans from its first element: the largest offset + 1."""
+    rows, cols = int(shape[0]), int(shape[1])
+    if rows <= 0 or cols <= 0:
+        return 0
+    lay = _layout(layout)
+    if lay.kind == TG_XOR_SWIZZLE:
+        return rows * cols * esize
+    if lay.kind == TG_COL_MAJOR:
+        ld = lay.ld or rows
+        return ((cols - 1) * ld + rows) * esize
+    ld = lay.ld or cols
+    return ((rows - 1) * ld + cols) * esize
+
+
+def _gemm_tensors(A, B, C, D, M, N, K, beta, ea, eb):
+    """ea, eb: operand element bytes (None for a format the library will reject)."""
+    m, n, k = max(int(M), 0), max(int(N), 0), max(int(K), 0)
+    _checked(("A", A, ea, m * k * (ea or 1)), ("B", B, eb, k * n * (eb or 1)),
+             ("C", C, 4, m * n * 4 if float(beta) == 1.0 else 0), ("D", D, 4, m * n * 4))
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
@@ -208,6 +268,8 @@ def _shape(shape):
 
 def tile_gemm(A, B, C, D, M, N, K, transA, transB, beta, dtype, stream=None):
     """D = A·B + beta·C through the library (see include/tilegemm.h)."""
+    e = ELEM_BYTES.get(int(dtype))
+    _gemm_tensors(A, B, C, D, M, N, K, beta, e, e)
     _check(lib().tile_gemm(_addr(A), _addr(B), _addr(C), _addr(D), M, N, K, int(transA),
                            int(transB), float(beta), int(dtype), _stream(stream)))
 
@@ -225,9 +287,18 @@ def gemm(A, B, C=None, beta=0.0, trans_a=False, trans_b=False, alpha=1.0, out=No
         raise TileError(TG_E_ARG, "alpha must be 1.0")
     if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
         raise TileError(TG_E_DTYPE, "A and B must both be float16 or both bfloat16")
+    if A.dim() != 2 or B.dim() != 2:
+        raise TileError(TG_E_SHAPE, "A and B must be matrices")
     M = A.shape[1] if trans_a else A.shape[0]
     K = A.shape[0] if trans_a else A.shape[1]
     N = B.shape[0] if trans_b else B.shape[1]
+    kb = B.shape[1] if trans_b else B.shape[0]
+    if kb != K:
+        raise TileError(TG_E_SHAPE, f"A has K = {K}, B has K = {kb}")
+    for name, t in (("C", C), ("out", out)):
+        if t is not None and (tuple(t.shape) != (M, N) or t.dtype != torch.float32):
+            raise TileError(TG_E_SHAPE, f"{name} must be a ({M}, {N}) float32 tensor, got "
+                                        f"{tuple(t.shape)} {t.dtype}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     tile_gemm(A, B, C, out, M, N, K, trans_a, trans_b, beta, TORCH_DTYPES[A.dtype], stream)
@@ -236,6 +307,7 @@ def gemm(A, B, C=None, beta=0.0, trans_a=False, trans_b=False, alpha=1.0, out=No
 
 def tile_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype, stream=None):
     """D = A·B + beta·C with fp8 operands through the library (see include/tilegemm.h)."""
+    _gemm_tensors(A, B, C, D, M, N, K, beta, 1, 1)
     _check(lib().tile_gemm_fp8(_addr(A), _addr(B), _addr(C), _addr(D), M, N, K, int(transA),
                                int(transB), float(beta), int(a_dtype), int(b_dtype),
                                _stream(stream)))
@@ -252,6 +324,10 @@ def tile_gemm_fp8_plan(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dty
 def tile_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype,
                  stream=None):
     """Block-scaled fp8 GEMM through the library (see include/tilegemm.h)."""
+    _gemm_tensors(A, B, C, D, M, N, K, beta, 1, 1)
+    kb = max(int(K), 0) // 32
+    _checked(("A", A, None, 0), ("SA", SA, 1, max(int(M), 0) * kb),
+             ("SB", SB, 1, max(int(N), 0) * kb), ("D", D, None, 0))
     _check(lib().tile_gemm_mx(_addr(A), _addr(B), _addr(SA), _addr(SB), _addr(C), _addr(D), M, N,
                               K, int(transA), int(transB), float(beta), int(a_dtype),
                               int(b_dtype), _stream(stream)))
@@ -275,14 +351,22 @@ def _opts(opts):
                     int(opts.get("flags", 0)))
 
 
+def _copy_tensors(src, dst, shape, dtype, src_layout, dst_layout):
+    e = ELEM_BYTES.get(int(dtype))
+    _checked(("src", src, e, _extent(shape, src_layout, e or 1)),
+             ("dst", dst, e, _extent(shape, dst_layout, e or 1)))
+
+
 def tile_copy(src, dst, shape, dtype, src_layout=None, dst_layout=None, stream=None):
     sl, dl = _layout(src_layout), _layout(dst_layout)
+    _copy_tensors(src, dst, shape, dtype, src_layout, dst_layout)
     _check(lib().tile_copy(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
                            ctypes.byref(dl), _stream(stream)))
 
 
 def tile_copy_ex(src, dst, shape, dtype, src_layout, dst_layout, opts, stream=None):
     sl, dl, o = _layout(src_layout), _layout(dst_layout), _opts(opts)
+    _copy_tensors(src, dst, shape, dtype, src_layout, dst_layout)
     _check(lib().tile_copy_ex(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
                               ctypes.byref(dl), ctypes.byref(o) if o is not None else None,
                               _stream(stream)))
@@ -308,6 +392,7 @@ def _async_opts(opts):
 def tile_copy_async(src, dst, shape, dtype, src_layout, dst_layout, opts, stream=None):
     """Copy with issue-only global -> LDS transfers, `depth` tiles in flight per workgroup."""
     sl, dl, o = _layout(src_layout), _layout(dst_layout), _async_opts(opts)
+    _copy_tensors(src, dst, shape, dtype, src_layout, dst_layout)
     _check(lib().tile_copy_async(_addr(src), _addr(dst), _shape(shape), int(dtype), ctypes.byref(sl),
                                  ctypes.byref(dl), ctypes.byref(o) if o is not None else None,
                                  _stream(stream)))
@@ -335,6 +420,9 @@ def tile_copy_partition(rows, cols, elem_bits, threads, drive, drive_base, other
 def tile_frag_load(src, image, shape, dtype, src_layout, kind, route=TG_FRAG_AUTO, stream=None):
     """Matrix -> register image of fragment `kind` (see include/tilegemm.h)."""
     lay = _layout(src_layout)
+    e = ELEM_BYTES.get(int(dtype))
+    n = max(int(shape[0]), 0) * max(int(shape[1]), 0)
+    _checked(("src", src, e, _extent(shape, src_layout, e or 1)), ("image", image, None, n * (e or 1)))
     _check(lib().tile_frag_load(_addr(src), _addr(image), _shape(shape), int(dtype),
                                 ctypes.byref(lay), int(kind), int(route), _stream(stream)))
 
@@ -342,6 +430,9 @@ def tile_frag_load(src, image, shape, dtype, src_layout, kind, route=TG_FRAG_AUT
 def tile_frag_store(image, dst, shape, dtype, dst_layout, kind, route=TG_FRAG_AUTO, stream=None):
     """Register image of fragment `kind` -> matrix."""
     lay = _layout(dst_layout)
+    e = ELEM_BYTES.get(int(dtype))
+    n = max(int(shape[0]), 0) * max(int(shape[1]), 0)
+    _checked(("image", image, None, n * (e or 1)), ("dst", dst, e, _extent(shape, dst_layout, e or 1)))
     _check(lib().tile_frag_store(_addr(image), _addr(dst), _shape(shape), int(dtype),
                                  ctypes.byref(lay), int(kind), int(route), _stream(stream)))
 
@@ -357,6 +448,11 @@ def tile_frag_plan(store, mem, image, shape, dtype, layout, kind, route=TG_FRAG_
 def tile_frag_mma(a_image, b_image, c_image, d_image, M, N, K, beta, a_dtype, b_dtype, shape,
                   stream=None):
     """D = A·B (+ C) over register images of the shape's kinds."""
+    ea, eb = ELEM_BYTES.get(int(a_dtype), 1), ELEM_BYTES.get(int(b_dtype), 1)
+    m, n, k = max(int(M), 0), max(int(N), 0), max(int(K), 0)
+    _checked(("a_image", a_image, None, m * k * ea), ("b_image", b_image, None, k * n * eb),
+             ("c_image", c_image, None, m * n * 4 if float(beta) == 1.0 else 0),
+             ("d_image", d_image, None, m * n * 4))
     _check(lib().tile_frag_mma(_addr(a_image), _addr(b_image), _addr(c_image), _addr(d_image), M,
                                N, K, float(beta), int(a_dtype), int(b_dtype), int(shape),
                                _stream(stream)))

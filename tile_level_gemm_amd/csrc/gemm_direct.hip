@@ -18,11 +18,15 @@ hipError_t launch_direct_dt(const GemmArgs& g, int64_t grid, hipStream_t s) {
 
 }  // namespace
 
-// Each operand under 2 GiB, so that every buffer offset (per-lane plus per-stage, and the
-// out-of-range 2^31 of a partial last stage plus the stage offset) fits the 32-bit fields.
+// Each operand, with K rounded up to whole 64-K stages, under 2 GiB: the DMA of an M/N-major
+// operand addresses k-rows up to the end of the last stage (those past K are range-checked
+// to zero), and every buffer offset (per-lane plus per-stage, and the out-of-range 2^31 of a
+// partial last stage plus the stage offset) must fit the 32-bit fields without wrapping back
+// into the operand.
 bool direct_gemm_fits(int64_t M, int64_t N, int64_t K) {
   const int64_t lim = (int64_t)1 << 31;
-  return M > 0 && N > 0 && K > 0 && M * K * 2 < lim && K * N * 2 < lim;
+  const int64_t kp = (K + 63) / 64 * 64;
+  return M > 0 && N > 0 && K > 0 && M * kp * 2 < lim && kp * N * 2 < lim;
 }
 
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
