@@ -116,7 +116,8 @@ typedef struct tg_copy_plan {
 /* Kernel choice of tile_gemm, reported by tile_gemm_plan. */
 typedef enum tg_gemm_kernel {
   TG_GEMM_NONE = 0,     /* nothing to launch (M == 0 or N == 0) */
-  TG_GEMM_ATOM = 1,     /* register kernel: one wave per 16x16 output tile, v_mfma_f32_16x16x32 */
+  TG_GEMM_ATOM = 1,     /* register kernel: one wave per output tile of one matrix instruction
+                           (tg_gemm_plan.atom; tile_gemm_atom_select says which) */
   TG_GEMM_TILED = 2,    /* LDS double-buffered kernel, v_mfma_f32_32x32x16 (fp8:
                            v_mfma_f32_32x32x64_f8f6f4) */
   TG_GEMM_FILL = 3      /* K == 0: D = beta*C without a product */
@@ -131,7 +132,7 @@ typedef struct tg_gemm_plan {
   int32_t lds_bytes;
   int64_t grid;                   /* workgroups */
   int32_t loader;                 /* 0: operands staged through VGPRs, 1: direct global -> LDS */
-  int32_t reserved;
+  int32_t atom;                   /* TG_GEMM_ATOM: the tg_mma_shape it runs (else 0) */
 } tg_gemm_plan;
 
 /*
@@ -480,15 +481,35 @@ int tile_frag_mma(const void* a_image, const void* b_image, const float* c_image
                   int64_t M, int64_t N, int64_t K, float beta, int a_dtype, int b_dtype,
                   int shape, void* stream);
 
+/*
+ * tile_gemm_atom_select — host-only: the matrix instruction tile_gemm's register kernel runs for
+ * a problem (tile_gemm takes that kernel when M·N <= 4096).  [TCGEN05-CP] 形状选择 tries the
+ * candidate shapes from the widest down against the operands' layouts; [SYNC-GEMM] 二 takes the
+ * k16 atom when K allows it and the k8 atom otherwise.  Here the candidates are 32x32x16,
+ * 16x16x32, 32x32x8 and 16x16x16 (widest first); one is admissible when its K depth divides K
+ * (K is never padded); M and N are padded up to it (MFMA has no 8-wide N; padded rows and
+ * columns are zero and never stored).  The admissible shape with the least work after padding
+ * wins; ties go to the fewest global loads per multiply-add for the stored layouts (a lane's
+ * run of K values is one vector load from a K-contiguous operand — A with transA == 0, B with
+ * transB == 1 — and one load per value otherwise), then to the wider shape.  16x8x16 takes
+ * 16x16x16; K = 8 or 24 takes 32x32x8.
+ *   M, N, K  > 0 and K % 8 == 0 (else TG_E_SHAPE); dtype TG_F16 or TG_BF16 (else TG_E_DTYPE);
+ *   transA, transB 0 or 1 (else TG_E_ARG); *shape receives a tg_mma_shape (NULL: TG_E_ARG).
+ * Needs no GPU.
+ */
+int tile_gemm_atom_select(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB,
+                          int* shape);
+
 /* Reason for the last failure on the calling thread ("" after a success): the readable
  * reason a call was refused, as the dispatcher reports why no variant accepts a call
  * ([SYNC-GEMM] 二, the failure reasons of the dispatch; [VEC-AUTO] 接受什么输入).  The
  * string stays valid until the next call on the same thread. */
 const char* tile_last_error(void);
 
-/* Library ABI version (this header: 6; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
+/* Library ABI version (this header: 7; 2 added tile_gemm_fp8 and tile_gemm_fp8_plan, 3 added
  * tile_gemm_mx and tile_gemm_mx_plan, 4 the register fragment calls tile_frag_*, 5
- * tile_copy_async and tile_copy_async_plan, 6 the K = 8 / 16 atoms and tile_mma_select). */
+ * tile_copy_async and tile_copy_async_plan, 6 the K = 8 / 16 atoms and tile_mma_select, 7
+ * tile_gemm_atom_select and tg_gemm_plan.atom). */
 int tile_abi_version(void);
 
 #ifdef __cplusplus

@@ -190,6 +190,47 @@ def select_mma(M, N, K, a_fmt, b_fmt):
     return None
 
 
+def gemm_atom_loads(shape, trans_a, trans_b):
+    """Global load instructions one lane issues per atom step for its A and B fragments.
+
+    A lane's fragment is a run of K values of one row of A (one column of B).  Stored
+    K-contiguous (A with trans_a false, B with trans_b true) the run is one vector load; stored
+    M- or N-contiguous the run crosses memory lines, one load per element."""
+    run = KINDS[SHAPES[shape][0]][3]          # K elements per lane
+    a = 1 if not trans_a else run
+    b = 1 if trans_b else run
+    return a + b
+
+
+def select_gemm_atom(M, N, K, fmt, trans_a, trans_b):
+    """The matrix instruction of the register-level GEMM for a whole problem, or None.
+
+    Readings of [TCGEN05-CP] 形状选择 (candidates from the widest atom down, each tested against
+    the operands' layouts) and [SYNC-GEMM] 二 (the k16 atom when K allows it, else k8):
+      * an atom is admissible when its K depth divides K: the K of an atom is never padded;
+      * M and N are padded up to the atom (no matrix instruction has an 8-wide N; padded rows
+        and columns are zero and never stored);
+      * the admissible atom with the least padded work (multiply-adds after padding) wins;
+      * ties go to the fewest global load instructions per multiply-add for the operands'
+        stored layouts (gemm_atom_loads), then to the earlier candidate (the wider atom).
+    For these four candidates a wider atom never needs more loads per multiply-add, so the
+    layout term never reverses the order that width gives (tests pin this).
+    """
+    if fmt not in ("f16", "bf16") or min(M, N, K) <= 0:
+        return None
+    best, best_key = None, None
+    for order, shape in enumerate(CANDIDATES_16):
+        am, an, ak = SHAPES[shape][3]
+        if K % ak:
+            continue
+        work = (-(-M // am) * am) * (-(-N // an) * an) * K
+        loads_per_mac = gemm_atom_loads(shape, trans_a, trans_b) / (am * an * ak)
+        key = (work, loads_per_mac, order)
+        if best_key is None or key < best_key:
+            best, best_key = shape, key
+    return best
+
+
 def unpack(image, rows, cols, kind, dtype):
     """The packed row-major rows x cols matrix a register image holds."""
     mem = np.zeros(rows * cols, dtype=dtype)

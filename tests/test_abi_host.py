@@ -33,13 +33,14 @@ def test_every_declared_symbol_is_exported():
             "tile_gemm_fp8", "tile_gemm_fp8_plan", "tile_gemm_mx", "tile_gemm_mx_plan",
             "tile_copy_partition", "tile_frag_load", "tile_frag_store", "tile_frag_plan",
             "tile_frag_mma", "tile_copy_async", "tile_copy_async_plan", "tile_mma_select",
+            "tile_gemm_atom_select",
             "tile_last_error",
             "tile_abi_version"} <= set(names)
     lib = tg.lib()
     for n in names:
         assert hasattr(lib, n), n
         assert n in tg._SIGS, n   # the binding marshals every declared entry point
-    assert tg.tile_abi_version() == 6
+    assert tg.tile_abi_version() == 7
 
 
 # ------------------------------------------------------------- planner ----
@@ -265,14 +266,20 @@ def test_gemm_kernel_choice():
     assert (p.block_m, p.grid, p.loader) == (64, 256, 0)
     p = tg.tile_gemm_plan(None, None, None, D_ADDR, 16, 8, 0, 0, 0, 0.0, tg.TG_F16)
     assert p.kernel == tg.TG_GEMM_FILL
-    # the direct kernel's 32-bit DMA offsets address whole 64-K stages: an M/N-major A with
-    # M = 2^26 and K = 8 is 1 GiB, but 64 k-rows of it are 8 GiB, so it takes the 64-bit tiled
-    # kernel; just under 2 GiB of whole stages it stays on the direct kernel
+    # the direct kernel's 32-bit DMA offsets address whole 64-K stages of an M/N-major operand:
+    # with M = 2^26 and K = 8 that operand is 1 GiB, but 64 k-rows of it are 8 GiB and the
+    # offsets would wrap back into it, so it takes the 64-bit tiled kernel; whole stages of
+    # exactly 2^32 bytes (M = 2^25) still do not wrap.  A K-major operand never addresses past
+    # its own rows, so 2 GiB of it stays on the direct kernel whatever K is.
     p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 1 << 26, 8, 8, 1, 0, 0.0, tg.TG_BF16)
     assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 0)
     p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 16, 1 << 26, 8, 0, 0, 0.0, tg.TG_BF16)
     assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 0)
-    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, (1 << 24) - 256, 8, 8, 1, 0, 0.0, tg.TG_BF16)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, (1 << 25) + 16, 8, 8, 1, 0, 0.0, tg.TG_BF16)
+    assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 0)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 1 << 25, 8, 8, 1, 0, 0.0, tg.TG_BF16)
+    assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 1)
+    p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, 1 << 26, 8, 8, 0, 0, 0.0, tg.TG_BF16)
     assert (p.kernel, p.loader) == (tg.TG_GEMM_TILED, 1)
     p = tg.tile_gemm_plan(None, None, None, None, 0, 8, 16, 0, 0, 0.0, tg.TG_F16)
     assert p.kernel == tg.TG_GEMM_NONE
@@ -393,3 +400,42 @@ def test_mx_scale_arguments():
     p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, SA_ADDR, SB_ADDR, None, D_ADDR, 8192, 8192, 8192, 1, 0,
                              0.0, e4, tg.TG_FP8_E5M2)
     assert (p.kernel, p.block_m, p.block_k, p.grid, p.loader) == (tg.TG_GEMM_TILED, 256, 128, 1024, 1)
+
+
+# ------------------------------------------------- register GEMM atom choice ----
+
+def _atom_name(code):
+    return {tg.TG_MMA_32x32x16: "32x32x16", tg.TG_MMA_16x16x32: "16x16x32",
+            tg.TG_MMA_32x32x8: "32x32x8", tg.TG_MMA_16x16x16: "16x16x16"}[code]
+
+
+def test_gemm_atom_choice_matches_oracle():
+    import itertools
+    from oracle.fragment import select_gemm_atom
+    for M, N, K, ta, tb, dt in itertools.product((16, 32, 48, 64, 96, 128, 256), (8, 16, 24, 32, 40, 64),
+                                                 (8, 16, 24, 32, 40, 48, 64, 96, 200),
+                                                 (0, 1), (0, 1), ("f16", "bf16")):
+        code = tg.TG_F16 if dt == "f16" else tg.TG_BF16
+        got = _atom_name(tg.tile_gemm_atom_select(M, N, K, code, ta, tb))
+        assert got == select_gemm_atom(M, N, K, dt, bool(ta), bool(tb)), (M, N, K, ta, tb)
+        if M * N <= 64 * 64:
+            p = tg.tile_gemm_plan(A_ADDR, B_ADDR, None, D_ADDR, M, N, K, ta, tb, 0.0, code)
+            assert p.kernel == tg.TG_GEMM_ATOM and _atom_name(p.atom) == got
+            am = 32 if got.startswith("32") else 16
+            assert (p.block_m, p.block_n, p.threads) == (am, am, 64)
+            assert p.grid == -(-M // am) * -(-N // am)
+            assert p.bounds_checked == int(M % am != 0 or N % am != 0)
+
+
+def test_gemm_atom_select_rejections():
+    for args, status in (((16, 8, 12, tg.TG_F16, 0, 0), tg.TG_E_SHAPE),
+                         ((0, 8, 16, tg.TG_F16, 0, 0), tg.TG_E_SHAPE),
+                         ((16, 8, 16, tg.TG_FP8_E4M3, 0, 0), tg.TG_E_DTYPE),
+                         ((16, 8, 16, tg.TG_F16, 2, 0), tg.TG_E_ARG)):
+        with pytest.raises(tg.TileError) as e:
+            tg.tile_gemm_atom_select(*args)
+        assert e.value.status == status
+    # the page's atom and its K = 8 / 24 cases
+    assert tg.tile_gemm_atom_select(16, 8, 16, tg.TG_F16, 0, 0) == tg.TG_MMA_16x16x16
+    assert tg.tile_gemm_atom_select(16, 8, 8, tg.TG_F16, 0, 0) == tg.TG_MMA_32x32x8
+    assert tg.tile_gemm_atom_select(32, 16, 24, tg.TG_BF16, 0, 1) == tg.TG_MMA_32x32x8

@@ -50,6 +50,27 @@ def test_atom_16x8x16(beta):
     assert guards and ok, worst
 
 
+# The register kernel's atoms: shapes whose choice is each of the four matrix instructions,
+# in every stored orientation, with M and N padded up to the atom where they are ragged.
+ATOM_SHAPES = [((16, 8, 16), tg.TG_MMA_16x16x16), ((48, 40, 16), tg.TG_MMA_16x16x16),
+               ((16, 8, 8), tg.TG_MMA_32x32x8), ((48, 24, 24), tg.TG_MMA_32x32x8),
+               ((16, 16, 32), tg.TG_MMA_16x16x32), ((48, 24, 96), tg.TG_MMA_16x16x32),
+               ((64, 64, 48), tg.TG_MMA_32x32x16), ((32, 32, 16), tg.TG_MMA_32x32x16)]
+
+
+@pytest.mark.parametrize("shape,atom", ATOM_SHAPES)
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("fmt,beta", [("f16", 1.0), ("bf16", 0.0)])
+def test_register_kernel_atoms(shape, atom, ta, tb, fmt, beta):
+    M, N, K = shape
+    code = FMT[fmt]
+    plan = tg.tile_gemm_plan(0x100000, 0x40000000, 0x80000000 if beta else None, 0xC0000000,
+                             M, N, K, int(ta), int(tb), beta, code)
+    assert (plan.kernel, plan.atom) == (tg.TG_GEMM_ATOM, atom)
+    say(f"gemm register atom {plan.atom} {M}x{N}x{K} {fmt} transA={ta} transB={tb} beta={beta}")
+    full_check(M, N, K, fmt, ta, tb, beta, (M + 21, N + 22, K + 23))
+
+
 def test_gemm_512x512x256_bf16_transb_beta1():
     say("gemm 512x512x256 bf16 transB beta=1")
     a_bits, b_bits, c = synth.gemm512_inputs()

@@ -349,3 +349,70 @@ def _pins_fail(monkeypatch, kind, how):
 ])
 def test_planted_map_mistakes_are_caught(monkeypatch, kind, how):
     assert _pins_fail(monkeypatch, kind, how) >= 1
+
+
+# ---- the register-level GEMM's atom choice (select_gemm_atom) ------------------------------
+
+def test_gemm_atom_page_cases():
+    from oracle.fragment import select_gemm_atom as sel
+    # the 16x8x16 atom of the page: N pads to 16 and the 16x16x16 atom does no other padding
+    assert sel(16, 8, 16, "f16", False, False) == "16x16x16"
+    # K = 8 and K = 24 ([SYNC-GEMM] test coverage): only the 8-deep atom takes K whole
+    assert sel(16, 8, 8, "f16", False, False) == "32x32x8"
+    assert sel(32, 16, 24, "bf16", False, True) == "32x32x8"
+    # K = 32 on a 16x16 output: the 16x16x32 atom (one load per operand per 8192 MACs) beats
+    # 16x16x16 at the same work
+    assert sel(16, 16, 32, "f16", False, False) == "16x16x32"
+    # whole 32x32 tiles: every atom does the same work; 32x32x16 has the fewest loads per MAC
+    assert sel(64, 64, 64, "bf16", False, True) == "32x32x16"
+    # stored transposed, a lane's K run is one load per element: the 8-deep 32x32 atom issues
+    # as many loads per MAC as 32x32x16 and the wider one wins the tie
+    assert sel(64, 64, 64, "bf16", True, False) == "32x32x16"
+    assert sel(16, 16, 0, "f16", False, False) is None
+    assert sel(16, 16, 16, "e4m3", False, False) is None
+
+
+def test_gemm_atom_brute_force_minimum():
+    # brute force over small problems: the chosen atom takes K whole, does the least padded work
+    # of all atoms that take K whole, and no cheaper-to-load atom does the same work
+    from itertools import product
+    from oracle.fragment import CANDIDATES_16, SHAPES, gemm_atom_loads, select_gemm_atom as sel
+    for M, N, K, ta, tb in product((16, 32, 48, 64), (8, 16, 24, 40, 64), (8, 16, 24, 32, 48, 64),
+                                   (False, True), (False, True)):
+        got = sel(M, N, K, "f16", ta, tb)
+        am, an, ak = SHAPES[got][3]
+        assert K % ak == 0
+        work = lambda s: (-(-M // SHAPES[s][3][0]) * SHAPES[s][3][0]) * \
+            (-(-N // SHAPES[s][3][1]) * SHAPES[s][3][1]) * K
+        lpm = lambda s: gemm_atom_loads(s, ta, tb) / np.prod(SHAPES[s][3])
+        ok = [s for s in CANDIDATES_16 if K % SHAPES[s][3][2] == 0]
+        assert work(got) == min(work(s) for s in ok), (M, N, K, got)
+        assert all(lpm(got) <= lpm(s) for s in ok if work(s) == work(got)), (M, N, K, ta, tb, got)
+
+
+def test_gemm_atom_load_counts():
+    from oracle.fragment import gemm_atom_loads
+    # K-major A and B: one vector load each, whatever the atom
+    assert gemm_atom_loads("32x32x16", False, True) == 2
+    assert gemm_atom_loads("16x16x16", False, True) == 2
+    # A stored [K, M]: its 8 (or 4) K values per lane are 8 (4) loads; B [K, N] likewise
+    assert gemm_atom_loads("16x16x32", True, True) == 9
+    assert gemm_atom_loads("32x32x8", True, False) == 8
+
+
+def test_gemm_atom_layout_term_never_reverses_width():
+    # For the four 16-bit shapes a wider atom never issues more loads per multiply-add, in any
+    # stored orientation: the layout term only separates ties that width already orders, so the
+    # choice is the same for all four (transA, transB).  (The term is kept because it is the
+    # page's criterion; this pin records that it does not bite for these candidates.)
+    from itertools import product
+    from oracle.fragment import CANDIDATES_16, SHAPES, gemm_atom_loads, select_gemm_atom as sel
+    for ta, tb in product((False, True), (False, True)):
+        lpm = [gemm_atom_loads(s, ta, tb) / np.prod(SHAPES[s][3]) for s in CANDIDATES_16]
+        macs = [np.prod(SHAPES[s][3]) for s in CANDIDATES_16]
+        for i in range(4):
+            for j in range(4):
+                if macs[i] > macs[j]:
+                    assert lpm[i] <= lpm[j]
+    for M, N, K in product((16, 32, 48, 64), (8, 16, 24, 40, 64), (8, 16, 24, 32, 48, 64)):
+        assert len({sel(M, N, K, "bf16", ta, tb) for ta in (False, True) for tb in (False, True)}) == 1

@@ -87,7 +87,7 @@ class GemmPlan(ctypes.Structure):
                 ("block_k", ctypes.c_int32), ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("bounds_checked", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int64), ("loader", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("atom", ctypes.c_int32)]
 
 
 class FragPlan(ctypes.Structure):
@@ -139,6 +139,7 @@ _SIGS = {
                               _INT, _INT, ctypes.POINTER(FragPlan)]),
     "tile_frag_mma": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _INT, _INT, _INT, _VP]),
     "tile_mma_select": (_INT, [_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(ctypes.c_int)]),
+    "tile_gemm_atom_select": (_INT, [_I64, _I64, _I64, _INT, _INT, _INT, ctypes.POINTER(ctypes.c_int)]),
     "tile_copy_async": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
                                ctypes.POINTER(Layout), ctypes.POINTER(AsyncOpts), _VP]),
     "tile_copy_async_plan": (_INT, [_VP, _VP, ctypes.POINTER(_I64), _INT, ctypes.POINTER(Layout),
@@ -462,4 +463,11 @@ def tile_mma_select(M, N, K, a_dtype, b_dtype):
     """The widest matrix-instruction shape whose atom divides (M, N, K) (a TG_MMA_* code)."""
     out = ctypes.c_int(0)
     _check(lib().tile_mma_select(M, N, K, int(a_dtype), int(b_dtype), ctypes.byref(out)))
+    return out.value
+
+
+def tile_gemm_atom_select(M, N, K, dtype, transA, transB):
+    """The matrix instruction tile_gemm's register kernel runs for a problem (a TG_MMA_* code)."""
+    out = ctypes.c_int(0)
+    _check(lib().tile_gemm_atom_select(M, N, K, int(dtype), int(transA), int(transB), ctypes.byref(out)))
     return out.value

@@ -151,7 +151,7 @@ void fill_plan(const GemmConfig& c, tg_gemm_plan* out) {
   out->lds_bytes = c.lds_bytes;
   out->grid = c.grid;
   out->loader = c.direct;
-  out->reserved = 0;
+  out->atom = c.kernel == TG_GEMM_ATOM ? c.atom : 0;
 }
 
 bool valid_kind(int k) { return k == TG_ROW_MAJOR || k == TG_COL_MAJOR || k == TG_XOR_SWIZZLE; }
@@ -371,7 +371,7 @@ extern "C" {
 
 const char* tile_last_error(void) { return g_last_error.c_str(); }
 
-int tile_abi_version(void) { return 6; }
+int tile_abi_version(void) { return 7; }
 
 int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D, int64_t M,
                    int64_t N, int64_t K, int transA, int transB, float beta, int dtype,
@@ -380,7 +380,7 @@ int tile_gemm_plan(const void* A, const void* B, const float* C, const float* D,
   if (!out) return fail(TG_E_ARG, "out is NULL");
   int st = validate_gemm(A, B, C, D, M, N, K, transA, transB, beta, dtype);
   if (st) return st;
-  fill_plan(choose_gemm(M, N, K), out);
+  fill_plan(choose_gemm(M, N, K, transA, transB), out);
   return TG_OK;
 }
 
@@ -389,7 +389,7 @@ int tile_gemm(const void* A, const void* B, const float* C, float* D, int64_t M,
   clear_error();
   int st = validate_gemm(A, B, C, D, M, N, K, transA, transB, beta, dtype);
   if (st) return st;
-  const GemmConfig cfg = choose_gemm(M, N, K);
+  const GemmConfig cfg = choose_gemm(M, N, K, transA, transB);
   if (cfg.kernel == TG_GEMM_NONE) return TG_OK;
   if (cfg.kernel == TG_GEMM_FILL && beta == 1.0f && C == D) return TG_OK;
   GemmArgs g{};

@@ -175,7 +175,7 @@ __device__ __forceinline__ void mn_dma_offsets(int64_t ld, int wave, int lane, u
   for (int p = 0; p < 2; ++p) {
     const uint32_t k = RPB * (uint32_t)(PER * wave + p) + (uint32_t)lane / CH;
     const uint32_t c = ((uint32_t)lane % CH) ^ sm<SMV>(k);
-    off[p] = (k * (uint32_t)ld + c * 8u) * 2u;    // bytes; < 64·ld·2 < 2^31 (whole stages of the operand fit 2 GiB)
+    off[p] = (k * (uint32_t)ld + c * 8u) * 2u;    // bytes; < 64·ld·2 <= 2^32 (whole stages span at most 2^32 bytes)
   }
 }
 

@@ -217,6 +217,20 @@ int tile_mma_select(int64_t M, int64_t N, int64_t K, int a_dtype, int b_dtype, i
   return fail(TG_E_SHAPE, fmt("no atom divides M=%lld, N=%lld, K=%lld", M, N, K));
 }
 
+int tile_gemm_atom_select(int64_t M, int64_t N, int64_t K, int dtype, int transA, int transB,
+                          int* shape) {
+  clear_error();
+  if (!shape) return fail(TG_E_ARG, "shape is NULL");
+  if (transA != 0 && transA != 1) return fail(TG_E_ARG, "transA must be 0 or 1");
+  if (transB != 0 && transB != 1) return fail(TG_E_ARG, "transB must be 0 or 1");
+  if (dtype != TG_F16 && dtype != TG_BF16)
+    return fail(TG_E_DTYPE, "the register GEMM takes TG_F16 or TG_BF16 operands");
+  if (M <= 0 || N <= 0 || K <= 0 || K % 8 != 0)
+    return fail(TG_E_SHAPE, fmt("need M, N, K > 0 and K %% 8 == 0 (got M=%lld, N=%lld, K=%lld)", M, N, K));
+  *shape = gemm_atom_choice(M, N, K, transA, transB);
+  return TG_OK;
+}
+
 int tile_frag_plan(int store, const void* mem, const void* image, const int64_t shape[2],
                    int dtype, const tg_layout* layout, int kind, int route, tg_frag_plan* out) {
   clear_error();

@@ -18,15 +18,21 @@ hipError_t launch_direct_dt(const GemmArgs& g, int64_t grid, hipStream_t s) {
 
 }  // namespace
 
-// Each operand, with K rounded up to whole 64-K stages, under 2 GiB: the DMA of an M/N-major
-// operand addresses k-rows up to the end of the last stage (those past K are range-checked
-// to zero), and every buffer offset (per-lane plus per-stage, and the out-of-range 2^31 of a
-// partial last stage plus the stage offset) must fit the 32-bit fields without wrapping back
-// into the operand.
-bool direct_gemm_fits(int64_t M, int64_t N, int64_t K) {
-  const int64_t lim = (int64_t)1 << 31;
+// Each operand under 2 GiB (its byte count is the 32-bit num_records of its buffer
+// descriptor), and no 32-bit buffer offset may wrap: a wrapped offset lands back inside the
+// operand instead of past its end, where the range check returns zeros.  A K-major operand
+// addresses its own rows only (a partial last stage masks the chunks past K per lane with the
+// offset 2^31, and 2^31 plus a stage offset stays below 2^32).  The DMA of an M/N-major
+// operand addresses k-rows up to the end of its last 64-K stage, so whole stages of it must
+// span at most 2^32 bytes; the k-rows past K then lie between the operand's end and 2^32 and
+// read as zero.
+bool direct_gemm_fits(int64_t M, int64_t N, int64_t K, int trans_a, int trans_b) {
+  const int64_t lim = (int64_t)1 << 31, wrap = (int64_t)1 << 32;
   const int64_t kp = (K + 63) / 64 * 64;
-  return M > 0 && N > 0 && K > 0 && M * kp * 2 < lim && kp * N * 2 < lim;
+  if (M <= 0 || N <= 0 || K <= 0 || M * K * 2 >= lim || K * N * 2 >= lim) return false;
+  if (trans_a && kp * M * 2 > wrap) return false;    // A stored [K][M]
+  if (!trans_b && kp * N * 2 > wrap) return false;   // B stored [K][N]
+  return true;
 }
 
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,

@@ -281,53 +281,106 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled(GemmArg
 }
 
 // --------------------------------------------------------- atom kernel ----
-// One wave per 16x16 block of D with v_mfma_f32_16x16x32: the register-level form of
-// the page's primitive (all fragments in registers, one atom per output tile per K
-// step).  N = 8 pads to 16 columns and K = 16 pads to 32 with zero fragments.
-template <bool TA, bool TB, int DT>
-__global__ __launch_bounds__(64) void gemm_atom(GemmArgs g) {
-  const int tiles_n = (g.N + 15) / 16;
-  const int m0 = ((int)blockIdx.x / tiles_n) * 16;
-  const int n0 = ((int)blockIdx.x % tiles_n) * 16;
-  const int lane = (int)threadIdx.x;
-  const int m = m0 + (lane & 15);   // always < M (M % 16 == 0)
-  const int n = n0 + (lane & 15);
-  f32x4 acc = f32x4{};
-  for (int k0 = 0; k0 < g.K; k0 += 32) {
-    const int kk = k0 + 8 * (lane >> 4);
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (kk < g.K) {   // K % 8 == 0: the 8-wide k chunk is wholly in or out
-      if (!TA) {
-        a = *(const u32x4*)(g.A + (int64_t)m * g.K + kk);
-      } else {
-        uint16_t e[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = g.A[(int64_t)(kk + q) * g.M + m];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = (uint32_t)e[2 * q] | ((uint32_t)e[2 * q + 1] << 16);
-      }
-      if (n < g.N) {
-        if (TB) {
-          b = *(const u32x4*)(g.B + (int64_t)n * g.K + kk);
-        } else {
-          uint16_t e[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) e[q] = g.B[(int64_t)(kk + q) * g.N + n];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) b[q] = (uint32_t)e[2 * q] | ((uint32_t)e[2 * q + 1] << 16);
-        }
-      }
+// Register kernel for small problems: one wave per output tile of the chosen matrix instruction
+// (its atom), every fragment loaded from global memory straight into the registers the
+// instruction reads, one instruction per K step accumulated in place — the page's primitive
+// as it stands (一: all fragments in registers, one atom per output tile per K step).  The atom
+// is chosen on the host among 32x32x16, 16x16x32, 32x32x8 and 16x16x16: its K depth divides K
+// (K is never padded, as the page takes k16 when K allows and k8 otherwise, 二), M and N pad
+// up to it (zero fragments, masked stores), and it does the least padded work, then needs the
+// fewest loads per multiply-add for the operands' layouts, then is the widest.
+//   lane l of an AM x AN x AK atom with R K values per lane supplies A[m0 + l % AM][k0 + R(l / AM)
+//   .. + R] and B[k0 + R(l / AN) .. + R][n0 + l % AN]; the 32x32 accumulator holds D[8(e/4) +
+//   4(l/32) + e%4][l%32] in register e, the 16x16 one D[4(l/16) + e][l%16].
+template <int SHAPE>
+struct AtomGeom {
+  static constexpr int AM = (SHAPE == TG_MMA_32x32x16 || SHAPE == TG_MMA_32x32x8) ? 32 : 16;
+  static constexpr int AK = SHAPE == TG_MMA_16x16x32 ? 32 : SHAPE == TG_MMA_32x32x8 ? 8 : 16;
+  static constexpr int R = (SHAPE == TG_MMA_32x32x8 || SHAPE == TG_MMA_16x16x16) ? 4 : 8;
+  static constexpr int ACC = AM == 32 ? 16 : 4;
+};
+
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+template <int SHAPE, int DT, class ACC>
+__device__ __forceinline__ ACC atom_mfma(u32x4 a, u32x4 b, ACC c) {
+  if constexpr (SHAPE == TG_MMA_32x32x16) return Mfma<DT>::m32(a, b, c);
+  else if constexpr (SHAPE == TG_MMA_16x16x32) return Mfma<DT>::m16(a, b, c);
+  else {
+    const u32x2 a2 = {a[0], a[1]}, b2 = {b[0], b[1]};
+    if constexpr (SHAPE == TG_MMA_32x32x8) {
+      if constexpr (DT == TG_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, a2),
+                                                    __builtin_bit_cast(f16x4, b2), c, 0, 0, 0);
+      else
+        return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a2),
+                                                        __builtin_bit_cast(s16x4, b2), c, 0, 0, 0);
+    } else {
+      if constexpr (DT == TG_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a2),
+                                                     __builtin_bit_cast(f16x4, b2), c, 0, 0, 0);
+      else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a2),
+                                                         __builtin_bit_cast(s16x4, b2), c, 0, 0, 0);
     }
-    acc = Mfma<DT>::m16(a, b, acc);
+  }
+}
+
+// R consecutive K values of one row (column) of an operand: one vector load when the operand
+// is stored K-contiguous, one 16-bit load per value when K runs across memory lines.  Rows
+// (columns) past the matrix and K past its end read as zero.
+template <int R, bool KCONTIG>
+__device__ __forceinline__ u32x4 atom_run(const uint16_t* p, int64_t line, int64_t ld, int64_t k,
+                                          bool in) {
+  u32x4 v = {0, 0, 0, 0};
+  if (!in) return v;
+  if constexpr (KCONTIG) {
+    if constexpr (R == 8) {
+      v = *(const u32x4*)(p + line * ld + k);
+    } else {
+      const u32x2 h = *(const u32x2*)(p + line * ld + k);
+      v[0] = h[0];
+      v[1] = h[1];
+    }
+  } else {
+    uint16_t e[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) e[q] = p[(k + q) * ld + line];
+#pragma unroll
+    for (int q = 0; q < R / 2; ++q) v[q] = (uint32_t)e[2 * q] | ((uint32_t)e[2 * q + 1] << 16);
+  }
+  return v;
+}
+
+template <bool TA, bool TB, int DT, int SHAPE>
+__global__ __launch_bounds__(64) void gemm_atom(GemmArgs g) {
+  using AG = AtomGeom<SHAPE>;
+  constexpr int AM = AG::AM, AN = AG::AM, AK = AG::AK, R = AG::R;
+  using Acc = typename std::conditional<AG::ACC == 16, f32x16, f32x4>::type;
+  const int tiles_n = (g.N + AN - 1) / AN;
+  const int m0 = ((int)blockIdx.x / tiles_n) * AM;
+  const int n0 = ((int)blockIdx.x % tiles_n) * AN;
+  const int lane = (int)threadIdx.x;
+  const int m = m0 + lane % AM, n = n0 + lane % AN;
+  const int kl = R * (lane / AM);   // this lane's first K value within an atom step (AM == AN)
+  Acc acc = Acc{};
+  for (int k0 = 0; k0 < g.K; k0 += AK) {   // AK divides K: every step is whole
+    const u32x4 a = atom_run<R, !TA>(g.A, m, TA ? g.M : g.K, k0 + kl, m < g.M);
+    const u32x4 b = atom_run<R, TB>(g.B, n, TB ? g.K : g.N, k0 + kl, n < g.N);
+    acc = atom_mfma<SHAPE, DT>(a, b, acc);
   }
   if (n < g.N) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int mm = m0 + 4 * (lane >> 4) + r;
-      const int64_t o = (int64_t)mm * g.N + n;
-      float d = acc[r];
-      if (g.use_c) d += g.C[o];
-      g.D[o] = d;
+    for (int e = 0; e < AG::ACC; ++e) {
+      const int mm = AM == 32 ? m0 + 8 * (e / 4) + 4 * (lane / 32) + e % 4 : m0 + 4 * (lane / 16) + e;
+      if (mm < g.M) {
+        const int64_t o = (int64_t)mm * g.N + n;
+        float d = acc[e];
+        if (g.use_c) d += g.C[o];
+        g.D[o] = d;
+      }
     }
   }
 }
@@ -353,7 +406,14 @@ hipError_t launch_tiled(const GemmArgs& g, const GemmConfig& c, hipStream_t s) {
 template <bool TA, bool TB, int DT>
 hipError_t launch_dt(const GemmArgs& g, const GemmConfig& c, hipStream_t s) {
   if (c.kernel == TG_GEMM_ATOM) {
-    hipLaunchKernelGGL((gemm_atom<TA, TB, DT>), dim3((unsigned)c.grid), dim3(64), 0, s, g);
+    const dim3 gd((unsigned)c.grid), bd(64);
+    switch (c.atom) {
+      case TG_MMA_32x32x16: hipLaunchKernelGGL((gemm_atom<TA, TB, DT, TG_MMA_32x32x16>), gd, bd, 0, s, g); break;
+      case TG_MMA_16x16x32: hipLaunchKernelGGL((gemm_atom<TA, TB, DT, TG_MMA_16x16x32>), gd, bd, 0, s, g); break;
+      case TG_MMA_32x32x8: hipLaunchKernelGGL((gemm_atom<TA, TB, DT, TG_MMA_32x32x8>), gd, bd, 0, s, g); break;
+      case TG_MMA_16x16x16: hipLaunchKernelGGL((gemm_atom<TA, TB, DT, TG_MMA_16x16x16>), gd, bd, 0, s, g); break;
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   if (c.bm == 256) return launch_tiled<256, 256, 128, 128, TA, TB, DT>(g, c, s);

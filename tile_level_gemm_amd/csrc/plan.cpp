@@ -13,8 +13,10 @@
 //   * 对齐约束的兜底 — misaligned strides or bases narrow the width, to 1 element.
 // Readings where the page is silent: widths below or not a multiple of the
 // element size are skipped; the width must divide elements/threads; a side
-// stored in the other order than the fused one only takes 1-element vectors;
-// a vector may cross a row only where the whole region is one contiguous run.
+// stored in the other order than the fused one only takes 1-element vectors
+// (unless the fused order's inner extent is 1: then both orders visit the same
+// sequence); a vector may cross a row only where the whole region is one
+// contiguous run.
 #include <algorithm>
 #include <cstdio>
 
@@ -150,6 +152,34 @@ bool tile_steps_aligned(const Side& s, int64_t tile_rows, int64_t tile_cols, int
 }
 
 // ---------------------------------------------------------------- GEMM ----
+// The register kernel's matrix instruction ([TCGEN05-CP] 形状选择: candidates tried from the
+// widest down against the operands' layouts; [SYNC-GEMM] 二: k16 when K allows it, else k8).
+// Per candidate (M, N, K of one atom; R K values per lane): admissible when K % K_atom == 0;
+// cost = (multiply-adds after padding M and N up to the atom, global loads per lane per atom
+// step / multiply-adds per atom, candidate order), smallest wins.  A lane's K run is one vector
+// load when its operand is stored K-contiguous, R loads when K runs across memory lines.
+int gemm_atom_choice(int64_t M, int64_t N, int64_t K, int trans_a, int trans_b) {
+  struct Cand { int shape, am, an, ak, r; };
+  static const Cand kCands[] = {{TG_MMA_32x32x16, 32, 32, 16, 8}, {TG_MMA_16x16x32, 16, 16, 32, 8},
+                                {TG_MMA_32x32x8, 32, 32, 8, 4}, {TG_MMA_16x16x16, 16, 16, 16, 4}};
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  int best = 0;
+  int64_t best_work = 0;
+  double best_lpm = 0.0;
+  for (const Cand& c : kCands) {
+    if (K % c.ak != 0) continue;
+    const int64_t work = ((M + c.am - 1) / c.am * c.am) * ((N + c.an - 1) / c.an * c.an) * K;
+    const int loads = (trans_a ? c.r : 1) + (trans_b ? 1 : c.r);
+    const double lpm = (double)loads / (double)(c.am * c.an * c.ak);
+    if (best == 0 || work < best_work || (work == best_work && lpm < best_lpm)) {
+      best = c.shape;
+      best_work = work;
+      best_lpm = lpm;
+    }
+  }
+  return best;
+}
+
 // Kernel choice.  The page lowers every (m, n) output tile to one atom per K
 // step, accumulated in place ([SYNC-GEMM] 四 step 3); on gfx950 a workgroup
 // owns a block of output tiles so that operands staged once in LDS feed many
@@ -159,7 +189,7 @@ bool tile_steps_aligned(const Side& s, int64_t tile_rows, int64_t tile_cols, int
 // blocks only where the larger ones are too few: measured, 128-wide blocks lose to
 // 256-wide ones once there are 256 of those (8192^3 bf16: 1082 against 890 us,
 // 6000^3: 554 against 435 us).
-GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
+GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K, int trans_a, int trans_b) {
   GemmConfig c{};
   if (M == 0 || N == 0) {
     c.kernel = TG_GEMM_NONE;
@@ -174,12 +204,13 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   auto blocks = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (M * N <= 64 * 64) {
     c.kernel = TG_GEMM_ATOM;
-    c.bm = c.bn = 16;
-    c.bk = 32;
-    c.wm = c.wn = 16;
+    c.atom = gemm_atom_choice(M, N, K, trans_a, trans_b);
+    const int am = (c.atom == TG_MMA_32x32x16 || c.atom == TG_MMA_32x32x8) ? 32 : 16;
+    c.bm = c.bn = c.wm = c.wn = am;
+    c.bk = c.atom == TG_MMA_16x16x32 ? 32 : c.atom == TG_MMA_32x32x8 ? 8 : 16;
     c.threads = 64;
-    c.bounds = (N % 16) != 0 || (K % 32) != 0;
-    c.grid = blocks(16, 16);
+    c.bounds = (M % am) != 0 || (N % am) != 0;
+    c.grid = blocks(am, am);
     return c;
   }
   c.kernel = TG_GEMM_TILED;
@@ -188,7 +219,7 @@ GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K) {
   // more, a CU runs three or more of them one after the other, slower than the one 256-wide
   // block it would get (fp8 3072^3: 41.7 against 35.6 us).  Operands of 2 GiB or more take
   // the VGPR-staged kernel on 256- or 64-wide tiles.
-  const bool fits = direct_gemm_fits(M, N, K);
+  const bool fits = direct_gemm_fits(M, N, K, trans_a, trans_b);
   if (blocks(256, 256) >= 256 || (fits && blocks(128, 128) > 512)) {
     c.bm = c.bn = 256;
     c.wm = c.wn = 128;

@@ -90,15 +90,23 @@ struct GemmConfig {
   int lds_bytes;
   int64_t grid;
   int direct;          // 1: gemm_direct (global -> LDS loads, whole 256x256 tiles, K % 128 == 0)
+  int atom;            // TG_GEMM_ATOM: the matrix instruction (tg_mma_shape)
 };
 
-// Host-side kernel choice for a validated problem.
-GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K);
+// The register kernel's matrix instruction for a problem: the candidates widest first; one is
+// admissible when its K depth divides K; the least work after padding M and N up to it wins,
+// then the fewest global loads per multiply-add for the stored layouts, then the widest.
+// Returns a tg_mma_shape, or 0 when none is admissible (K <= 0 or K % 8 != 0).
+int gemm_atom_choice(int64_t M, int64_t N, int64_t K, int trans_a, int trans_b);
+
+// Host-side kernel choice for a validated problem (the transposes decide which operand extents
+// the direct kernel's 32-bit offsets must cover).
+GemmConfig choose_gemm(int64_t M, int64_t N, int64_t K, int trans_a, int trans_b);
 
 int launch_gemm(const GemmArgs& g, const GemmConfig& cfg, int trans_a, int trans_b, int dtype,
                 void* stream);
 
-bool direct_gemm_fits(int64_t M, int64_t N, int64_t K);
+bool direct_gemm_fits(int64_t M, int64_t N, int64_t K, int trans_a, int trans_b);
 
 // fp8 GEMM (any operand orientation): 256x256 blocks (128x128 when there are fewer than 256 of
 // the larger and at most 512 of the smaller), 512 threads, grid = ceil(M/bm)·ceil(N/bn);
