@@ -25,6 +25,13 @@ semantics with NaN-filled C, transposition equivalence over all four
 (transA, transB) pairs and both formats, identity and zero matrices, and the
 acceptance table against the page's listed rejections.
 
+The block-scaled entry points with 6- and 4-bit operands (accepts_mx and the gemm_mx_*
+functions on packed rows) are pinned by tests/test_oracle_gemm_mx_small.py: the fp4 value
+table, the formats' extremes, fp4 inside e2m3 and every fp6 value an e4m3 value, hand-built
+packed bytes, Fraction brute force of the scaled sums, an all-ones A giving column sums, one
+scale step doubling exactly one block, and the acceptance table; planted mistakes are caught
+(tests/test_oracle_mutations.py).
+
 The fp8 entry points (accepts_fp8, gemm_fp8_ref, gemm_fp8_ref_at, abs_bound_fp8)
 are pinned by tests/test_oracle_gemm_fp8.py: exact int64 products of operands
 decoded by torch's own float8 types (all four format pairs, all transposes,
@@ -34,7 +41,7 @@ products, and their acceptance table.
 
 import numpy as np
 
-from .numerics import decode, e8m0_bits_to_f64
+from .numerics import SMALL, SMALL_WIDTH, decode, e8m0_bits_to_f64, unpack_rows
 
 FORMATS = ("f16", "bf16")
 
@@ -193,9 +200,65 @@ def gemm_fp8_ref_at(a_bits, b_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype,
 
 MX_BLOCK = 32
 
+# The 6- and 4-bit operands (e2m3, e3m2, e2m1; [SYNC-GEMM] 七 names fp4) take the same
+# block-scaled product.  Readings: both operands are 6- or 4-bit (any pair of the three
+# formats; a mix with fp8 is not a pair this path takes); they are stored K-contiguous, A as
+# [M][K] and B as [N][K] (transA = 0, transB = 1), each row a packed bit stream
+# (numerics.unpack_rows), because the packing and the block scales both run along K; shapes
+# as for fp8 (M, N multiples of 16, K of 128).
+
+
+def accepts_mx(M, N, K, a_dtype, b_dtype, trans_a=False, trans_b=True, c_dtype="f32",
+               d_dtype="f32", alpha=1.0, beta=0.0):
+    """Acceptance of the block-scaled GEMM.  Returns (ok, category); categories as accepts_fp8
+    plus "layout" (a 6- or 4-bit operand not stored K-contiguous)."""
+    small = a_dtype in SMALL or b_dtype in SMALL
+    if not small:
+        return accepts_fp8(M, N, K, a_dtype, b_dtype, c_dtype, d_dtype, alpha, beta)
+    if min(M, N, K) < 0 or M % 16 or N % 16 or K % 128:
+        return False, "shape"
+    if a_dtype not in SMALL or b_dtype not in SMALL or c_dtype != "f32" or d_dtype != "f32":
+        return False, "dtype"
+    if trans_a or not trans_b:
+        return False, "layout"
+    if alpha != 1.0:
+        return False, "alpha"
+    if beta not in (0.0, 1.0):
+        return False, "beta"
+    return True, None
+
+
+def _packed_rows(bits, nrows, K, fmt, rows=None):
+    """Decoded K values of the given rows (all when rows is None) of a packed K-contiguous
+    operand of nrows rows: float64 [len(rows), K]."""
+    w = SMALL_WIDTH[fmt]
+    b = np.ascontiguousarray(bits, dtype=np.uint8).reshape(nrows, K * w // 8)
+    if rows is not None:
+        b = b[np.asarray(rows, dtype=np.int64)]
+    return decode(unpack_rows(b, b.shape[0], K, w), fmt)
+
+
+def mx_logical(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype):
+    """A[M, K] and B[K, N] in float64 for any block-scaled operand format."""
+    if a_dtype in SMALL and b_dtype in SMALL:
+        return _packed_rows(a_bits, M, K, a_dtype), _packed_rows(b_bits, N, K, b_dtype).T
+    return logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype)
+
+
+def _mx_rows_of_a(a_bits, M, K, trans_a, rows, a_dtype):
+    if a_dtype in SMALL:
+        return _packed_rows(a_bits, M, K, a_dtype, rows)
+    return decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, rows)), a_dtype)
+
+
+def _mx_cols_of_b(b_bits, N, K, trans_b, cols, b_dtype):
+    if b_dtype in SMALL:
+        return _packed_rows(b_bits, N, K, b_dtype, cols)
+    return decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, cols)), b_dtype)
+
 
 def _scaled_operands(a_bits, b_bits, sa_bits, sb_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype):
-    a_l, b_l = logical_operands(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype)
+    a_l, b_l = mx_logical(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_dtype)
     sa = e8m0_bits_to_f64(np.asarray(sa_bits, np.uint8).reshape(M, K // MX_BLOCK))
     sb = e8m0_bits_to_f64(np.asarray(sb_bits, np.uint8).reshape(N, K // MX_BLOCK))
     a_s = a_l * np.repeat(sa, MX_BLOCK, axis=1)
@@ -205,8 +268,8 @@ def _scaled_operands(a_bits, b_bits, sa_bits, sb_bits, M, N, K, trans_a, trans_b
 
 def gemm_mx_ref(a_bits, b_bits, sa_bits, sb_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype,
                 b_dtype):
-    """Full float64 D_ref of the block-scaled fp8 GEMM (scales applied exactly: powers of 2)."""
-    ok, why = accepts_fp8(M, N, K, a_dtype, b_dtype, beta=beta)
+    """Full float64 D_ref of the block-scaled GEMM (scales applied exactly: powers of 2)."""
+    ok, why = accepts_mx(M, N, K, a_dtype, b_dtype, trans_a, trans_b, beta=beta)
     if not ok:
         raise ValueError(f"oracle: call rejected ({why})")
     if K == 0:
@@ -223,7 +286,7 @@ def gemm_mx_ref(a_bits, b_bits, sa_bits, sb_bits, c, M, N, K, trans_a, trans_b, 
 def gemm_mx_ref_at(a_bits, b_bits, sa_bits, sb_bits, c, M, N, K, trans_a, trans_b, beta, a_dtype,
                    b_dtype, rows, cols, chunk=512):
     """D_ref and the bound of the block-scaled GEMM at sampled outputs, one float64 dot each."""
-    ok, why = accepts_fp8(M, N, K, a_dtype, b_dtype, beta=beta)
+    ok, why = accepts_mx(M, N, K, a_dtype, b_dtype, trans_a, trans_b, beta=beta)
     if not ok:
         raise ValueError(f"oracle: call rejected ({why})")
     rows = np.asarray(rows, dtype=np.int64)
@@ -235,8 +298,8 @@ def gemm_mx_ref_at(a_bits, b_bits, sa_bits, sb_bits, c, M, N, K, trans_a, trans_
     for s0 in range(0, rows.size, chunk):
         r = rows[s0:s0 + chunk]
         q = cols[s0:s0 + chunk]
-        a = decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, r)), a_dtype)
-        b = decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, q)), b_dtype)
+        a = _mx_rows_of_a(a_bits, M, K, trans_a, r, a_dtype)
+        b = _mx_cols_of_b(b_bits, N, K, trans_b, q, b_dtype)
         a = a * np.repeat(e8m0_bits_to_f64(sa[r]), MX_BLOCK, axis=1)
         b = b * np.repeat(e8m0_bits_to_f64(sb[q]), MX_BLOCK, axis=1)
         prod = a * b
@@ -284,8 +347,8 @@ def fp8_unit_allowance_at(a_bits, b_bits, M, N, K, trans_a, trans_b, a_dtype, b_
     out = np.zeros(rows.size)
     if K == 0 or rows.size == 0:
         return out
-    a = decode(np.ascontiguousarray(_row_of_a(a_bits, M, K, trans_a, rows)), a_dtype)
-    b = decode(np.ascontiguousarray(_col_of_b(b_bits, N, K, trans_b, cols)), b_dtype)
+    a = _mx_rows_of_a(a_bits, M, K, trans_a, rows, a_dtype)
+    b = _mx_cols_of_b(b_bits, N, K, trans_b, cols, b_dtype)
     if sa_bits is not None:
         sa = e8m0_bits_to_f64(np.asarray(sa_bits, np.uint8).reshape(M, K // MX_BLOCK)[rows])
         sb = e8m0_bits_to_f64(np.asarray(sb_bits, np.uint8).reshape(N, K // MX_BLOCK)[cols])

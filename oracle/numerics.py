@@ -31,13 +31,16 @@ def bf16_bits_to_f64(bits):
 
 
 def decode(bits, dtype):
-    """Decode by format name: 'f16', 'bf16', 'e4m3' or 'e5m2'."""
+    """Decode by format name: 'f16', 'bf16', 'e4m3', 'e5m2', or the 6- and 4-bit 'e2m3',
+    'e3m2', 'e2m1' (codes one per array element, in the low bits)."""
     if dtype == "f16":
         return f16_bits_to_f64(bits)
     if dtype == "bf16":
         return bf16_bits_to_f64(bits)
     if dtype in _FP8:
         return fp8_bits_to_f64(bits, dtype)
+    if dtype in SMALL:
+        return small_bits_to_f64(bits, dtype)
     raise ValueError(f"oracle: unknown format {dtype!r}")
 
 
@@ -82,3 +85,52 @@ def e8m0_bits_to_f64(bits):
     """E8M0 block-scale patterns (uint8 array) -> float64: 2^(E-127), E = 255 is NaN."""
     u = np.ascontiguousarray(bits, dtype=np.uint8).astype(np.int64)
     return np.where(u == 255, np.nan, np.ldexp(1.0, u - 127))
+
+
+# ---- 6- and 4-bit formats of the block-scaled asynchronous GEMM -------------------------
+# [SYNC-GEMM] 七 names fp4 among the asynchronous GEMM's operand precisions, with SFA / SFB
+# block scales.  The formats here are the OCP microscaling element types, read from their
+# definition (sign bit, exponent field, fraction field, exponent bias):
+#
+#   e2m3 (fp6): 1 + 2 + 3 bits, bias 1;   e3m2 (fp6): 1 + 3 + 2 bits, bias 3;
+#   e2m1 (fp4): 1 + 2 + 1 bits, bias 1.
+#
+# A zero exponent field encodes the subnormals (fraction / 2^f) * 2^(1 - bias); any other
+# field e the normals (1 + fraction / 2^f) * 2^(e - bias).  None of the three has infinities
+# or NaNs: every code is a finite value, so the largest magnitudes are 7.5, 28 and 6.
+#
+# Packing (our reading; the page gives none): an operand stored K-contiguous keeps each row's
+# K codes as one little-endian bit stream, code k at bits [w·k, w·k + w) of the row, w = 6
+# or 4 — for fp4 two codes per byte, the even one in the low nibble; for fp6 four codes in
+# every 3 bytes.  A row of K codes is K·w/8 bytes.
+
+SMALL = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3), "e2m1": (2, 1, 1)}   # exponent bits, fraction bits, bias
+SMALL_WIDTH = {"e2m3": 6, "e3m2": 6, "e2m1": 4}
+
+
+def small_bits_to_f64(codes, fmt):
+    """6- or 4-bit codes (an integer array, one code per element) -> float64, exact."""
+    if fmt not in SMALL:
+        raise ValueError(f"oracle: unknown small format {fmt!r}")
+    ebits, fbits, bias = SMALL[fmt]
+    u = np.ascontiguousarray(codes).astype(np.int64)
+    if np.any((u < 0) | (u >= (1 << (1 + ebits + fbits)))):
+        raise ValueError("oracle: code out of range for the format")
+    sign = np.where((u >> (ebits + fbits)) & 1, -1.0, 1.0)
+    e = (u >> fbits) & ((1 << ebits) - 1)
+    f = u & ((1 << fbits) - 1)
+    normal = np.ldexp(((1 << fbits) + f).astype(np.float64), e - bias - fbits)
+    sub = np.ldexp(f.astype(np.float64), 1 - bias - fbits)
+    return sign * np.where(e == 0, sub, normal)
+
+
+def unpack_rows(packed, rows, K, width):
+    """Codes [rows, K] from rows of K·width/8 bytes, code k of a row at bits [width·k, width·k +
+    width) of that row's little-endian bit stream."""
+    if (K * width) % 8:
+        raise ValueError("oracle: a packed row must be a whole number of bytes")
+    nb = K * width // 8
+    b = np.ascontiguousarray(packed, dtype=np.uint8).reshape(rows, nb)
+    bits = np.unpackbits(b, axis=1, bitorder="little")          # [rows, K·width], bit i of the row
+    bits = bits.reshape(rows, K, width).astype(np.int64)
+    return (bits << np.arange(width, dtype=np.int64)).sum(axis=2)

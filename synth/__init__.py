@@ -18,6 +18,11 @@ Workloads (seeds are part of the recipe):
            transA, beta=1, sample seed 57
   gemm8kf8 A e4m3 [8192,8192] N(0,1) (61), B e4m3 stored [N,K] N(0,1) (62), transB,
            beta=0, sample seed 63
+  gemm8kf4 A e2m1 [8192,8192] N(0,1) (65), B e2m1 stored [N,K] N(0,1) (66), packed rows,
+           E8M0 scales 2^-10..2^10 (67), beta=0 (the e2m3 and e3m2 variants: seeds 68-70)
+
+6- and 4-bit operands (e2m3, e3m2, e2m1) are stored K-contiguous as packed rows: code k of a
+row at bits [w·k, w·k + w) of the row's little-endian bit stream (w = 6 or 4).
 """
 
 import numpy as np
@@ -183,3 +188,62 @@ def stream_input(rows=16384, cols=16384, seed=41):
         n = min(step, out.size - s)
         out[s:s + n] = f16_bits(g.random(n, dtype=np.float32) * np.float32(2.0) - np.float32(1.0))
     return out
+
+
+# ---- 6- and 4-bit operands ------------------------------------------------------------------
+# (exponent bits, fraction bits, exponent bias) of the OCP microscaling element types
+SMALL_FMT = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3), "e2m1": (2, 1, 1)}
+SMALL_W = {"e2m3": 6, "e3m2": 6, "e2m1": 4}
+
+
+def small_codes(x, fmt):
+    """float array -> codes of a 6- or 4-bit format: round to nearest, ties to the even
+    fraction, saturating at the largest finite magnitude (the formats have no infinities)."""
+    eb, fb, bias = SMALL_FMT[fmt]
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.int64)
+    a = np.abs(x)
+    e_max = (1 << eb) - 1 - bias
+    top = (2.0 - 2.0 ** -fb) * 2.0 ** e_max
+    e_min = 1 - bias
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    e = np.maximum(e, e_min)
+    q = np.rint(a / np.ldexp(1.0, e - fb)).astype(np.int64)       # significand in units of 2^(e-fb)
+    carry = q >= (2 << fb)
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, q >> 1, q)
+    normal = q >= (1 << fb)
+    field = np.where(normal, e + bias, 0)
+    frac = np.where(normal, q - (1 << fb), q)
+    code = (field << fb) | frac
+    code = np.where(a >= top, (((1 << eb) - 1) << fb) | ((1 << fb) - 1), code)
+    return ((sign << (eb + fb)) | code).astype(np.uint8)
+
+
+def pack_rows(codes, width):
+    """codes [rows, K] (one code per element) -> packed rows [rows, K·width/8] (uint8)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, K = codes.shape
+    bits = (codes[:, :, None] >> np.arange(width, dtype=np.uint8)) & 1
+    return np.packbits(bits.reshape(rows, K * width), axis=1, bitorder="little")
+
+
+def gemm_mx_small_inputs(M, N, K, a_fmt, b_fmt, beta, seeds, dist="codes", scale_range=(117, 138)):
+    """Packed A [M, K·wa/8], packed B [N, K·wb/8] (both K-contiguous), their codes, E8M0
+    scales SA [M, K/32], SB [N, K/32] and C (float32 U[-1, 1]) or None.
+
+    dist "codes": every code equally likely; "normal": N(0, 1) rounded to the format."""
+    sa_, sb_, sc_ = seeds
+    ga, gb = rng(sa_), rng(sb_)
+    if dist == "codes":
+        ca = ga.integers(0, 1 << SMALL_W[a_fmt], size=(M, K)).astype(np.uint8)
+        cb = gb.integers(0, 1 << SMALL_W[b_fmt], size=(N, K)).astype(np.uint8)
+    else:
+        ca = small_codes(ga.standard_normal((M, K), dtype=np.float32), a_fmt)
+        cb = small_codes(gb.standard_normal((N, K), dtype=np.float32), b_fmt)
+    gs = rng(sc_)
+    sa = gs.integers(scale_range[0], scale_range[1], size=(M, K // 32)).astype(np.uint8)
+    sb = gs.integers(scale_range[0], scale_range[1], size=(N, K // 32)).astype(np.uint8)
+    c = uniform(sc_ + 1000, M * N).reshape(M, N) if beta == 1.0 else None
+    return pack_rows(ca, SMALL_W[a_fmt]), pack_rows(cb, SMALL_W[b_fmt]), ca, cb, sa, sb, c

@@ -268,3 +268,66 @@ def test_fp8_acceptance_mutants_are_caught():
     run(G.accepts_fp8)
     for mutant in (k64, n8, any16):
         assert _caught(run, mutant)
+
+
+# ---- 6- and 4-bit operands of the block-scaled GEMM --------------------------------------
+
+def _small_pins():
+    import tests.test_oracle_gemm_mx_small as T
+    checks = [T.test_e2m1_value_table, T.test_fp4_embeds_in_e2m3, T.test_unpack_hand_built_bytes,
+              lambda: T.test_unpack_inverts_the_input_packer(4),
+              lambda: T.test_unpack_inverts_the_input_packer(6),
+              lambda: T.test_fraction_brute_force("e2m1", "e2m1"),
+              lambda: T.test_fraction_brute_force("e2m3", "e3m2"),
+              T.test_scale_raises_one_block_by_two]
+    checks += [lambda f=f: T.test_fp6_values_are_e4m3_values(f) for f in ("e2m3", "e3m2")]
+    checks += [lambda f=f, t=t, s=s: T.test_extremes_monotone_and_symmetric(f, t, s)
+               for f, t, s in (("e2m3", 7.5, 0.125), ("e3m2", 28.0, 0.0625), ("e2m1", 6.0, 0.5))]
+    checks += [lambda f=f: T.test_ones_times_b_is_column_sums(f) for f in ("e2m3", "e3m2", "e2m1")]
+    return checks
+
+
+@pytest.mark.parametrize("kind", ["high_nibble_first", "e2m3_bias_2", "e3m2_subnormal_as_normal",
+                                  "fp6_in_bytes", "scale_block_16", "scales_of_b_on_a"])
+def test_small_format_mutant_is_caught(kind, monkeypatch):
+    import oracle.numerics as Nm
+    orig_small, orig_unpack = Nm.small_bits_to_f64, Nm.unpack_rows
+
+    def small(codes, fmt):
+        u = np.asarray(codes).astype(np.int64)
+        if kind == "e2m3_bias_2" and fmt == "e2m3":
+            return orig_small(codes, fmt) / 2.0
+        if kind == "e3m2_subnormal_as_normal" and fmt == "e3m2":
+            e, f = (u >> 2) & 7, u & 3
+            v = orig_small(codes, fmt)
+            return np.where((e == 0) & (f != 0), np.where(u >> 5, -1.0, 1.0) * (4 + f) / 16.0, v)
+        return orig_small(codes, fmt)
+
+    def unpack(packed, rows, K, width):
+        if kind == "high_nibble_first" and width == 4:
+            b = np.ascontiguousarray(packed, np.uint8)
+            return orig_unpack(((b >> 4) | (b << 4)).astype(np.uint8), rows, K, width)
+        if kind == "fp6_in_bytes" and width == 6:
+            b = np.ascontiguousarray(packed, np.uint8).reshape(rows, -1)
+            out = np.zeros((rows, K), np.int64)
+            n = min(K, b.shape[1])
+            out[:, :n] = b[:, :n] & 63
+            return out
+        return orig_unpack(packed, rows, K, width)
+
+    monkeypatch.setattr(Nm, "small_bits_to_f64", small)
+    monkeypatch.setattr(Nm, "unpack_rows", unpack)
+    monkeypatch.setattr(G, "unpack_rows", unpack)
+    import tests.test_oracle_gemm_mx_small as T
+    monkeypatch.setattr(T, "small_bits_to_f64", small)
+    monkeypatch.setattr(T, "unpack_rows", unpack)
+    if kind == "scale_block_16":
+        monkeypatch.setattr(G, "MX_BLOCK", 16)
+    if kind == "scales_of_b_on_a":
+        orig = G._scaled_operands
+
+        def swapped(a_bits, b_bits, sa_bits, sb_bits, M, N, K, ta, tb, af, bf):
+            return orig(a_bits, b_bits, sb_bits if M == N else sa_bits, sa_bits if M == N else sb_bits,
+                        M, N, K, ta, tb, af, bf)
+        monkeypatch.setattr(G, "_scaled_operands", swapped)
+    assert any(_caught(lambda _: c(), None) for c in _small_pins())
