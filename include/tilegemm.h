@@ -39,7 +39,8 @@ extern "C" {
 #endif
 
 /* Element formats.  tile_gemm operands take TG_F16 or TG_BF16, tile_gemm_fp8 operands
- * TG_FP8_E4M3 or TG_FP8_E5M2; copies move any of them as raw bits. */
+ * TG_FP8_E4M3 or TG_FP8_E5M2, tile_gemm_mx those two or the 6- and 4-bit formats; copies move
+ * the whole-byte formats as raw bits (a packed 6- or 4-bit matrix copies as TG_U8 bytes). */
 typedef enum tg_dtype {
   TG_F16 = 1,       /* IEEE binary16 */
   TG_BF16 = 2,      /* bfloat16 */
@@ -47,7 +48,10 @@ typedef enum tg_dtype {
   TG_U8 = 4,        /* uint8 */
   TG_I8 = 5,        /* int8 */
   TG_FP8_E4M3 = 6,  /* float8 e4m3fn */
-  TG_FP8_E5M2 = 7   /* float8 e5m2 */
+  TG_FP8_E5M2 = 7,  /* float8 e5m2 */
+  TG_FP6_E2M3 = 8,  /* 6-bit e2m3 (bias 1, largest 7.5), packed rows: tile_gemm_mx only */
+  TG_FP6_E3M2 = 9,  /* 6-bit e3m2 (bias 3, largest 28), packed rows: tile_gemm_mx only */
+  TG_FP4_E2M1 = 10  /* 4-bit e2m1 (bias 1, largest 6), packed rows: tile_gemm_mx only */
 } tg_dtype;
 
 typedef enum tg_status {
@@ -221,6 +225,17 @@ int tile_gemm_fp8_plan(const void* A, const void* B, const float* C, const float
  *   The scales are applied by the matrix unit per 32-K block (exact: powers of two); the
  *   scaled products are summed in aligned groups of 8 on the grid tile_gemm_fp8 describes, and
  *   the group sums accumulated in fp32.
+ *
+ *   6- and 4-bit operands ([SYNC-GEMM] 七 names fp4 among the operand precisions):
+ *   a_dtype and b_dtype each TG_FP6_E2M3, TG_FP6_E3M2 or TG_FP4_E2M1 (any pair of the three;
+ *   a mix with an fp8 operand is TG_E_DTYPE).  The OCP microscaling element types: sign,
+ *   exponent and fraction fields of 1+2+3, 1+3+2 and 1+2+1 bits, biases 1, 3 and 1, subnormals
+ *   at a zero exponent field, no infinities or NaNs.  Both operands are stored K-contiguous as
+ *   packed rows — A [M][K·w/8] bytes (transA == 0) and B [N][K·w/8] bytes (transB == 1), w the
+ *   operand's bits — with code k of a row at bits [w·k, w·k + w) of that row's little-endian bit
+ *   stream (fp4: two codes per byte, the even one in the low nibble; fp6: four codes in every
+ *   three bytes).  Any other orientation is TG_E_LAYOUT.  Shapes, scales, C, D, beta and
+ *   alignment as above; each packed operand under 2 GiB.
  * Returns TG_OK or a tg_status; asynchronous on `stream`.
  */
 int tile_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,

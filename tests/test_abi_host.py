@@ -439,3 +439,36 @@ def test_gemm_atom_select_rejections():
     assert tg.tile_gemm_atom_select(16, 8, 16, tg.TG_F16, 0, 0) == tg.TG_MMA_16x16x16
     assert tg.tile_gemm_atom_select(16, 8, 8, tg.TG_F16, 0, 0) == tg.TG_MMA_32x32x8
     assert tg.tile_gemm_atom_select(32, 16, 24, tg.TG_BF16, 0, 1) == tg.TG_MMA_32x32x8
+
+
+# ------------------------------------------ block-scaled 6- and 4-bit operands ----
+
+def test_packed_mx_validation_matches_oracle():
+    import itertools
+    from oracle.gemm import accepts_mx
+    name = {tg.TG_FP6_E2M3: "e2m3", tg.TG_FP6_E3M2: "e3m2", tg.TG_FP4_E2M1: "e2m1",
+            tg.TG_FP8_E4M3: "e4m3", tg.TG_FP8_E5M2: "e5m2"}
+    cat_of = {tg.TG_E_SHAPE: "shape", tg.TG_E_DTYPE: "dtype", tg.TG_E_LAYOUT: "layout",
+              tg.TG_E_BETA: "beta"}
+    for (M, N, K), af, bf, ta, tb, beta in itertools.product(
+            [(32, 32, 128), (16, 48, 256), (40, 32, 128), (32, 32, 192), (0, 16, 128)],
+            [tg.TG_FP6_E2M3, tg.TG_FP6_E3M2, tg.TG_FP4_E2M1, tg.TG_FP8_E4M3],
+            [tg.TG_FP6_E3M2, tg.TG_FP4_E2M1, tg.TG_FP8_E5M2], (0, 1), (0, 1), (0.0, 1.0, 0.5)):
+        if af == tg.TG_FP8_E4M3 and bf == tg.TG_FP8_E5M2:
+            continue   # the fp8 pairs are the fp8 block-scaled path's own table
+        ok, cat = accepts_mx(M, N, K, name[af], name[bf], bool(ta), bool(tb), beta=beta)
+        try:
+            tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28),
+                                 C_ADDR if beta else None, D_ADDR, M, N, K, ta, tb, beta, af, bf)
+            got = (True, None)
+        except tg.TileError as e:
+            got = (False, cat_of.get(e.status, "other"))
+        assert got == (ok, cat), (M, N, K, af, bf, ta, tb, beta, got)
+
+
+def test_packed_mx_plan():
+    p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None, D_ADDR,
+                             1040, 272, 640, 0, 1, 0.0, tg.TG_FP4_E2M1, tg.TG_FP6_E2M3)
+    assert (p.kernel, p.block_m, p.block_n, p.block_k, p.threads, p.loader) == (tg.TG_GEMM_TILED, 128, 128, 128, 256, 0)
+    assert (p.grid, p.bounds_checked) == (9 * 3, 1)
+    assert p.lds_bytes == 2 * (128 * 80 + 128 * 104) + 2 * 256 * 4

@@ -1,0 +1,121 @@
+"""GPU parity of tile_gemm_mx with 6- and 4-bit operands (e2m3, e3m2, e2m1; [SYNC-GEMM] 七: fp4
+operands with SFA / SFB block scales) against the oracle, element by element, with the fp8
+bar (the unit's grouped-sum allowance on the scaled products) and the plain 16-bit bar
+recorded beside it."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import tile_level_gemm_amd as tg
+from oracle import gemm as og
+from tests.gpu_util import Guarded, say, upload_f32
+
+pytestmark = pytest.mark.gpu
+
+FMT = {"e2m3": tg.TG_FP6_E2M3, "e3m2": tg.TG_FP6_E3M2, "e2m1": tg.TG_FP4_E2M1}
+
+
+def up8(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda:0")
+
+
+def run_small(M, N, K, af, bf, beta, seed, dist="codes", c_is_d=False, scale_range=(117, 138)):
+    pa, pb, _, _, sa, sb, c = synth.gemm_mx_small_inputs(M, N, K, af, bf, beta,
+                                                          (seed, seed + 1, seed + 2), dist=dist,
+                                                          scale_range=scale_range)
+    D = Guarded(M * N * 4, fill=(c if c_is_d else np.full((M, N), np.nan, np.float32)))
+    Cd = upload_f32(c) if beta == 1.0 and not c_is_d else None
+    tg.tile_gemm_mx(up8(pa), up8(pb), up8(sa), up8(sb), D.ptr if c_is_d else Cd, D.ptr, M, N, K,
+                    0, 1, beta, FMT[af], FMT[bf])
+    torch.cuda.synchronize()
+    return D.host(np.float32).reshape(M, N), D.guards_intact(), (pa, pb, sa, sb, c)
+
+
+def full_check(M, N, K, af, bf, beta, seed, **kw):
+    d, guards, (pa, pb, sa, sb, c) = run_small(M, N, K, af, bf, beta, seed, **kw)
+    ref = og.gemm_mx_ref(pa, pb, sa, sb, c, M, N, K, False, True, beta, af, bf)
+    bound = og.abs_bound_mx(pa, pb, sa, sb, M, N, K, False, True, af, bf)
+    ok, worst = og.check_fp8(d, ref, bound, pa, pb, M, N, K, False, True, af, bf, sa_bits=sa,
+                             sb_bits=sb)
+    assert guards, "guard band written"
+    assert ok, f"worst |D-D_ref|/tol = {worst}"
+    return og.check(d, ref, bound)[1]
+
+
+PAIRS = [(a, b) for a in FMT for b in FMT]
+
+
+@pytest.mark.parametrize("af,bf", PAIRS)
+def test_format_pairs(af, bf):
+    say(f"gemm_mx packed 256x256x384 {af} x {bf}")
+    full_check(256, 256, 384, af, bf, 1.0, 7)
+
+
+# whole and ragged 128x128 blocks, one to many 128-K stages, beta 0 and 1
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (128, 128, 128), (144, 208, 256), (400, 272, 640),
+                                   (1024, 1040, 1152)])
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+@pytest.mark.parametrize("af,bf", [("e2m1", "e2m1"), ("e3m2", "e2m3")])
+def test_shapes(M, N, K, beta, af, bf):
+    say(f"gemm_mx packed {M}x{N}x{K} {af} x {bf} beta={beta}")
+    full_check(M, N, K, af, bf, beta, M + N + K)
+
+
+@pytest.mark.parametrize("af", ["e2m1", "e2m3"])
+def test_normal_data_and_wide_scales(af):
+    # N(0,1) rounded to the format, scales over 2^-60 .. 2^60
+    say(f"gemm_mx packed 512x512x1024 {af} normal data, wide scales")
+    full_check(512, 512, 1024, af, af, 0.0, 41, dist="normal", scale_range=(67, 188))
+
+
+def test_in_place_c_is_d():
+    say("gemm_mx packed in place C == D")
+    full_check(272, 144, 384, "e2m1", "e3m2", 1.0, 51, c_is_d=True)
+
+
+def test_sampled_2048():
+    M = N = K = 2048
+    say("gemm_mx packed 2048^3 e2m1 sampled")
+    d, guards, (pa, pb, sa, sb, c) = run_small(M, N, K, "e2m1", "e2m1", 0.0, 61, dist="normal")
+    rows, cols = synth.sample_points(M, N, 64, count=4096, tile=(128, 128))
+    ref, bound = og.gemm_mx_ref_at(pa, pb, sa, sb, None, M, N, K, False, True, 0.0, "e2m1", "e2m1",
+                                   rows, cols)
+    ok, worst = og.check_fp8(d[rows, cols], ref, bound, pa, pb, M, N, K, False, True, "e2m1", "e2m1",
+                             rows, cols, sa_bits=sa, sb_bits=sb)
+    assert guards and ok, worst
+
+
+def test_one_hot_block_scales_reach_their_block():
+    # A = 1.0 everywhere, B one-hot per column in one block, scales 2^(n mod 7) on that block of B:
+    # each output is exactly the chosen B scale times the A scale of the block
+    M, N, K = 32, 32, 256
+    ca = np.full((M, K), 0x2, np.uint8)          # e2m1 1.0
+    cb = np.zeros((N, K), np.uint8)
+    ks = (np.arange(N) * 37) % K
+    cb[np.arange(N), ks] = 0x2
+    sa = np.full((M, K // 32), 127, np.uint8)
+    sa[:, 3] = 130
+    sb = (127 + (np.arange(N)[:, None] % 7) + np.zeros((1, K // 32), int)).astype(np.uint8)
+    D = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    say("gemm_mx packed one-hot block scales")
+    tg.tile_gemm_mx(up8(synth.pack_rows(ca, 4)), up8(synth.pack_rows(cb, 4)), up8(sa), up8(sb), None,
+                    D, M, N, K, 0, 1, 0.0, tg.TG_FP4_E2M1, tg.TG_FP4_E2M1)
+    torch.cuda.synchronize()
+    want = og.gemm_mx_ref(synth.pack_rows(ca, 4), synth.pack_rows(cb, 4), sa, sb, None, M, N, K,
+                          False, True, 0.0, "e2m1", "e2m1")
+    assert np.array_equal(D.cpu().numpy(), want.astype(np.float32))
+
+
+def test_rejections():
+    A = torch.zeros(8192, dtype=torch.uint8, device="cuda:0")
+    S = torch.zeros(1024, dtype=torch.uint8, device="cuda:0")
+    D = torch.zeros(64 * 64, dtype=torch.float32, device="cuda:0")
+    for args, status in (((0, 0), tg.TG_E_LAYOUT), ((1, 1), tg.TG_E_LAYOUT),
+                         ((0, 1, tg.TG_FP4_E2M1, tg.TG_FP8_E4M3), tg.TG_E_DTYPE)):
+        ta, tb = args[:2]
+        af, bf = (args[2], args[3]) if len(args) > 2 else (tg.TG_FP4_E2M1, tg.TG_FP4_E2M1)
+        with pytest.raises(tg.TileError) as e:
+            tg.tile_gemm_mx(A, A, S, S, None, D, 64, 64, 128, ta, tb, 0.0, af, bf)
+        assert e.value.status == status

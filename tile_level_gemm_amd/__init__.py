@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libtilegemm.so")
 
 # enums of include/tilegemm.h
 TG_F16, TG_BF16, TG_F32, TG_U8, TG_I8, TG_FP8_E4M3, TG_FP8_E5M2 = 1, 2, 3, 4, 5, 6, 7
+TG_FP6_E2M3, TG_FP6_E3M2, TG_FP4_E2M1 = 8, 9, 10   # packed K-contiguous rows (tile_gemm_mx)
 TG_OK, TG_E_NULL, TG_E_SHAPE, TG_E_DTYPE, TG_E_BETA, TG_E_ALIAS = 0, -1, -2, -3, -4, -5
 TG_E_ALIGN, TG_E_THREADS, TG_E_LAYOUT, TG_E_HIP, TG_E_ARG = -6, -7, -8, -9, -10
 TG_ROW_MAJOR, TG_COL_MAJOR, TG_XOR_SWIZZLE = 0, 1, 2
@@ -192,6 +193,7 @@ def _addr(x):
 
 
 ELEM_BYTES = {TG_F16: 2, TG_BF16: 2, TG_F32: 4, TG_U8: 1, TG_I8: 1, TG_FP8_E4M3: 1, TG_FP8_E5M2: 1}
+PACKED_BITS = {TG_FP6_E2M3: 6, TG_FP6_E3M2: 6, TG_FP4_E2M1: 4}
 
 
 def _on_gpu(t):
@@ -324,9 +326,17 @@ def tile_gemm_fp8_plan(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dty
 
 def tile_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype,
                  stream=None):
-    """Block-scaled fp8 GEMM through the library (see include/tilegemm.h)."""
-    _gemm_tensors(A, B, C, D, M, N, K, beta, 1, 1)
-    kb = max(int(K), 0) // 32
+    """Block-scaled GEMM (fp8, or packed 6- / 4-bit rows) through the library (see
+    include/tilegemm.h)."""
+    m, n, k = max(int(M), 0), max(int(N), 0), max(int(K), 0)
+    if int(a_dtype) in PACKED_BITS or int(b_dtype) in PACKED_BITS:
+        # byte tensors holding packed rows of K codes
+        _checked(("A", A, 1, m * k * PACKED_BITS.get(int(a_dtype), 8) // 8),
+                 ("B", B, 1, n * k * PACKED_BITS.get(int(b_dtype), 8) // 8),
+                 ("C", C, 4, m * n * 4 if float(beta) == 1.0 else 0), ("D", D, 4, m * n * 4))
+    else:
+        _gemm_tensors(A, B, C, D, M, N, K, beta, 1, 1)
+    kb = k // 32
     _checked(("A", A, None, 0), ("SA", SA, 1, max(int(M), 0) * kb),
              ("SB", SB, 1, max(int(N), 0) * kb), ("D", D, None, 0))
     _check(lib().tile_gemm_mx(_addr(A), _addr(B), _addr(SA), _addr(SB), _addr(C), _addr(D), M, N,

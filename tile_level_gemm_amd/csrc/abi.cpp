@@ -123,12 +123,63 @@ int validate_gemm_fp8(const void* A, const void* B, const float* C, const float*
   return TG_OK;
 }
 
-// tile_gemm_mx: the fp8 checks plus the block scales SA [M][K/32] and SB [N][K/32]
-// (present when K > 0, 4-byte aligned for the 4-byte scale loads, not overlapping D).
+bool is_packed(int d) { return d == TG_FP6_E2M3 || d == TG_FP6_E3M2 || d == TG_FP4_E2M1; }
+int packed_bits(int d) { return d == TG_FP4_E2M1 ? 4 : 6; }
+// MFMA format code of a packed operand (2 = e2m3, 3 = e3m2, 4 = e2m1)
+int packed_fmt(int d) { return d == TG_FP6_E2M3 ? 2 : d == TG_FP6_E3M2 ? 3 : 4; }
+
+// 6- and 4-bit operands: both packed, stored K-contiguous (A [M][K·w/8], B [N][K·w/8]), the fp8
+// shape rules, each packed operand under 2 GiB.
+int validate_gemm_packed(const void* A, const void* B, const float* C, const float* D, int64_t M,
+                         int64_t N, int64_t K, int transA, int transB, float beta, int a_dtype,
+                         int b_dtype) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(TG_E_SHAPE, fmt("negative extent (M=%lld, N=%lld, K=%lld)", M, N, K));
+  if (M % 16 || N % 16 || K % 128)
+    return fail(TG_E_SHAPE,
+                fmt("block-scaled gemm needs M %% 16 == 0, N %% 16 == 0, K %% 128 == 0 (got M=%lld, "
+                    "N=%lld, K=%lld)", M, N, K));
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(TG_E_SHAPE, "extent above 2^30");
+  if (!is_packed(a_dtype) || !is_packed(b_dtype))
+    return fail(TG_E_DTYPE, fmt("6- and 4-bit operands pair only with each other (got a_dtype %lld, "
+                                "b_dtype %lld)", a_dtype, b_dtype));
+  const int64_t abytes = M * K * packed_bits(a_dtype) / 8, bbytes = N * K * packed_bits(b_dtype) / 8;
+  if (abytes >= ((int64_t)1 << 31) || bbytes >= ((int64_t)1 << 31))
+    return fail(TG_E_SHAPE, "each packed operand must be under 2 GiB");
+  if (transA != 0 && transA != 1) return fail(TG_E_ARG, "transA must be 0 or 1");
+  if (transB != 0 && transB != 1) return fail(TG_E_ARG, "transB must be 0 or 1");
+  if (transA != 0 || transB != 1)
+    return fail(TG_E_LAYOUT, "6- and 4-bit operands are packed along K: A stored [M][K] (transA = 0) "
+                             "and B stored [N][K] (transB = 1)");
+  if (!(beta == 0.0f || beta == 1.0f))
+    return fail(TG_E_BETA, "beta must be exactly 0.0 or 1.0 (alpha is fixed at 1)");
+  if (M == 0 || N == 0) return TG_OK;
+  if (!D) return fail(TG_E_NULL, "D is NULL");
+  if (beta == 1.0f && !C) return fail(TG_E_NULL, "beta == 1 needs C");
+  if (K > 0 && (!A || !B)) return fail(TG_E_NULL, "A or B is NULL");
+  const int64_t dbytes = M * N * 4;
+  if (K > 0) {
+    if (overlaps(D, dbytes, A, abytes) || overlaps(D, dbytes, B, bbytes))
+      return fail(TG_E_ALIAS, "D overlaps A or B");
+    if ((uintptr_t)A % 16 || (uintptr_t)B % 16)
+      return fail(TG_E_ALIGN, "A and B must be 16-byte aligned for 128-bit operand loads");
+  }
+  if (beta == 1.0f && C != D && overlaps(D, dbytes, C, dbytes))
+    return fail(TG_E_ALIAS, "C overlaps D without being exactly D");
+  if ((uintptr_t)D % 4 || (beta == 1.0f && (uintptr_t)C % 4))
+    return fail(TG_E_ALIGN, "C and D must be 4-byte aligned");
+  return TG_OK;
+}
+
+// tile_gemm_mx: the fp8 (or packed 6- / 4-bit) checks plus the block scales SA [M][K/32] and
+// SB [N][K/32] (present when K > 0, 4-byte aligned for the 4-byte scale loads, not overlapping D).
 int validate_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
                      const float* C, const float* D, int64_t M, int64_t N, int64_t K, int transA,
                      int transB, float beta, int a_dtype, int b_dtype) {
-  int st = validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
+  int st = (is_packed(a_dtype) || is_packed(b_dtype))
+               ? validate_gemm_packed(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype)
+               : validate_gemm_fp8(A, B, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
   if (st || M == 0 || N == 0 || K == 0) return st;
   if (!SA || !SB) return fail(TG_E_NULL, "SA or SB is NULL");
   if ((uintptr_t)SA % 4 || (uintptr_t)SB % 4)
@@ -137,6 +188,31 @@ int validate_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint
   if (overlaps(D, dbytes, SA, M * (K / 32)) || overlaps(D, dbytes, SB, N * (K / 32)))
     return fail(TG_E_ALIAS, "D overlaps SA or SB");
   return TG_OK;
+}
+
+// 6- / 4-bit block-scaled GEMM: 128x128 blocks of 256 threads (4 waves of 64x64), 128-K stages.
+GemmConfig choose_gemm_packed(int64_t M, int64_t N, int64_t K, int a_dtype, int b_dtype) {
+  GemmConfig c{};
+  if (M == 0 || N == 0) {
+    c.kernel = TG_GEMM_NONE;
+    return c;
+  }
+  if (K == 0) {
+    c.kernel = TG_GEMM_FILL;
+    c.threads = 256;
+    c.grid = std::min<int64_t>((M * N + 1023) / 1024, 65536);
+    return c;
+  }
+  c.kernel = TG_GEMM_TILED;
+  c.bm = c.bn = 128;
+  c.bk = 128;
+  c.wm = c.wn = 64;
+  c.threads = 256;
+  c.bounds = (M % 128) != 0 || (N % 128) != 0;
+  c.lds_bytes = packed_lds_bytes(packed_fmt(a_dtype), packed_fmt(b_dtype));
+  c.grid = ((M + 127) / 128) * ((N + 127) / 128);
+  c.direct = 0;
+  return c;
 }
 
 void fill_plan(const GemmConfig& c, tg_gemm_plan* out) {
@@ -465,7 +541,8 @@ int tile_gemm_mx_plan(const void* A, const void* B, const uint8_t* SA, const uin
   if (!out) return fail(TG_E_ARG, "out is NULL");
   int st = validate_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
   if (st) return st;
-  fill_plan(choose_gemm_fp8(M, N, K, true), out);
+  fill_plan(is_packed(a_dtype) ? choose_gemm_packed(M, N, K, a_dtype, b_dtype)
+                                : choose_gemm_fp8(M, N, K, true), out);
   return TG_OK;
 }
 
@@ -475,8 +552,30 @@ int tile_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t*
   clear_error();
   int st = validate_gemm_mx(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype);
   if (st) return st;
-  return run_gemm_fp8(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype, true,
-                      stream);
+  if (!is_packed(a_dtype))
+    return run_gemm_fp8(A, B, SA, SB, C, D, M, N, K, transA, transB, beta, a_dtype, b_dtype, true,
+                        stream);
+  const GemmConfig cfg = choose_gemm_packed(M, N, K, a_dtype, b_dtype);
+  if (cfg.kernel == TG_GEMM_NONE) return TG_OK;
+  if (cfg.kernel == TG_GEMM_FILL && beta == 1.0f && C == D) return TG_OK;
+  GemmArgs g{};
+  g.A = (const uint16_t*)A;
+  g.B = (const uint16_t*)B;
+  g.C = beta == 1.0f ? C : nullptr;
+  g.D = D;
+  g.M = (int32_t)M;
+  g.N = (int32_t)N;
+  g.K = (int32_t)K;
+  g.use_c = beta == 1.0f;
+  if (cfg.kernel == TG_GEMM_FILL) return launch_gemm(g, cfg, 0, 0, TG_BF16, stream);
+  g.tiles_m = (int32_t)((M + cfg.bm - 1) / cfg.bm);
+  g.tiles_n = (int32_t)((N + cfg.bn - 1) / cfg.bn);
+  g.SA = SA;
+  g.SB = SB;
+  const hipError_t e = launch_gemm_mx_packed(g, cfg.grid, packed_fmt(a_dtype), packed_fmt(b_dtype),
+                                             cfg.bounds != 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TG_E_HIP, std::string("tile_gemm_mx launch: ") + hipGetErrorString(e));
+  return TG_OK;
 }
 
 int tile_copy_plan(const void* src, const void* dst, const int64_t shape[2], int dtype,
