@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_TFLOPS = 2516.6   # dense fp16/bf16: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 LEG_WARMUP = 60               # untimed launches before each leg timed after the steps
 PEAK_FP8_TFLOPS = 5033.2    # dense fp8: twice the fp16/bf16 rate
+PEAK_FP4_TFLOPS = 10100.0   # dense fp6 and fp4 (MI355X published)
 PEAK_HBM_GBS = 8000.0       # HBM3E
 M = N = K = 8192
 ROWS = COLS = 16384
@@ -53,6 +54,7 @@ KERNEL_SOURCES = {
     "fp8": ("gemm_fp8.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "mx": ("gemm_mx_kk.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
+    "packed": ("gemm_mx_packed.hip", "tg_internal.h"),
     "frag": ("frag_kernels.hip", "tg_internal.h"),
     "async": ("async_copy.hip", "lds_layout.h", "tg_internal.h"),
 }
@@ -92,6 +94,10 @@ TRAFFIC_KERNELS = {
                                  2 * M * K + M * N * 4),
     "gemm_mx_256x256_e4m3_tn": ("gemm_direct<false, false, 32, 2, 4, false, 0>", "mx",
                                 2 * M * K + 2 * M * (K // 32) + M * N * 4),
+    "gemm_mx_packed_256x256_e2m1": ("gemm_mx_packed<4, 4, false, 256>", "packed",
+                                    2 * M * K // 2 + 2 * M * (K // 32) + M * N * 4),
+    "gemm_mx_packed_256x256_e2m3": ("gemm_mx_packed<2, 2, false, 256>", "packed",
+                                    2 * M * K * 6 // 8 + 2 * M * (K // 32) + M * N * 4),
     "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4, 4, 128>", "copy", 2 * ROWS * COLS * 2),
     "frag_load_a16_32x32x16_col_16384x16384": ("frag_lds<1, false, true>", "frag",
                                                2 * ROWS * COLS * 2),
@@ -290,6 +296,8 @@ def main():
     g = synth.rng(64)
     sa = g.integers(117, 138, size=(M, K // 32)).astype(np.uint8)
     sb = g.integers(117, 138, size=(N, K // 32)).astype(np.uint8)
+    small_in = {f: synth.gemm_mx_small_inputs(M, N, K, f, f, 0.0, seeds, dist="normal")
+                for f, seeds in (("e2m1", (65, 66, 67)), ("e2m3", (68, 69, 70)))}
     cr, cc = ROWS // 2, COLS
     acc_bits = synth.uniform(43, cr * cc).view(np.uint32)
     other_in = {}
@@ -395,6 +403,17 @@ def main():
     mx_list = per_launch(lambda: tg.tile_gemm_mx(A8, B8, SA, SB, None, Dm, M, N, K, 0, 1, 0.0, e4, e4))
     del A8, B8, SA, SB
 
+    print("bench: 6- and 4-bit block-scaled gemm", file=sys.stderr, flush=True)
+    small_code = {"e2m1": tg.TG_FP4_E2M1, "e2m3": tg.TG_FP6_E2M3}
+    small_run = {}
+    for f, (pa_, pb_, _, _, sa_, sb_, _) in small_in.items():
+        Ap, Bp, SAp, SBp = up8(pa_), up8(pb_), up8(sa_), up8(sb_)
+        Dp = torch.empty((M, N), dtype=torch.float32, device=dev)
+        code = small_code[f]
+        lst = per_launch(lambda: tg.tile_gemm_mx(Ap, Bp, SAp, SBp, None, Dp, M, N, K, 0, 1, 0.0, code, code))
+        small_run[f] = (lst, Dp)
+        del Ap, Bp, SAp, SBp
+
     print("bench: fragment copies and the asynchronous copy", file=sys.stderr, flush=True)
     img = torch.empty_like(S)
     fl_list = per_launch(lambda: tg.tile_frag_load(S, img, (ROWS, COLS), tg.TG_F16, (tg.TG_COL_MAJOR, 0),
@@ -480,6 +499,22 @@ def main():
     bb_ms = float(np.mean(bb_list))
     bb_gbs = copy_bytes / (bb_ms * 1e-3) / 1e9
 
+    def hbm_leg(lst, nbytes, traffic_key, parity, workload):
+        ms = float(np.mean(lst))
+        gb = nbytes / (ms * 1e-3) / 1e9
+        return {"value": round(gb, 2), "unit": "GB/s", **_stats(lst), "workload": workload,
+                "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(gb / PEAK_HBM_GBS, 4),
+                             "traffic": traffic_for(traffic_key)},
+                "parity": parity}
+
+    def mfma_leg(lst, peak, traffic_key, parity, workload):
+        tf = flops / (float(np.mean(lst)) * 1e-3) / 1e12
+        return {"value": round(tf, 3), "unit": "TFLOP/s", **_stats(lst), "workload": workload,
+                "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak, "unit": "TFLOP/s",
+                             "frac": round(tf / peak, 4), "traffic": traffic_for(traffic_key)},
+                "parity": parity}
+
     # ---- 4. parity of every leg against the oracle (host) ------------------------------------
     print("bench: parity checks (oracle)", file=sys.stderr, flush=True)
     rows, cols = synth.sample_points(M, N, 53, count=256)
@@ -518,6 +553,20 @@ def main():
     mx_ok, mx_worst = og.check_fp8(gotm, refm, boundm, fin[0], fin[1], M, N, K, False, True, "e4m3",
                                    "e4m3", rows, cols, sa_bits=sa, sb_bits=sb)
     mx_plain = og.check(gotm, refm, boundm)[1]
+    small_legs = {}
+    for f, (lst, Dp) in small_run.items():
+        pa_, pb_, _, _, sa_, sb_, _ = small_in[f]
+        refp, boundp = og.gemm_mx_ref_at(pa_, pb_, sa_, sb_, None, M, N, K, False, True, 0.0, f, f,
+                                         rows, cols)
+        gotp = Dp.cpu().numpy()[rows, cols]
+        p_ok, p_worst = og.check_fp8(gotp, refp, boundp, pa_, pb_, M, N, K, False, True, f, f, rows, cols,
+                                     sa_bits=sa_, sb_bits=sb_)
+        small_legs[f"gemm_mx_{f}_tn"] = mfma_leg(
+            lst, PEAK_FP4_TFLOPS, f"gemm_mx_packed_256x256_{f}",
+            {"sampled_ok": bool(p_ok), "worst_err_over_tol": round(p_worst, 5),
+             "worst_err_over_16bit_tol": round(og.check(gotp, refp, boundp)[1], 5)},
+            f"tile_gemm_mx 8192x8192x8192, A {f} [M,K] and B {f} [N,K] packed rows, N(0,1) rounded "
+            f"to {f}, E8M0 scales per 32 K in 2^-10..2^10, fp32 D, beta=0")
     gi = synth.rng(79)
     fl_ok = True
     imgv = img.view(-1, 64, 8)
@@ -557,22 +606,6 @@ def main():
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         base = cpu_baseline(gin, copy_src_bits, c3)
-
-    def hbm_leg(lst, nbytes, traffic_key, parity, workload):
-        ms = float(np.mean(lst))
-        gb = nbytes / (ms * 1e-3) / 1e9
-        return {"value": round(gb, 2), "unit": "GB/s", **_stats(lst), "workload": workload,
-                "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": round(gb / PEAK_HBM_GBS, 4),
-                             "traffic": traffic_for(traffic_key)},
-                "parity": parity}
-
-    def mfma_leg(lst, peak, traffic_key, parity, workload):
-        tf = flops / (float(np.mean(lst)) * 1e-3) / 1e12
-        return {"value": round(tf, 3), "unit": "TFLOP/s", **_stats(lst), "workload": workload,
-                "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak, "unit": "TFLOP/s",
-                             "frac": round(tf / peak, 4), "traffic": traffic_for(traffic_key)},
-                "parity": parity}
 
     out = {
         "metric": METRIC,
@@ -627,6 +660,7 @@ def main():
              "worst_err_over_16bit_tol": round(mx_plain, 5)},
             "tile_gemm_mx 8192x8192x8192, A e4m3 [M,K], B e4m3 [N,K], E8M0 scales per 32 K in "
             "2^-10..2^10, fp32 D, beta=0"),
+        **small_legs,
         "frag_load_a16_32x32x16_col": hbm_leg(
             fl_list, 2.0 * ROWS * COLS * 2, "frag_load_a16_32x32x16_col_16384x16384",
             {"sampled_tiles_bit_exact": fl_ok, "tiles_checked": 64},

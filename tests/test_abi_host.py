@@ -472,3 +472,12 @@ def test_packed_mx_plan():
     assert (p.kernel, p.block_m, p.block_n, p.block_k, p.threads, p.loader) == (tg.TG_GEMM_TILED, 128, 128, 128, 256, 0)
     assert (p.grid, p.bounds_checked) == (9 * 3, 1)
     assert p.lds_bytes == 2 * (128 * 80 + 128 * 104) + 2 * 256 * 4
+    # 256 or more 256x256 blocks: 512 threads on 256x256 blocks
+    p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None, D_ADDR,
+                             4096, 4112, 640, 0, 1, 0.0, tg.TG_FP6_E3M2, tg.TG_FP4_E2M1)
+    assert (p.block_m, p.block_n, p.block_k, p.threads) == (256, 256, 128, 512)
+    assert (p.grid, p.bounds_checked) == (16 * 17, 1)
+    assert p.lds_bytes == 2 * (256 * 104 + 256 * 80) + 2 * 512 * 4
+    p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None, D_ADDR,
+                             4096, 3840, 640, 0, 1, 0.0, tg.TG_FP4_E2M1, tg.TG_FP4_E2M1)
+    assert (p.block_m, p.threads, p.grid, p.bounds_checked) == (128, 256, 32 * 30, 0)

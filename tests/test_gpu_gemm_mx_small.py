@@ -63,6 +63,16 @@ def test_shapes(M, N, K, beta, af, bf):
     full_check(M, N, K, af, bf, beta, M + N + K)
 
 
+# 256x256 blocks of 512 threads (256 or more of them): whole and ragged, beta 0 and 1
+@pytest.mark.parametrize("M,N,K,af,bf,beta", [(4096, 4096, 256, "e2m1", "e2m1", 0.0),
+                                              (4096, 4112, 384, "e3m2", "e2m1", 1.0),
+                                              (4112, 4096, 256, "e2m3", "e3m2", 1.0),
+                                              (4352, 4240, 128, "e2m1", "e2m3", 0.0)])
+def test_large_blocks(M, N, K, af, bf, beta):
+    say(f"gemm_mx packed {M}x{N}x{K} {af} x {bf} beta={beta} (256x256 blocks)")
+    full_check(M, N, K, af, bf, beta, M + K)
+
+
 @pytest.mark.parametrize("af", ["e2m1", "e2m3"])
 def test_normal_data_and_wide_scales(af):
     # N(0,1) rounded to the format, scales over 2^-60 .. 2^60
@@ -83,6 +93,20 @@ def test_sampled_2048():
     ref, bound = og.gemm_mx_ref_at(pa, pb, sa, sb, None, M, N, K, False, True, 0.0, "e2m1", "e2m1",
                                    rows, cols)
     ok, worst = og.check_fp8(d[rows, cols], ref, bound, pa, pb, M, N, K, False, True, "e2m1", "e2m1",
+                             rows, cols, sa_bits=sa, sb_bits=sb)
+    assert guards and ok, worst
+
+
+@pytest.mark.parametrize("af,seed", [("e2m1", 65), ("e2m3", 68)])
+def test_sampled_8192(af, seed):
+    # the 8192^3 timed configuration: same inputs and launch, outputs sampled over every block
+    M = N = K = 8192
+    say(f"gemm_mx packed 8192^3 {af} sampled")
+    d, guards, (pa, pb, sa, sb, c) = run_small(M, N, K, af, af, 0.0, seed, dist="normal")
+    rows, cols = synth.sample_points(M, N, 64, count=4096, tile=(256, 256))
+    ref, bound = og.gemm_mx_ref_at(pa, pb, sa, sb, None, M, N, K, False, True, 0.0, af, af,
+                                   rows, cols)
+    ok, worst = og.check_fp8(d[rows, cols], ref, bound, pa, pb, M, N, K, False, True, af, af,
                              rows, cols, sa_bits=sa, sb_bits=sb)
     assert guards and ok, worst
 

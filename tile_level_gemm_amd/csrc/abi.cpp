@@ -190,7 +190,9 @@ int validate_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint
   return TG_OK;
 }
 
-// 6- / 4-bit block-scaled GEMM: 128x128 blocks of 256 threads (4 waves of 64x64), 128-K stages.
+// 6- / 4-bit block-scaled GEMM, 128-K stages: 256x256 blocks of 512 threads (8 waves of 128x64)
+// when there are at least 256 of them (as for the 16-bit kernel), else 128x128 blocks of 256
+// threads (4 waves of 64x64).
 GemmConfig choose_gemm_packed(int64_t M, int64_t N, int64_t K, int a_dtype, int b_dtype) {
   GemmConfig c{};
   if (M == 0 || N == 0) {
@@ -203,14 +205,17 @@ GemmConfig choose_gemm_packed(int64_t M, int64_t N, int64_t K, int a_dtype, int 
     c.grid = std::min<int64_t>((M * N + 1023) / 1024, 65536);
     return c;
   }
+  auto blocks = [&](int64_t b) { return ((M + b - 1) / b) * ((N + b - 1) / b); };
+  const int bs = blocks(256) >= 256 ? 256 : 128;
   c.kernel = TG_GEMM_TILED;
-  c.bm = c.bn = 128;
+  c.bm = c.bn = bs;
   c.bk = 128;
-  c.wm = c.wn = 64;
-  c.threads = 256;
-  c.bounds = (M % 128) != 0 || (N % 128) != 0;
-  c.lds_bytes = packed_lds_bytes(packed_fmt(a_dtype), packed_fmt(b_dtype));
-  c.grid = ((M + 127) / 128) * ((N + 127) / 128);
+  c.wm = bs / 2;
+  c.wn = 64;
+  c.threads = bs == 256 ? 512 : 256;
+  c.bounds = (M % bs) != 0 || (N % bs) != 0;
+  c.lds_bytes = packed_lds_bytes(packed_fmt(a_dtype), packed_fmt(b_dtype), bs);
+  c.grid = blocks(bs);
   c.direct = 0;
   return c;
 }
@@ -573,7 +578,7 @@ int tile_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t*
   g.SA = SA;
   g.SB = SB;
   const hipError_t e = launch_gemm_mx_packed(g, cfg.grid, packed_fmt(a_dtype), packed_fmt(b_dtype),
-                                             cfg.bounds != 0, (hipStream_t)stream);
+                                             cfg.bounds != 0, cfg.bm, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TG_E_HIP, std::string("tile_gemm_mx launch: ") + hipGetErrorString(e));
   return TG_OK;
 }

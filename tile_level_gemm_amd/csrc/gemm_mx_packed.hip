@@ -14,7 +14,8 @@
 // values over both blocks instead.)  So a lane's operand is one contiguous run of a stored
 // row: 16 bytes of fp4 or 24 bytes of fp6.
 //
-// Kernel: 128x128 blocks, 4 waves of 64x64 (2x2 accumulator tiles of 32x32), 128-K stages.
+// Kernel: BS x BS blocks, 128 (4 waves of 64x64) or 256 (8 waves of 128x64, for problems with at
+// least 256 such blocks: half the operand traffic per flop), 128-K stages.
 //  * global -> LDS through registers: a stage row is 64 (fp4) or 96 (fp6) bytes, moved as
 //    16-byte chunks (consecutive threads take consecutive chunks of a row: coalesced); rows
 //    past M or N are written as zeros;
@@ -38,30 +39,32 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kBM = 128, kBN = 128, kBK = 128, kThreads = 256;
+constexpr int kBK = 128;
 constexpr int kGroupM = 8;   // tile-rows per scheduling group
 
-// Per operand format code (2 = e2m3, 3 = e3m2, 4 = e2m1): bits per value, bytes of one row per
-// stage, padded LDS pitch, 16-byte chunks per row.
-template <int F>
+// Per operand format code (2 = e2m3, 3 = e3m2, 4 = e2m1) and block size: bits per value, bytes
+// of one row per stage, padded LDS pitch, 16-byte chunks per row, chunks per thread (the block
+// has 2·BS threads... BS = 128: 256 threads, BS = 256: 512).
+template <int F, int BS>
 struct Pk {
+  static constexpr int kThreads = BS == 256 ? 512 : 256;
   static constexpr int kBits = F == 4 ? 4 : 6;
   static constexpr int kRow = kBK * kBits / 8;          // 64 or 96
   static constexpr int kPitch = F == 4 ? 80 : 104;
   static constexpr int kChunks = kRow / 16;              // 4 or 6
-  static constexpr int kPer = kBM * kChunks / kThreads;  // 2 or 3 chunks per thread
+  static constexpr int kPer = BS * kChunks / kThreads;   // 2 or 3 chunks per thread
 };
 
 // One operand's stage: global -> registers -> LDS.
-template <int F, bool BOUNDS>
+template <int F, int BS, bool BOUNDS>
 struct PkLoader {
-  using P = Pk<F>;
+  using P = Pk<F, BS>;
   u32x4 v[P::kPer];
   __device__ __forceinline__ void load(const uint8_t* base, int64_t row_bytes, int rows_left,
                                        int kt, int tid) {
 #pragma unroll
     for (int i = 0; i < P::kPer; ++i) {
-      const int c = tid + i * kThreads;
+      const int c = tid + i * P::kThreads;
       const int r = c / P::kChunks, q = c - r * P::kChunks;
       if (!BOUNDS || r < rows_left)
         v[i] = *(const u32x4*)(base + (int64_t)r * row_bytes + (int64_t)kt * P::kRow + q * 16);
@@ -72,7 +75,7 @@ struct PkLoader {
   __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < P::kPer; ++i) {
-      const int c = tid + i * kThreads;
+      const int c = tid + i * P::kThreads;
       const int r = c / P::kChunks, q = c - r * P::kChunks;
       uint8_t* p = lds + r * P::kPitch + q * 16;
       if constexpr (P::kPitch % 16 == 0) {
@@ -88,7 +91,7 @@ struct PkLoader {
 // This lane's 32 K values of row `row` in 64-K step s: bytes (64s + 32h)·bits/8 of the row.
 template <int F>
 __device__ __forceinline__ i32x8 pk_frag(const uint8_t* lds, int row, int s, int h) {
-  using P = Pk<F>;
+  using P = Pk<F, 128>;
   const uint8_t* p = lds + row * P::kPitch + (64 * s + 32 * h) * P::kBits / 8;
   i32x8 f = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (F == 4) {
@@ -108,10 +111,14 @@ __device__ __forceinline__ f32x16 pk_mfma(i32x8 a, i32x8 b, f32x16 c, uint32_t s
                                                          (int)sb);
 }
 
-template <int AF, int BF, bool BOUNDS>
-__global__ __launch_bounds__(kThreads) void gemm_mx_packed(GemmArgs g) {
-  using PA = Pk<AF>;
-  using PB = Pk<BF>;
+template <int AF, int BF, bool BOUNDS, int BS>
+__global__ __launch_bounds__(BS == 256 ? 512 : 256) void gemm_mx_packed(GemmArgs g) {
+  using PA = Pk<AF, BS>;
+  using PB = Pk<BF, BS>;
+  constexpr int kBM = BS, kBN = BS;
+  constexpr int WGN = BS == 256 ? 4 : 2;                 // waves along N (2 along M)
+  constexpr int WM = BS / 2, WN = BS / WGN;              // 128x64 or 64x64
+  constexpr int TM = WM / 32, TN = WN / 32;
   __shared__ __attribute__((aligned(16))) uint8_t la[2][kBM * PA::kPitch];
   __shared__ __attribute__((aligned(16))) uint8_t lb[2][kBN * PB::kPitch];
   __shared__ __attribute__((aligned(16))) uint32_t ls[2][kBM + kBN];   // 4 scale bytes per row
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_packed(GemmArgs g) {
 
   const int tid = (int)threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave / WGN) * WM, wn = (wave % WGN) * WN;
   const int h = lane >> 5, lr = lane & 31;
 
   const int64_t rowa = (int64_t)g.K * PA::kBits / 8, rowb = (int64_t)g.K * PB::kBits / 8;
@@ -136,14 +143,14 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_packed(GemmArgs g) {
   const uint8_t* bbase = (const uint8_t*)g.B + (int64_t)n0 * rowb;
   const int ma = g.M - m0, nbl = g.N - n0;
   const int kb = g.K / 32;   // scale bytes per row
-  // scales: threads 0..127 carry A's rows, 128..255 B's; one 4-byte load per row and stage
+  // scales: threads 0..BS-1 carry A's rows, BS..2BS-1 B's; one 4-byte load per row and stage
   const bool sa_side = tid < kBM;
   const int srow = sa_side ? tid : tid - kBM;
   const bool s_in = !BOUNDS || srow < (sa_side ? ma : nbl);
   const uint8_t* sbase = sa_side ? g.SA + (int64_t)(m0 + srow) * kb : g.SB + (int64_t)(n0 + srow) * kb;
 
-  PkLoader<AF, BOUNDS> lda;
-  PkLoader<BF, BOUNDS> ldb;
+  PkLoader<AF, BS, BOUNDS> lda;
+  PkLoader<BF, BS, BOUNDS> ldb;
   uint32_t sv = 0;
   auto gload = [&](int kt) {
     lda.load(abase, rowa, ma, kt, tid);
@@ -156,30 +163,30 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_packed(GemmArgs g) {
     ls[buf][tid] = sv;
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
   auto compute = [&](int buf) {
     // the scale words of this lane's rows, shifted so that byte 2s is block 2s + h
-    uint32_t qa[2], qb[2];
+    uint32_t qa[TM], qb[TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) qa[i] = ls[buf][wm + 32 * i + lr] >> (8 * h);
+    for (int i = 0; i < TM; ++i) qa[i] = ls[buf][wm + 32 * i + lr] >> (8 * h);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) qb[j] = ls[buf][kBM + wn + 32 * j + lr] >> (8 * h);
+    for (int j = 0; j < TN; ++j) qb[j] = ls[buf][kBM + wn + 32 * j + lr] >> (8 * h);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      i32x8 a[2], b[2];
+      i32x8 a[TM], b[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = pk_frag<AF>(la[buf], wm + 32 * i + lr, s, h);
+      for (int i = 0; i < TM; ++i) a[i] = pk_frag<AF>(la[buf], wm + 32 * i + lr, s, h);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = pk_frag<BF>(lb[buf], wn + 32 * j + lr, s, h);
+      for (int j = 0; j < TN; ++j) b[j] = pk_frag<BF>(lb[buf], wn + 32 * j + lr, s, h);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TN; ++j) {
           if (s == 0) acc[i][j] = pk_mfma<AF, BF, 0>(a[i], b[j], acc[i][j], qa[i], qb[j]);
           else acc[i][j] = pk_mfma<AF, BF, 2>(a[i], b[j], acc[i][j], qa[i], qb[j]);
         }
@@ -200,9 +207,9 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_packed(GemmArgs g) {
 
   // epilogue: lane holds column lr of each tile, rows 8(e/4) + 4h + e%4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -214,38 +221,39 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_packed(GemmArgs g) {
       }
 }
 
-template <int AF, int BF>
+template <int AF, int BF, int BS>
 hipError_t launch_pk(const GemmArgs& g, int64_t grid, bool bounds, hipStream_t s) {
+  const dim3 gd((unsigned)grid), bd(BS == 256 ? 512 : 256);
   if (bounds)
-    hipLaunchKernelGGL((gemm_mx_packed<AF, BF, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, g);
+    hipLaunchKernelGGL((gemm_mx_packed<AF, BF, true, BS>), gd, bd, 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_mx_packed<AF, BF, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, g);
+    hipLaunchKernelGGL((gemm_mx_packed<AF, BF, false, BS>), gd, bd, 0, s, g);
   return hipGetLastError();
 }
 
 template <int AF>
-hipError_t launch_pk_b(const GemmArgs& g, int64_t grid, int b_fmt, bool bounds, hipStream_t s) {
+hipError_t launch_pk_b(const GemmArgs& g, int64_t grid, int b_fmt, bool bounds, int bs, hipStream_t s) {
   switch (b_fmt) {
-    case 2: return launch_pk<AF, 2>(g, grid, bounds, s);
-    case 3: return launch_pk<AF, 3>(g, grid, bounds, s);
-    case 4: return launch_pk<AF, 4>(g, grid, bounds, s);
+    case 2: return bs == 256 ? launch_pk<AF, 2, 256>(g, grid, bounds, s) : launch_pk<AF, 2, 128>(g, grid, bounds, s);
+    case 3: return bs == 256 ? launch_pk<AF, 3, 256>(g, grid, bounds, s) : launch_pk<AF, 3, 128>(g, grid, bounds, s);
+    case 4: return bs == 256 ? launch_pk<AF, 4, 256>(g, grid, bounds, s) : launch_pk<AF, 4, 128>(g, grid, bounds, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int packed_lds_bytes(int a_fmt, int b_fmt) {
+int packed_lds_bytes(int a_fmt, int b_fmt, int bs) {
   auto pitch = [](int f) { return f == 4 ? 80 : 104; };
-  return 2 * (kBM * pitch(a_fmt) + kBN * pitch(b_fmt)) + 2 * (kBM + kBN) * 4;
+  return 2 * bs * (pitch(a_fmt) + pitch(b_fmt)) + 2 * 2 * bs * 4;
 }
 
 hipError_t launch_gemm_mx_packed(const GemmArgs& g, int64_t grid, int a_fmt, int b_fmt, bool bounds,
-                                 hipStream_t s) {
+                                 int bs, hipStream_t s) {
   switch (a_fmt) {
-    case 2: return launch_pk_b<2>(g, grid, b_fmt, bounds, s);
-    case 3: return launch_pk_b<3>(g, grid, b_fmt, bounds, s);
-    case 4: return launch_pk_b<4>(g, grid, b_fmt, bounds, s);
+    case 2: return launch_pk_b<2>(g, grid, b_fmt, bounds, bs, s);
+    case 3: return launch_pk_b<3>(g, grid, b_fmt, bounds, bs, s);
+    case 4: return launch_pk_b<4>(g, grid, b_fmt, bounds, bs, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -116,11 +116,11 @@ GemmConfig choose_gemm_fp8(int64_t M, int64_t N, int64_t K, bool scaled);
 hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int a_dtype,
                            int b_dtype, bool bounds, bool scaled, int bs, hipStream_t s);
 // Block-scaled GEMM with 6- and 4-bit packed K-contiguous operands (MFMA format codes
-// a_fmt, b_fmt: 2 = e2m3, 3 = e3m2, 4 = e2m1) on 128x128 blocks of 256 threads; grid =
-// ceil(M/128)·ceil(N/128); bounds: M or N not a multiple of 128.
+// a_fmt, b_fmt: 2 = e2m3, 3 = e3m2, 4 = e2m1) on bs x bs blocks (128: 256 threads, 256: 512);
+// grid = ceil(M/bs)·ceil(N/bs); bounds: M or N not a multiple of bs.
 hipError_t launch_gemm_mx_packed(const GemmArgs& g, int64_t grid, int a_fmt, int b_fmt, bool bounds,
-                                 hipStream_t s);
-int packed_lds_bytes(int a_fmt, int b_fmt);
+                                 int bs, hipStream_t s);
+int packed_lds_bytes(int a_fmt, int b_fmt, int bs);
 
 // 16-bit direct-load GEMM on bs x bs blocks (256 or 128).
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
