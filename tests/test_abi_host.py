@@ -481,3 +481,21 @@ def test_packed_mx_plan():
     p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None, D_ADDR,
                              4096, 3840, 640, 0, 1, 0.0, tg.TG_FP4_E2M1, tg.TG_FP4_E2M1)
     assert (p.block_m, p.threads, p.grid, p.bounds_checked) == (128, 256, 32 * 30, 0)
+
+
+@pytest.mark.parametrize("M,N,K,bs", [(4096, 4112, 1024, 256), (8192, 8192, 8192, 256),
+                                      (1024, 1040, 512, 128), (144, 208, 256, 128)])
+def test_packed_fp4_direct_plan(M, N, K, bs):
+    # e2m1 x e2m1 with K % 256 == 0: the direct-load kernel, 256-K stages, block size as fp8
+    p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None, D_ADDR,
+                             M, N, K, 0, 1, 0.0, tg.TG_FP4_E2M1, tg.TG_FP4_E2M1)
+    assert (p.kernel, p.block_m, p.block_n, p.block_k, p.threads, p.loader) == (
+        tg.TG_GEMM_TILED, bs, bs, 256, 512, 1)
+    assert p.grid == ((M + bs - 1) // bs) * ((N + bs - 1) // bs)
+    assert p.bounds_checked == int(M % bs != 0 or N % bs != 0)
+    assert p.lds_bytes == 4 * bs * 128 + 3 * 2 * 260 * (bs // 16)
+    # the same shape with K % 256 != 0, or a 6-bit operand, stays on the packed kernel
+    for k, bf in ((K + 128, tg.TG_FP4_E2M1), (K, tg.TG_FP6_E2M3)):
+        q = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None,
+                                 D_ADDR, M, N, k, 0, 1, 0.0, tg.TG_FP4_E2M1, bf)
+        assert (q.block_k, q.loader) == (128, 0)

@@ -73,6 +73,22 @@ def test_large_blocks(M, N, K, af, bf, beta):
     full_check(M, N, K, af, bf, beta, M + K)
 
 
+# e2m1 x e2m1 with K % 256 == 0 runs the direct-load kernel: one, an even and an odd number of
+# 256-K stages, 128- and 256-wide blocks, whole and ragged, beta 0 and 1
+@pytest.mark.parametrize("M,N,K,beta", [(144, 208, 256, 1.0), (256, 384, 512, 0.0),
+                                        (400, 272, 768, 1.0), (1024, 1040, 1280, 0.0),
+                                        (4096, 4096, 512, 0.0), (4112, 4096, 768, 1.0),
+                                        (4096, 4352, 256, 1.0), (4352, 4240, 1024, 0.0)])
+def test_fp4_direct(M, N, K, beta):
+    say(f"gemm_mx e2m1 direct {M}x{N}x{K} beta={beta}")
+    full_check(M, N, K, "e2m1", "e2m1", beta, M + N + K, dist="normal", scale_range=(100, 154))
+
+
+def test_fp4_direct_in_place_and_codes():
+    say("gemm_mx e2m1 direct in place C == D, every code")
+    full_check(512, 768, 1536, "e2m1", "e2m1", 1.0, 53, c_is_d=True)
+
+
 @pytest.mark.parametrize("af", ["e2m1", "e2m3"])
 def test_normal_data_and_wide_scales(af):
     # N(0,1) rounded to the format, scales over 2^-60 .. 2^60

@@ -11,9 +11,12 @@
 //    LDS swizzle is applied on the global side: lane i fetches the logical 16-byte chunk
 //    that belongs at physical slot i.
 //  * one K stage is one 128-byte row of K per operand row: 64 K of a 16-bit operand, 128 K of
-//    an fp8 operand.  Both formats therefore share the LDS geometry, the DMA pattern and the
-//    bytes per stage; a stage is 4 MFMA K steps of 16 (v_mfma_f32_32x32x16_{f16,bf16}) or 2
-//    of 64 (v_mfma_f32_32x32x64_f8f6f4), the same MFMA cycles either way.
+//    an fp8 operand, 256 K of a packed e2m1 operand.  All formats therefore share the LDS
+//    geometry, the DMA pattern and the bytes per stage; a stage is 4 MFMA K steps of 16
+//    (v_mfma_f32_32x32x16_{f16,bf16}), 2 of 64 (v_mfma_f32_32x32x64_f8f6f4, fp8) or 4 of 64
+//    (the same instruction with e2m1 operands, which takes half the fp8 cycles), the same MFMA
+//    cycles per stage in every case.  An e2m1 lane carries 16 bytes (32 K) per step, like a
+//    16-bit lane, so e2m1 stages take the 16-bit fragment reads.
 //  * K-contiguous operands (A without transA, B with transB) keep [rows][128 bytes] stages
 //    (chunk XOR row bits) and are read as fragments with ds_read_b128: one per 16-bit
 //    fragment, two per fp8 fragment (32 bytes of K per lane).
@@ -66,17 +69,21 @@ constexpr int kGroupM = 8;       // tile-rows per scheduling group (measured: 8 
 
 // Format codes of the template's DT parameter: TG_F16 / TG_BF16, an fp8 pair kF8 + 2·a + b,
 // or a block-scaled fp8 pair kMX + 2·a + b, with a, b the MFMA's operand format codes
-// (0 = e4m3, 1 = e5m2).
-constexpr int kF8 = 16, kMX = 32;
+// (0 = e4m3, 1 = e5m2); kP4: a block-scaled e2m1 pair, both operands K-contiguous packed rows
+// (value k of a row at bits [4k, 4k + 4) of its bytes).
+constexpr int kF8 = 16, kMX = 32, kP4 = 64;
 constexpr int fp8_code(int a_fmt, int b_fmt) { return kF8 + 2 * a_fmt + b_fmt; }
 constexpr int mx_code(int a_fmt, int b_fmt) { return kMX + 2 * a_fmt + b_fmt; }
 
+// Addressing unit: one element of a 16-bit or fp8 operand, one byte (two values) of e2m1.
 template <int DT>
 struct Elem {
-  static constexpr bool kFp8 = DT >= kF8;
+  static constexpr bool kFp4 = DT == kP4;
+  static constexpr bool kFp8 = DT >= kF8 && !kFp4;
   static constexpr bool kScaled = DT >= kMX;      // E8M0 scale per 32 K of each row / column
-  static constexpr int kBytes = kFp8 ? 1 : 2;
-  static constexpr int kBK = kRowBytes / kBytes;   // K elements per stage
+  static constexpr int kBytes = kFp8 || kFp4 ? 1 : 2;   // bytes per addressing unit
+  static constexpr int kPer = kFp4 ? 2 : 1;        // K values per addressing unit
+  static constexpr int kBK = kRowBytes / kBytes;   // addressing units per stage
   static constexpr int kSteps = kFp8 ? 2 : 4;      // MFMA K steps per stage
   static constexpr int kParts = kFp8 ? 2 : 1;      // 16-byte K-major reads per fragment
   using Frag = typename std::conditional<kFp8, u32x8, u32x4>::type;
@@ -105,6 +112,19 @@ __device__ __forceinline__ f32x16 mfma32s(F a, F b, f32x16 c, uint32_t sa, uint3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
       __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, (DT & 3) >> 1, DT & 1,
       OPSEL, (int)sa, OPSEL, (int)sb);
+}
+
+// Block-scaled e2m1 MFMA (format code 4 for both operands): lane l carries the 32
+// consecutive K of block l / 32 of the 64-K step for row / column l % 32, as 16 packed bytes
+// in the low half of the 8-register operand, and that block's scale is the byte OPSEL selects
+// from the lane's own scale register (measured on gfx950 with an in-bounds probe).  The
+// compiler passes only the four low registers for this format.
+template <int OPSEL>
+__device__ __forceinline__ f32x16 mfma32p4(u32x4 a, u32x4 b, f32x16 c, uint32_t sa, uint32_t sb) {
+  const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, OPSEL, (int)sa, OPSEL,
+                                                         (int)sb);
 }
 
 // ---- LDS layouts --------------------------------------------------------------------
@@ -420,8 +440,10 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   constexpr bool TAIL = (KS & kTail) != 0;
   static_assert(PER % 2 == 0 && TM >= 1 && TN >= 1 && TM <= 4 && TN <= 4, "wave grid");
   static_assert(!TAIL || !EL::kFp8, "a partial last stage is served for 16-bit operands");
+  static_assert(!TAIL || !EL::kFp4, "a partial last stage is served for 16-bit operands");
+  static_assert(!EL::kFp4 || (!A_MN && !B_MN), "e2m1 operands are K-contiguous");
   static_assert(BS == 256 || BS == 128, "block size");
-  // block-scaled fp8: a group of four stages' scales holds BS rows x 16 bytes per operand in
+  // block-scaled fp8 (e2m1): a group of four (two) stages' scales holds BS rows x 16 bytes per operand in
   // blocks of 16 rows, each block 4 bytes longer than its 256 bytes (QB), so that rows r and
   // r + 16 start in different banks; QH: B's offset in a group; QG: a group's bytes; QR: rows
   // per operand in a quarter of a group
@@ -449,8 +471,10 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = (wave / WGN) * WM, wn = (wave % WGN) * WN;
 
-  const int64_t lda = A_MN ? g.M : g.K;
-  const int64_t ldb = B_MN ? g.N : g.K;
+  // K in addressing units (bytes of a packed e2m1 row)
+  const int64_t Kx = g.K / EL::kPer;
+  const int64_t lda = A_MN ? g.M : Kx;
+  const int64_t ldb = B_MN ? g.N : Kx;
   using OA = Operand<A_MN, TM, PER, DT, BS>;
   using OB = Operand<B_MN, TN, PER, DT, BS>;
   OA oa;
@@ -458,10 +482,10 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   oa.init(lda, wm, wave, lane);
   ob.init(ldb, wn, wave, lane);
   // operand panels of this block at K stage 0, and the per-stage advance in bytes
-  const int64_t a0 = A_MN ? (int64_t)m0 : (int64_t)m0 * g.K;
-  const int64_t b0 = B_MN ? (int64_t)n0 : (int64_t)n0 * g.K;
-  oa.bind((const uint8_t*)g.A + a0 * E, ((int64_t)g.M * g.K - a0) * E);
-  ob.bind((const uint8_t*)g.B + b0 * E, ((int64_t)g.K * g.N - b0) * E);
+  const int64_t a0 = A_MN ? (int64_t)m0 : (int64_t)m0 * Kx;
+  const int64_t b0 = B_MN ? (int64_t)n0 : (int64_t)n0 * Kx;
+  oa.bind((const uint8_t*)g.A + a0 * E, ((int64_t)g.M * Kx - a0) * E);
+  ob.bind((const uint8_t*)g.B + b0 * E, (Kx * g.N - b0) * E);
   const uint32_t adv_a = A_MN ? (uint32_t)(BK * g.M * E) : (uint32_t)(BK * E);
   const uint32_t adv_b = B_MN ? (uint32_t)(BK * g.N * E) : (uint32_t)(BK * E);
 
@@ -472,10 +496,12 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
   auto mfmas = [&](const Frag (&a)[TM], const Frag (&b)[TN]) {
+    if constexpr (!EL::kFp4) {   // e2m1 stages use mfmas_p4
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<DT>(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32<DT>(a[i], b[j], acc[i][j]);
+    }
   };
 
   // Pipeline (K stage kt in buffer `cur`, kt+1 already loading into `nxt`):
@@ -485,9 +511,9 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   //   then step NS-1's MFMAs (operands already in registers) overlap the reads of stage
   //   kt+1's first fragments and the DMA of stage kt+2 into `cur`.
   // The last two stages are peeled off the loop so the steady-state body is branch free.
-  const int KT = TAIL ? (g.K + BK - 1) / BK : g.K / BK;   // >= 1, of shape KSH
+  const int KT = TAIL ? (int)((Kx + BK - 1) / BK) : (int)(Kx / BK);   // >= 1, of shape KSH
   // valid bytes of each K row in stage s: all 128 but in a partial last stage
-  const uint32_t krem = (uint32_t)(g.K - (KT - 1) * BK) * E;
+  const uint32_t krem = (uint32_t)(Kx - (int64_t)(KT - 1) * BK) * E;
   auto lim = [&](int s) -> uint32_t { return s == KT - 1 ? krem : (uint32_t)kRowBytes; };
   auto load_ab = [&](uint32_t s, uint8_t* stage_a, uint8_t* stage_b) {
     oa.template load<TAIL>(s * adv_a, lda, stage_a, wave, lim((int)s));
@@ -496,7 +522,9 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
 
   // Block scales (scaled fp8): K/32 bytes per row, 4 per 128-K stage.  They travel in groups
   // of four stages, 16 bytes per row, into a ring of three LDS group buffers ([row][16 bytes],
-  // A's BS rows then B's).  Stage kt loads quarter kt % 4 of group kt/4 + 2: rows QR·q ..
+  // A's BS rows then B's).  (e2m1: 8 bytes per 256-K stage, groups of two stages; stage kt
+  // loads quarters 2(kt % 2) and 2(kt % 2) + 1 of group kt/2 + 2, and the timing argument
+  // below holds with stages counted in pairs.)  Stage kt loads quarter kt % 4 of group kt/4 + 2: rows QR·q ..
   // QR·q + QR-1 of A (waves 0-3, 16 rows each) and of B (waves 4-7), four lanes per row with
   // 4 bytes each, so the lanes of a row share one cache line — 128 lines per stage on 256-wide
   // blocks, where one 4-byte load per row and stage took 512.  On 128-wide blocks a quarter
@@ -523,10 +551,18 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void*)(qg + (G % 3u) * QG + qlds + QB * (QR / 16) * q),
                                                4, qvoff, QR * q * qkb + 16u * G, 0, 0);
   };
-  auto qroll = [&](int kt) { qload_part((uint32_t)(kt >> 2) + 2u, (uint32_t)(kt & 3)); };
-  // stage kt's 4 scale bytes of row 0 in the ring
+  auto qroll = [&](int kt) {
+    if constexpr (EL::kFp4) {
+      qload_part((uint32_t)(kt >> 1) + 2u, 2u * (uint32_t)(kt & 1));
+      qload_part((uint32_t)(kt >> 1) + 2u, 2u * (uint32_t)(kt & 1) + 1u);
+    } else {
+      qload_part((uint32_t)(kt >> 2) + 2u, (uint32_t)(kt & 3));
+    }
+  };
+  // stage kt's scale bytes (4, e2m1: 8) of row 0 in the ring
   auto qstage = [&](int kt) -> const uint8_t* {
-    return qg + ((uint32_t)(kt >> 2) % 3u) * QG + 4u * (uint32_t)(kt & 3);
+    if constexpr (EL::kFp4) return qg + ((uint32_t)(kt >> 1) % 3u) * QG + 8u * (uint32_t)(kt & 1);
+    else return qg + ((uint32_t)(kt >> 2) % 3u) * QG + 4u * (uint32_t)(kt & 3);
   };
   // This lane's scales of one stage for A tile i / B tile j, shifted so that byte 2s holds
   // the block of K step s this lane supplies (K half lane / 32).  One per-lane LDS offset per
@@ -551,6 +587,24 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
       for (int j = 0; j < TN; ++j) qb[j] = qread_b(q, j);
     }
   };
+  // e2m1: a stage holds blocks 0..7 of each row (8 bytes); lane half h supplies block 2s + h
+  // in K step s, so one register per tile carries this lane's four (bytes h, 2+h, 4+h, 6+h,
+  // gathered with v_perm) and step s's MFMA selects byte s.
+  const uint32_t psel = (lane >> 5) ? 0x07050301u : 0x06040200u;
+  auto qread_p4 = [&](const uint8_t* q) {
+    if constexpr (EL::kFp4) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint8_t* p = q + qoa + 2 * QB * i;
+        qa[i] = __builtin_amdgcn_perm(*(const uint32_t*)(p + 4), *(const uint32_t*)p, psel);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint8_t* p = q + qob + 2 * QB * j;
+        qb[j] = __builtin_amdgcn_perm(*(const uint32_t*)(p + 4), *(const uint32_t*)p, psel);
+      }
+    }
+  };
 
   load_ab(0u, sa0, sb0);
   if constexpr (EL::kScaled) {
@@ -564,12 +618,22 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   Frag a[TM], b[TN], an[TM], bn[TN];
   oa.frags(sa0, 0, a);
   ob.frags(sb0, 0, b);
-  qread(qstage(0));
+  if constexpr (EL::kFp4) qread_p4(qstage(0));
+  else qread(qstage(0));
   if constexpr (KSH != kSingle) load_ab(1u, sa1, sb1);
 
   constexpr int kMfma = TM * TN;
   constexpr int kReads = OA::kReads + OB::kReads;
-  constexpr int kDma = 2 * PER + (EL::kScaled ? 1 : 0);
+  constexpr int kDma = 2 * PER + (EL::kFp4 ? 2 : EL::kScaled ? 1 : 0);
+
+  // e2m1 MFMAs of K step S: scale byte S of the gathered registers
+  auto mfmas_p4 = [&](auto S) {
+    constexpr int st = decltype(S)::value;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32p4<st>(a[i], b[j], acc[i][j], qa[i], qb[j]);
+  };
 
   // fp8 K step in place: this step's MFMAs, tile by tile of A, while the next step's
   // fragments (K step `sn` of stages `xa` / `xb`) are read — B's into bn, A tile i's into
@@ -615,6 +679,46 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   // the next stage's first fragments (false only for the last stage).
   auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, int kt, auto dma,
                    auto next) {
+    if constexpr (EL::kFp4) {
+      // steps 0..2 read step s+1's fragments; the last step, after the barrier, reads the
+      // next stage's first fragments and its scales
+      constexpr bool kNext = decltype(next)::value;
+      auto step = [&](auto S) {
+        constexpr int st = decltype(S)::value;
+        oa.frags(ca, st + 1, an);
+        ob.frags(cb, st + 1, bn);
+        mfmas_p4(S);
+        interleave<kMfma, kReads, 0>();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) a[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = bn[j];
+      };
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if constexpr (kNext) {
+        oa.frags(na, 0, an);
+        ob.frags(nb_, 0, bn);
+      }
+      if constexpr (decltype(dma)::value) {
+        load_ab((uint32_t)(kt + 2), ca, cb);
+        qroll(kt);
+      }
+      mfmas_p4(std::integral_constant<int, 3>{});
+      if constexpr (kNext) qread_p4(qstage(kt + 1));
+      constexpr int nr = kNext ? kReads + 2 * (TM + TN) : 0;
+      if constexpr (decltype(dma)::value) interleave<kMfma, nr, kDma>();
+      else if constexpr (kNext) interleave<kMfma, nr, 0>();
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = bn[j];
+      return;
+    }
     if constexpr (EL::kFp8) {
       static_assert(NS == 2, "fp8 stages are two 64-K steps");
       step_inplace(ca, cb, 1, std::true_type{}, std::false_type{}, std::integral_constant<int, 0>{},

@@ -121,6 +121,9 @@ hipError_t launch_gemm_fp8(const GemmArgs& g, int64_t grid, int trans_a, int tra
 hipError_t launch_gemm_mx_packed(const GemmArgs& g, int64_t grid, int a_fmt, int b_fmt, bool bounds,
                                  int bs, hipStream_t s);
 int packed_lds_bytes(int a_fmt, int b_fmt, int bs);
+// Block-scaled e2m1 x e2m1 GEMM on the direct-load kernel (A [M][K/2], B [N][K/2] packed rows,
+// K % 256 == 0), bs x bs blocks (256 or 128) of 512 threads; grid = ceil(M/bs)·ceil(N/bs).
+hipError_t launch_fp4_direct(const GemmArgs& g, int64_t grid, bool bounds, int bs, hipStream_t s);
 
 // 16-bit direct-load GEMM on bs x bs blocks (256 or 128).
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
