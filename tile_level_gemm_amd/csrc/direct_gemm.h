@@ -568,6 +568,7 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   // the block of K step s this lane supplies (K half lane / 32).  One per-lane LDS offset per
   // operand; tiles are immediates.
   uint32_t qa[TM], qb[TN], qbn[TN];
+  uint32_t qan[TM], qbn2[TN];   // e2m1: the next stage's scales, read one step before its barrier
   const uint32_t qsh = 8u * (uint32_t)(lane >> 5);
   // row r of an operand's group: block r / 16, 16 bytes per row within it; tiles are 32 rows
   // (two blocks) apart
@@ -591,17 +592,17 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   // in K step s, so one register per tile carries this lane's four (bytes h, 2+h, 4+h, 6+h,
   // gathered with v_perm) and step s's MFMA selects byte s.
   const uint32_t psel = (lane >> 5) ? 0x07050301u : 0x06040200u;
-  auto qread_p4 = [&](const uint8_t* q) {
+  auto qread_p4 = [&](const uint8_t* q, uint32_t (&xa)[TM], uint32_t (&xb)[TN]) {
     if constexpr (EL::kFp4) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const uint8_t* p = q + qoa + 2 * QB * i;
-        qa[i] = __builtin_amdgcn_perm(*(const uint32_t*)(p + 4), *(const uint32_t*)p, psel);
+        xa[i] = __builtin_amdgcn_perm(*(const uint32_t*)(p + 4), *(const uint32_t*)p, psel);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const uint8_t* p = q + qob + 2 * QB * j;
-        qb[j] = __builtin_amdgcn_perm(*(const uint32_t*)(p + 4), *(const uint32_t*)p, psel);
+        xb[j] = __builtin_amdgcn_perm(*(const uint32_t*)(p + 4), *(const uint32_t*)p, psel);
       }
     }
   };
@@ -618,7 +619,7 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   Frag a[TM], b[TN], an[TM], bn[TN];
   oa.frags(sa0, 0, a);
   ob.frags(sb0, 0, b);
-  if constexpr (EL::kFp4) qread_p4(qstage(0));
+  if constexpr (EL::kFp4) qread_p4(qstage(0), qa, qb);
   else qread(qstage(0));
   if constexpr (KSH != kSingle) load_ab(1u, sa1, sb1);
 
@@ -680,15 +681,18 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   auto stage = [&](uint8_t* ca, uint8_t* cb, const uint8_t* na, const uint8_t* nb_, int kt, auto dma,
                    auto next) {
     if constexpr (EL::kFp4) {
-      // steps 0..2 read step s+1's fragments; the last step, after the barrier, reads the
-      // next stage's first fragments and its scales
+      // steps 0..2 read step s+1's fragments, step 2 also the next stage's scales (its group
+      // landed stages ago); the last step, after the barrier, reads the next stage's first
+      // fragments.  Reading the scales after the barrier instead left them on the path to the
+      // next stage's first MFMAs: 8 % slower at 8192^3.
       constexpr bool kNext = decltype(next)::value;
       auto step = [&](auto S) {
         constexpr int st = decltype(S)::value;
         oa.frags(ca, st + 1, an);
         ob.frags(cb, st + 1, bn);
         mfmas_p4(S);
-        interleave<kMfma, kReads, 0>();
+        if constexpr (st == 2 && kNext) qread_p4(qstage(kt + 1), qan, qbn2);
+        interleave<kMfma, kReads + (st == 2 && kNext ? 2 * (TM + TN) : 0), 0>();
 #pragma unroll
         for (int i = 0; i < TM; ++i) a[i] = an[i];
 #pragma unroll
@@ -709,14 +713,19 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
         qroll(kt);
       }
       mfmas_p4(std::integral_constant<int, 3>{});
-      if constexpr (kNext) qread_p4(qstage(kt + 1));
-      constexpr int nr = kNext ? kReads + 2 * (TM + TN) : 0;
+      constexpr int nr = kNext ? kReads : 0;
       if constexpr (decltype(dma)::value) interleave<kMfma, nr, kDma>();
       else if constexpr (kNext) interleave<kMfma, nr, 0>();
 #pragma unroll
       for (int i = 0; i < TM; ++i) a[i] = an[i];
 #pragma unroll
       for (int j = 0; j < TN; ++j) b[j] = bn[j];
+      if constexpr (kNext) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) qa[i] = qan[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) qb[j] = qbn2[j];
+      }
       return;
     }
     if constexpr (EL::kFp8) {
