@@ -460,6 +460,22 @@ def main():
             call = lambda: tg.tile_gemm_fp8(Ax, Bx, None, Dx, m_, n_, k_, 0, 1, 0.0, e4, e4)  # noqa: E731
         other_run[tag] = (batched(call, groups=5), plan.block_m, Dx)
         del Ax, Bx
+
+    # context, not this library: the vendor GEMM (torch.mm -> hipBLASLt) on the headline's
+    # operands, bf16 in, fp32 out, timed the same way; its result is compared with ours after
+    # the timed steps
+    print("bench: library GEMM (context)", file=sys.stderr, flush=True)
+    lib_ctx = {}
+    Ab, Bb = A.view(torch.bfloat16), B.view(torch.bfloat16)
+    try:
+        Dl = torch.mm(Ab, Bb, out_dtype=torch.float32)
+        lib_out = "fp32"
+    except (RuntimeError, TypeError):
+        Dl = torch.mm(Ab, Bb)
+        lib_out = "bf16"
+    lib_ms = per_launch(lambda: torch.mm(Ab, Bb, out_dtype=torch.float32) if lib_out == "fp32"
+                        else torch.mm(Ab, Bb))
+    lib_ctx = {"lst": lib_ms, "out": lib_out, "D": Dl}
     gpu_legs_s = time.perf_counter() - t_gpu
 
     # ---- 3. the headline steps: W warm-up steps, then K timed steps -------------------------
@@ -498,6 +514,12 @@ def main():
                       per_group=max(5, args.steps // 2), warm=1)
     bb_ms = float(np.mean(bb_list))
     bb_gbs = copy_bytes / (bb_ms * 1e-3) / 1e9
+    # context: the runtime's own device-to-device copy of the same 512 MiB, back to back
+    # (into a buffer of its own: T is checked against S below)
+    T3 = torch.empty_like(S)
+    rt_list = batched(lambda: T3.copy_(S), groups=5, per_group=max(5, args.steps // 2), warm=1)
+    rt_gbs = copy_bytes / (float(np.mean(rt_list)) * 1e-3) / 1e9
+    del T3
 
     def hbm_leg(lst, nbytes, traffic_key, parity, workload):
         ms = float(np.mean(lst))
@@ -521,6 +543,8 @@ def main():
     ref, bound = og.gemm_ref_at(gin[0], gin[1], None, M, N, K, False, False, 0.0, "bf16", rows, cols)
     g_ok, g_worst = og.check(D.cpu().numpy()[rows, cols], ref, bound)
     c_ok = bool(torch.equal(S, T))
+    lib_diff = round(float((lib_ctx["D"].float() - D).abs().max()), 6)
+    del lib_ctx["D"]
     for beta, (a, b, c) in atoms_in.items():
         ok, worst = og.check(small_out[beta].cpu().numpy(),
                              og.gemm_ref(a, b, c, 16, 8, 16, False, False, beta, "f16"),
@@ -643,7 +667,18 @@ def main():
                              "frac": round(bb_gbs / PEAK_HBM_GBS, 4),
                              "note": "the same copy launched back to back after the timed steps "
                                      "(5 batches); value above is each step's copy, right after its GEMM"},
+            "runtime_copy": {"value": round(rt_gbs, 2), "unit": "GB/s", **_stats(rt_list),
+                             "frac": round(rt_gbs / PEAK_HBM_GBS, 4),
+                             "note": "context, not this library: torch copy_ (the HIP runtime's "
+                                     "device-to-device copy kernel) of the same 512 MiB, back to back"},
         },
+        "library_gemm_context": {
+            "value": round(flops / (float(np.mean(lib_ctx["lst"])) * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            **_stats(lib_ctx["lst"]),
+            "frac": round(flops / (float(np.mean(lib_ctx["lst"])) * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "max_abs_diff_vs_tile_gemm": lib_diff,
+            "note": f"context, not this library: torch.mm (hipBLASLt) on the same 8192^3 bf16 operands, "
+                    f"{lib_ctx['out']} out, per-launch HIP events"},
         "small_configs": small,
         "gemm_f16_transA_beta1": mfma_leg(
             h_ms, PEAK_MFMA_TFLOPS, "gemm_direct_256x256_f16_transA_beta1",
