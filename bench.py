@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "mx": ("gemm_mx_kk.hip", "gemm_fp8_launch.h", "direct_gemm.h", "tg_internal.h"),
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
     "packed": ("gemm_mx_packed.hip", "tg_internal.h"),
+    "fp4": ("gemm_mx_fp4.hip", "direct_gemm.h", "tg_internal.h"),
     "frag": ("frag_kernels.hip", "tg_internal.h"),
     "async": ("async_copy.hip", "lds_layout.h", "tg_internal.h"),
 }
@@ -94,8 +95,8 @@ TRAFFIC_KERNELS = {
                                  2 * M * K + M * N * 4),
     "gemm_mx_256x256_e4m3_tn": ("gemm_direct<false, false, 32, 2, 4, false, 0>", "mx",
                                 2 * M * K + 2 * M * (K // 32) + M * N * 4),
-    "gemm_mx_packed_256x256_e2m1": ("gemm_mx_packed<4, 4, false, 256>", "packed",
-                                    2 * M * K // 2 + 2 * M * (K // 32) + M * N * 4),
+    "gemm_mx_256x256_e2m1_tn": ("gemm_direct<false, false, 64, 2, 4, false, 0>", "fp4",
+                                2 * M * K // 2 + 2 * M * (K // 32) + M * N * 4),
     "gemm_mx_packed_256x256_e2m3": ("gemm_mx_packed<2, 2, false, 256>", "packed",
                                     2 * M * K * 6 // 8 + 2 * M * (K // 32) + M * N * 4),
     "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4, 4, 128>", "copy", 2 * ROWS * COLS * 2),
@@ -586,7 +587,8 @@ def main():
         p_ok, p_worst = og.check_fp8(gotp, refp, boundp, pa_, pb_, M, N, K, False, True, f, f, rows, cols,
                                      sa_bits=sa_, sb_bits=sb_)
         small_legs[f"gemm_mx_{f}_tn"] = mfma_leg(
-            lst, PEAK_FP4_TFLOPS, f"gemm_mx_packed_256x256_{f}",
+            lst, PEAK_FP4_TFLOPS,
+            "gemm_mx_256x256_e2m1_tn" if f == "e2m1" else f"gemm_mx_packed_256x256_{f}",
             {"sampled_ok": bool(p_ok), "worst_err_over_tol": round(p_worst, 5),
              "worst_err_over_16bit_tol": round(og.check(gotp, refp, boundp)[1], 5)},
             f"tile_gemm_mx 8192x8192x8192, A {f} [M,K] and B {f} [N,K] packed rows, N(0,1) rounded "
