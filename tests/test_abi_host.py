@@ -485,6 +485,22 @@ def test_packed_mx_plan():
 
 @pytest.mark.parametrize("M,N,K,bs", [(4096, 4112, 1024, 256), (8192, 8192, 8192, 256),
                                       (1024, 1040, 512, 128), (144, 208, 256, 128)])
+def test_packed_fp6_direct_plan(M, N, K, bs):
+    # two 6-bit operands: the direct-load kernel, 128-K stages of 96-byte rows, block size as fp8
+    for af, bf in ((tg.TG_FP6_E2M3, tg.TG_FP6_E2M3), (tg.TG_FP6_E3M2, tg.TG_FP6_E2M3)):
+        p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None,
+                                 D_ADDR, M, N, K + 128, 0, 1, 0.0, af, bf)
+        assert (p.kernel, p.block_m, p.block_k, p.threads, p.loader) == (tg.TG_GEMM_TILED, bs, 128, 512, 1)
+        assert p.grid == ((M + bs - 1) // bs) * ((N + bs - 1) // bs)
+        assert p.lds_bytes == 4 * bs * 128 + 3 * 2 * 260 * (bs // 16)
+    # a 6-bit operand with an e2m1 one stays on the packed kernel
+    q = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None, D_ADDR,
+                             M, N, K, 0, 1, 0.0, tg.TG_FP6_E3M2, tg.TG_FP4_E2M1)
+    assert (q.block_k, q.loader) == (128, 0)
+
+
+@pytest.mark.parametrize("M,N,K,bs", [(4096, 4112, 1024, 256), (8192, 8192, 8192, 256),
+                                      (1024, 1040, 512, 128), (144, 208, 256, 128)])
 def test_packed_fp4_direct_plan(M, N, K, bs):
     # e2m1 x e2m1 with K % 256 == 0: the direct-load kernel, 256-K stages, block size as fp8
     p = tg.tile_gemm_mx_plan(A_ADDR, B_ADDR, A_ADDR + (1 << 28), B_ADDR + (1 << 28), None, D_ADDR,

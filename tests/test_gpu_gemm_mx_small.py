@@ -84,6 +84,26 @@ def test_fp4_direct(M, N, K, beta):
     full_check(M, N, K, "e2m1", "e2m1", beta, M + N + K, dist="normal", scale_range=(100, 154))
 
 
+# two 6-bit operands run the direct-load kernel: one, an even and an odd number of 128-K stages,
+# 128- and 256-wide blocks, whole and ragged, beta 0 and 1, every pair of the two types
+@pytest.mark.parametrize("M,N,K,af,bf,beta", [(144, 208, 128, "e2m3", "e2m3", 1.0),
+                                              (256, 384, 256, "e3m2", "e3m2", 0.0),
+                                              (400, 272, 384, "e2m3", "e3m2", 1.0),
+                                              (1024, 1040, 640, "e3m2", "e2m3", 0.0),
+                                              (4096, 4096, 256, "e2m3", "e2m3", 0.0),
+                                              (4112, 4096, 384, "e3m2", "e2m3", 1.0),
+                                              (4096, 4352, 128, "e2m3", "e3m2", 1.0),
+                                              (4352, 4240, 512, "e3m2", "e3m2", 0.0)])
+def test_fp6_direct(M, N, K, af, bf, beta):
+    say(f"gemm_mx 6-bit direct {M}x{N}x{K} {af} x {bf} beta={beta}")
+    full_check(M, N, K, af, bf, beta, M + N + K + 1, dist="normal", scale_range=(100, 154))
+
+
+def test_fp6_direct_in_place_and_codes():
+    say("gemm_mx 6-bit direct in place C == D, every code")
+    full_check(512, 768, 1152, "e3m2", "e2m3", 1.0, 57, c_is_d=True)
+
+
 def test_fp4_direct_in_place_and_codes():
     say("gemm_mx e2m1 direct in place C == D, every code")
     full_check(512, 768, 1536, "e2m1", "e2m1", 1.0, 53, c_is_d=True)

@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["abi.cpp", "plan.cpp", "copy_kernels.hip", "gemm_kernels.hip", "gemm_direct.hip",
            "gemm_direct_kk.hip", "gemm_direct_km.hip", "gemm_direct_mk.hip", "gemm_direct_mm.hip",
            "gemm_fp8.hip", "gemm_fp8_km.hip", "gemm_fp8_mk.hip", "gemm_fp8_mm.hip",
-           "gemm_mx_kk.hip", "gemm_mx_km.hip", "gemm_mx_mk.hip", "gemm_mx_mm.hip", "gemm_mx_packed.hip", "gemm_mx_fp4.hip",
+           "gemm_mx_kk.hip", "gemm_mx_km.hip", "gemm_mx_mk.hip", "gemm_mx_mm.hip", "gemm_mx_packed.hip", "gemm_mx_fp4.hip", "gemm_mx_fp6.hip",
            "frag.cpp", "frag_kernels.hip", "async_copy.hip"]
 
 # -packed-fp32-ops: no v_pk_*_f32 in generated code (the device pass honours it; the

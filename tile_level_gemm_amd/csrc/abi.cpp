@@ -190,11 +190,12 @@ int validate_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint
   return TG_OK;
 }
 
-// 6- / 4-bit block-scaled GEMM.  e2m1 x e2m1 with K a multiple of 256: the direct-load kernel
-// (256-K stages of 128-byte rows, DMA into LDS), block size as for fp8.  Otherwise the packed
-// kernel, 128-K stages: 256x256 blocks of 512 threads (8 waves of 128x64) when there are at
-// least 256 of them (as for the 16-bit kernel), else 128x128 blocks of 256 threads (4 waves of
-// 64x64).
+// 6- / 4-bit block-scaled GEMM.  The direct-load kernel (DMA into LDS, block size as for fp8)
+// takes e2m1 x e2m1 with K a multiple of 256 (256-K stages of 128-byte rows) and every pair of
+// 6-bit operands (128-K stages of 96-byte rows).  The packed kernel takes the rest (a 6-bit
+// operand with an e2m1 one, e2m1 with K % 256 != 0), 128-K stages: 256x256 blocks of 512
+// threads (8 waves of 128x64) when there are at least 256 of them (as for the 16-bit kernel),
+// else 128x128 blocks of 256 threads (4 waves of 64x64).
 GemmConfig choose_gemm_packed(int64_t M, int64_t N, int64_t K, int a_dtype, int b_dtype) {
   GemmConfig c{};
   if (M == 0 || N == 0) {
@@ -213,6 +214,7 @@ GemmConfig choose_gemm_packed(int64_t M, int64_t N, int64_t K, int a_dtype, int 
     c.bk = 256;
     return c;
   }
+  if (a_dtype != TG_FP4_E2M1 && b_dtype != TG_FP4_E2M1) return choose_gemm_fp8(M, N, K, true);
   const int bs = blocks(256) >= 256 ? 256 : 128;
   c.kernel = TG_GEMM_TILED;
   c.bm = c.bn = bs;
@@ -584,10 +586,13 @@ int tile_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t*
   g.tiles_n = (int32_t)((N + cfg.bn - 1) / cfg.bn);
   g.SA = SA;
   g.SB = SB;
+  const int af = packed_fmt(a_dtype), bf = packed_fmt(b_dtype);
   const hipError_t e =
-      cfg.direct ? launch_fp4_direct(g, cfg.grid, cfg.bounds != 0, cfg.bm, (hipStream_t)stream)
-                 : launch_gemm_mx_packed(g, cfg.grid, packed_fmt(a_dtype), packed_fmt(b_dtype),
-                                         cfg.bounds != 0, cfg.bm, (hipStream_t)stream);
+      !cfg.direct ? launch_gemm_mx_packed(g, cfg.grid, af, bf, cfg.bounds != 0, cfg.bm,
+                                          (hipStream_t)stream)
+      : af == 4   ? launch_fp4_direct(g, cfg.grid, cfg.bounds != 0, cfg.bm, (hipStream_t)stream)
+                  : launch_fp6_direct(g, cfg.grid, af, bf, cfg.bounds != 0, cfg.bm,
+                                      (hipStream_t)stream);
   if (e != hipSuccess) return fail(TG_E_HIP, std::string("tile_gemm_mx launch: ") + hipGetErrorString(e));
   return TG_OK;
 }

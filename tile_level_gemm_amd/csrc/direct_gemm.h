@@ -16,7 +16,10 @@
 //    (v_mfma_f32_32x32x16_{f16,bf16}), 2 of 64 (v_mfma_f32_32x32x64_f8f6f4, fp8) or 4 of 64
 //    (the same instruction with e2m1 operands, which takes half the fp8 cycles), the same MFMA
 //    cycles per stage in every case.  An e2m1 lane carries 16 bytes (32 K) per step, like a
-//    16-bit lane, so e2m1 stages take the 16-bit fragment reads.
+//    16-bit lane, so e2m1 stages take the 16-bit fragment reads.  A 6-bit operand (e2m3, e3m2)
+//    fills 96 bytes of the row with 128 K: its stages take the fp8 schedule (2 steps of 64 K,
+//    MFMAs at the e2m1 rate), the row's last two chunks are zeros (the lanes that would fetch
+//    them get an out-of-range offset), and a lane's 24 bytes per step are three 8-byte reads.
 //  * K-contiguous operands (A without transA, B with transB) keep [rows][128 bytes] stages
 //    (chunk XOR row bits) and are read as fragments with ds_read_b128: one per 16-bit
 //    fragment, two per fp8 fragment (32 bytes of K per lane).
@@ -55,6 +58,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(8))) uint32_t u32x8;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -70,22 +74,28 @@ constexpr int kGroupM = 8;       // tile-rows per scheduling group (measured: 8 
 // Format codes of the template's DT parameter: TG_F16 / TG_BF16, an fp8 pair kF8 + 2·a + b,
 // or a block-scaled fp8 pair kMX + 2·a + b, with a, b the MFMA's operand format codes
 // (0 = e4m3, 1 = e5m2); kP4: a block-scaled e2m1 pair, both operands K-contiguous packed rows
-// (value k of a row at bits [4k, 4k + 4) of its bytes).
-constexpr int kF8 = 16, kMX = 32, kP4 = 64;
+// (value k of a row at bits [4k, 4k + 4) of its bytes); kP6 + 2·(a − 2) + (b − 2): a block-scaled
+// pair of 6-bit operands (format codes a, b: 2 = e2m3, 3 = e3m2), K-contiguous packed rows
+// (value k at bits [6k, 6k + 6)).
+constexpr int kF8 = 16, kMX = 32, kP4 = 64, kP6 = 96;
+constexpr int p6_code(int a_fmt, int b_fmt) { return kP6 + 2 * (a_fmt - 2) + (b_fmt - 2); }
 constexpr int fp8_code(int a_fmt, int b_fmt) { return kF8 + 2 * a_fmt + b_fmt; }
 constexpr int mx_code(int a_fmt, int b_fmt) { return kMX + 2 * a_fmt + b_fmt; }
 
-// Addressing unit: one element of a 16-bit or fp8 operand, one byte (two values) of e2m1.
+// Addressing unit: one element of a 16-bit or fp8 operand, one byte of a packed operand.
+// kFp8: the two-step (64-K) stage schedule, which 6-bit operands share.
 template <int DT>
 struct Elem {
   static constexpr bool kFp4 = DT == kP4;
+  static constexpr bool kFp6 = DT >= kP6;
   static constexpr bool kFp8 = DT >= kF8 && !kFp4;
   static constexpr bool kScaled = DT >= kMX;      // E8M0 scale per 32 K of each row / column
   static constexpr int kBytes = kFp8 || kFp4 ? 1 : 2;   // bytes per addressing unit
-  static constexpr int kPer = kFp4 ? 2 : 1;        // K values per addressing unit
+  static constexpr int kPer = kFp4 ? 2 : 1;        // K values per addressing unit (not 6-bit)
   static constexpr int kBK = kRowBytes / kBytes;   // addressing units per stage
+  static constexpr int kStageBytes = kFp6 ? 96 : kRowBytes;   // bytes of a K row per stage
   static constexpr int kSteps = kFp8 ? 2 : 4;      // MFMA K steps per stage
-  static constexpr int kParts = kFp8 ? 2 : 1;      // 16-byte K-major reads per fragment
+  static constexpr int kParts = kFp6 ? 3 : kFp8 ? 2 : 1;   // K-major reads per fragment
   using Frag = typename std::conditional<kFp8, u32x8, u32x4>::type;
 };
 
@@ -107,11 +117,16 @@ __device__ __forceinline__ f32x16 mfma32(F a, F b, f32x16 c) {
 // Block-scaled fp8 MFMA: the unit's 32-K block q of the 64-K step is bytes 16q .. 16q+15 of
 // both lane halves (lanes n and n + 32 of row / column n); its scale is the byte OPSEL selects
 // from the scale register of lane n + 32q.
+// A 6-bit pair (DT kP6 + …) takes format codes 2 / 3 and its six low operand registers; lane
+// half h carries block h of the step, whose scale is the lane's own register, so the same
+// byte selection serves it.
 template <int DT, int OPSEL, class F>
 __device__ __forceinline__ f32x16 mfma32s(F a, F b, f32x16 c, uint32_t sa, uint32_t sb) {
+  constexpr int fa = DT >= kP6 ? 2 + ((DT - kP6) >> 1) : (DT & 3) >> 1;
+  constexpr int fb = DT >= kP6 ? 2 + ((DT - kP6) & 1) : DT & 1;
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-      __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, (DT & 3) >> 1, DT & 1,
-      OPSEL, (int)sa, OPSEL, (int)sb);
+      __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, fa, fb, OPSEL, (int)sa,
+      OPSEL, (int)sb);
 }
 
 // Block-scaled e2m1 MFMA (format code 4 for both operands): lane l carries the 32
@@ -231,6 +246,18 @@ __device__ __forceinline__ void km_frag_offsets(int row_base, int lane, uint32_t
     off[u] = r * 128u + ((kc ^ sk<SKV>(r)) << 4);
   }
 }
+// 6-bit K-major fragments of 32-row tile t: lane l reads row base + 32t + l%32, and in K step s
+// the 24 bytes 48s + 24h .. +23 of the row (h = l/32), as three 8-byte reads u = 3s + p at
+// logical byte x = 48s + 24h + 8p: chunk x/16, swizzled, plus x%16.  Tiles are +4096 bytes.
+__device__ __forceinline__ void km6_frag_offsets(int row_base, int lane, uint32_t (&off)[6]) {
+  const uint32_t r = (uint32_t)(row_base + (lane & 31));
+  const uint32_t h = (uint32_t)lane >> 5;
+#pragma unroll
+  for (int u = 0; u < 6; ++u) {
+    const uint32_t x = 48u * (uint32_t)(u / 3) + 24u * h + 8u * (uint32_t)(u % 3);
+    off[u] = r * 128u + (((x >> 4) ^ sk<SKV>(r)) << 4) + (x & 15u);
+  }
+}
 // M/N-major fragment of 32-column tile t, K step s, half h (two ds_read_b64_tr_b16): lane
 // l = 16g + j supplies k-row 16s + 8(g/2) + 4h + j/4 and columns mn_base + 32t + 16(g&1) +
 // 4(j&3) .. +3.  sm(k) depends on j only; its bits 2-3 XOR with the tile index, so one byte
@@ -278,7 +305,7 @@ struct Operand {
   static constexpr int kRowB = BS * EL::kBytes;   // M/N-major: bytes per k-row
   uint32_t dma[2];   // byte offsets of the two DMA parities
   uint32_t kbyte[2]; // K-major: first byte within the K row of each parity's chunk
-  uint32_t frag[4];  // byte offsets: per K-major read slot, or per M/N-major tile
+  uint32_t frag[EL::kFp6 ? 6 : 4];   // byte offsets: per K-major read slot, or per M/N-major tile
 
   // LDS read instructions per fragment and per K step
   static constexpr int kTileReads = MN ? (EL::kFp8 ? 4 : 2) : EL::kParts;
@@ -291,6 +318,10 @@ struct Operand {
     } else if constexpr (MN) {
       mn_dma_offsets<PER, kRowB>(ld, wave, lane, dma);
       mn_frag_offsets<T, kRowB>(base, lane, frag);
+    } else if constexpr (EL::kFp6) {
+      static_assert(!MN, "6-bit operands are K-contiguous");
+      km_dma_offsets<PER, EL::kBytes>(ld, wave, lane, dma, kbyte);
+      km6_frag_offsets(base, lane, frag);
     } else {
       km_dma_offsets<PER, EL::kBytes>(ld, wave, lane, dma, kbyte);
       km_frag_offsets<EL::kFp8>(base, lane, frag);
@@ -314,7 +345,7 @@ struct Operand {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       uint32_t v = dma[i & 1];
-      if constexpr (TAIL && !MN) v = kbyte[i & 1] < lim ? v : 0x80000000u;
+      if constexpr ((TAIL || EL::kFp6) && !MN) v = kbyte[i & 1] < lim ? v : 0x80000000u;
       // K-major: +8 rows per instruction pair; M/N-major: +1024/kRowB k-rows
       const uint32_t step = MN ? (uint32_t)((1024 / kRowB) * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes
                                : (uint32_t)(8 * (i & ~1)) * (uint32_t)ld * (uint32_t)EL::kBytes;
@@ -339,6 +370,9 @@ struct Operand {
         }
         f[t] = out;
       }
+    } else if constexpr (EL::kFp6) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) frag_tile(stage, s, t, f[t]);
     } else if constexpr (EL::kFp8) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
@@ -352,10 +386,19 @@ struct Operand {
     }
   }
   // One fp8 fragment (tile t, K step s): two ds_read_b128 (K-major) or four
-  // ds_read_b64_tr_b8 (M/N-major).
+  // ds_read_b64_tr_b8 (M/N-major); a 6-bit one: three ds_read_b64 (its top two registers 0).
   __device__ __forceinline__ void frag_tile(const uint8_t* stage, int s, int t, Frag& f) const {
-    static_assert(EL::kFp8, "per-tile reads are used for fp8 operands");
-    if constexpr (MN) {
+    static_assert(EL::kFp8, "per-tile reads are used for fp8 and 6-bit operands");
+    if constexpr (EL::kFp6) {
+      u32x8 out = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const u32x2 v = *(const u32x2*)(stage + frag[3 * s + p] + t * 4096);
+        out[2 * p] = v[0];
+        out[2 * p + 1] = v[1];
+      }
+      f = out;
+    } else if constexpr (MN) {
       u32x8 out;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -472,7 +515,7 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   const int wm = (wave / WGN) * WM, wn = (wave % WGN) * WN;
 
   // K in addressing units (bytes of a packed e2m1 row)
-  const int64_t Kx = g.K / EL::kPer;
+  const int64_t Kx = EL::kFp6 ? (int64_t)g.K / 4 * 3 : (int64_t)g.K / EL::kPer;
   const int64_t lda = A_MN ? g.M : Kx;
   const int64_t ldb = B_MN ? g.N : Kx;
   using OA = Operand<A_MN, TM, PER, DT, BS>;
@@ -486,8 +529,8 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   const int64_t b0 = B_MN ? (int64_t)n0 : (int64_t)n0 * Kx;
   oa.bind((const uint8_t*)g.A + a0 * E, ((int64_t)g.M * Kx - a0) * E);
   ob.bind((const uint8_t*)g.B + b0 * E, (Kx * g.N - b0) * E);
-  const uint32_t adv_a = A_MN ? (uint32_t)(BK * g.M * E) : (uint32_t)(BK * E);
-  const uint32_t adv_b = B_MN ? (uint32_t)(BK * g.N * E) : (uint32_t)(BK * E);
+  const uint32_t adv_a = A_MN ? (uint32_t)(BK * g.M * E) : (uint32_t)EL::kStageBytes;
+  const uint32_t adv_b = B_MN ? (uint32_t)(BK * g.N * E) : (uint32_t)EL::kStageBytes;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -511,10 +554,14 @@ __device__ __forceinline__ void direct_body(const GemmArgs& g) {
   //   then step NS-1's MFMAs (operands already in registers) overlap the reads of stage
   //   kt+1's first fragments and the DMA of stage kt+2 into `cur`.
   // The last two stages are peeled off the loop so the steady-state body is branch free.
-  const int KT = TAIL ? (int)((Kx + BK - 1) / BK) : (int)(Kx / BK);   // >= 1, of shape KSH
+  const int KT = TAIL ? (int)((Kx + BK - 1) / BK)
+                      : (int)(EL::kFp6 ? g.K / 128 : Kx / BK);   // >= 1, of shape KSH
   // valid bytes of each K row in stage s: all 128 but in a partial last stage
   const uint32_t krem = (uint32_t)(Kx - (int64_t)(KT - 1) * BK) * E;
-  auto lim = [&](int s) -> uint32_t { return s == KT - 1 ? krem : (uint32_t)kRowBytes; };
+  auto lim = [&](int s) -> uint32_t {
+    if constexpr (EL::kFp6) return (uint32_t)EL::kStageBytes;   // chunks 6, 7 of every row: zeros
+    return s == KT - 1 ? krem : (uint32_t)kRowBytes;
+  };
   auto load_ab = [&](uint32_t s, uint8_t* stage_a, uint8_t* stage_b) {
     oa.template load<TAIL>(s * adv_a, lda, stage_a, wave, lim((int)s));
     ob.template load<TAIL>(s * adv_b, ldb, stage_b, wave, lim((int)s));

@@ -42,9 +42,9 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 constexpr int kBK = 128;
 constexpr int kGroupM = 8;   // tile-rows per scheduling group
 
-// Per operand format code (2 = e2m3, 3 = e3m2, 4 = e2m1) and block size: bits per value, bytes
-// of one row per stage, padded LDS pitch, 16-byte chunks per row, chunks per thread (the block
-// has 2·BS threads... BS = 128: 256 threads, BS = 256: 512).
+// Per operand format code (2 = e2m3, 3 = e3m2, 4 = e2m1) and block size BS: bits per value,
+// bytes of one row per stage, padded LDS pitch, 16-byte chunks per row, and chunks per thread
+// (256 threads on 128-wide blocks, 512 on 256-wide ones).
 template <int F, int BS>
 struct Pk {
   static constexpr int kThreads = BS == 256 ? 512 : 256;

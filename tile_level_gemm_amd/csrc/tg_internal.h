@@ -124,6 +124,10 @@ int packed_lds_bytes(int a_fmt, int b_fmt, int bs);
 // Block-scaled e2m1 x e2m1 GEMM on the direct-load kernel (A [M][K/2], B [N][K/2] packed rows,
 // K % 256 == 0), bs x bs blocks (256 or 128) of 512 threads; grid = ceil(M/bs)·ceil(N/bs).
 hipError_t launch_fp4_direct(const GemmArgs& g, int64_t grid, bool bounds, int bs, hipStream_t s);
+// Block-scaled 6-bit GEMM on the direct-load kernel (A [M][3K/4], B [N][3K/4] packed rows, K % 128
+// == 0; af, bf: 2 = e2m3, 3 = e3m2), bs x bs blocks (256 or 128) of 512 threads.
+hipError_t launch_fp6_direct(const GemmArgs& g, int64_t grid, int af, int bf, bool bounds, int bs,
+                             hipStream_t s);
 
 // 16-bit direct-load GEMM on bs x bs blocks (256 or 128).
 hipError_t launch_gemm_direct(const GemmArgs& g, int64_t grid, int trans_a, int trans_b, int dtype,
