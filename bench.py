@@ -56,6 +56,7 @@ KERNEL_SOURCES = {
     "copy": ("copy_kernels.hip", "lds_layout.h", "tg_internal.h"),
     "packed": ("gemm_mx_packed.hip", "tg_internal.h"),
     "fp4": ("gemm_mx_fp4.hip", "direct_gemm.h", "tg_internal.h"),
+    "fp6": ("gemm_mx_fp6.hip", "direct_gemm.h", "tg_internal.h"),
     "frag": ("frag_kernels.hip", "tg_internal.h"),
     "async": ("async_copy.hip", "lds_layout.h", "tg_internal.h"),
 }
@@ -97,8 +98,10 @@ TRAFFIC_KERNELS = {
                                 2 * M * K + 2 * M * (K // 32) + M * N * 4),
     "gemm_mx_256x256_e2m1_tn": ("gemm_direct<false, false, 64, 2, 4, false, 0>", "fp4",
                                 2 * M * K // 2 + 2 * M * (K // 32) + M * N * 4),
-    "gemm_mx_packed_256x256_e2m3": ("gemm_mx_packed<2, 2, false, 256>", "packed",
-                                    2 * M * K * 6 // 8 + 2 * M * (K // 32) + M * N * 4),
+    "gemm_mx_256x256_e2m3_tn": ("gemm_direct<false, false, 96, 2, 4, false, 0>", "fp6",
+                                2 * M * K * 6 // 8 + 2 * M * (K // 32) + M * N * 4),
+    "gemm_mx_256x256_e2m1xe2m3_tn": ("gemm_mx_packed<4, 2, false, 256>", "packed",
+                                     M * K // 2 + M * K * 6 // 8 + 2 * M * (K // 32) + M * N * 4),
     "tile_copy_16384x16384_f16": ("tile_copy_rows<16, 4, 4, 128>", "copy", 2 * ROWS * COLS * 2),
     "frag_load_a16_32x32x16_col_16384x16384": ("frag_lds<1, false, true>", "frag",
                                                2 * ROWS * COLS * 2),
@@ -297,8 +300,11 @@ def main():
     g = synth.rng(64)
     sa = g.integers(117, 138, size=(M, K // 32)).astype(np.uint8)
     sb = g.integers(117, 138, size=(N, K // 32)).astype(np.uint8)
-    small_in = {f: synth.gemm_mx_small_inputs(M, N, K, f, f, 0.0, seeds, dist="normal")
-                for f, seeds in (("e2m1", (65, 66, 67)), ("e2m3", (68, 69, 70)))}
+    # 6- and 4-bit legs: e2m1 and e2m3 pairs (direct-load kernel), e2m1 x e2m3 (packed kernel)
+    small_pairs = {"e2m1": ("e2m1", "e2m1", (65, 66, 67)), "e2m3": ("e2m3", "e2m3", (68, 69, 70)),
+                   "e2m1xe2m3": ("e2m1", "e2m3", (71, 72, 73))}
+    small_in = {f: synth.gemm_mx_small_inputs(M, N, K, af, bf, 0.0, seeds, dist="normal")
+                for f, (af, bf, seeds) in small_pairs.items()}
     cr, cc = ROWS // 2, COLS
     acc_bits = synth.uniform(43, cr * cc).view(np.uint32)
     other_in = {}
@@ -410,8 +416,8 @@ def main():
     for f, (pa_, pb_, _, _, sa_, sb_, _) in small_in.items():
         Ap, Bp, SAp, SBp = up8(pa_), up8(pb_), up8(sa_), up8(sb_)
         Dp = torch.empty((M, N), dtype=torch.float32, device=dev)
-        code = small_code[f]
-        lst = per_launch(lambda: tg.tile_gemm_mx(Ap, Bp, SAp, SBp, None, Dp, M, N, K, 0, 1, 0.0, code, code))
+        ca_, cb_ = small_code[small_pairs[f][0]], small_code[small_pairs[f][1]]
+        lst = per_launch(lambda: tg.tile_gemm_mx(Ap, Bp, SAp, SBp, None, Dp, M, N, K, 0, 1, 0.0, ca_, cb_))
         small_run[f] = (lst, Dp)
         del Ap, Bp, SAp, SBp
 
@@ -581,18 +587,19 @@ def main():
     small_legs = {}
     for f, (lst, Dp) in small_run.items():
         pa_, pb_, _, _, sa_, sb_, _ = small_in[f]
-        refp, boundp = og.gemm_mx_ref_at(pa_, pb_, sa_, sb_, None, M, N, K, False, True, 0.0, f, f,
+        af_, bf_ = small_pairs[f][0], small_pairs[f][1]
+        refp, boundp = og.gemm_mx_ref_at(pa_, pb_, sa_, sb_, None, M, N, K, False, True, 0.0, af_, bf_,
                                          rows, cols)
         gotp = Dp.cpu().numpy()[rows, cols]
-        p_ok, p_worst = og.check_fp8(gotp, refp, boundp, pa_, pb_, M, N, K, False, True, f, f, rows, cols,
-                                     sa_bits=sa_, sb_bits=sb_)
+        p_ok, p_worst = og.check_fp8(gotp, refp, boundp, pa_, pb_, M, N, K, False, True, af_, bf_,
+                                     rows, cols, sa_bits=sa_, sb_bits=sb_)
         small_legs[f"gemm_mx_{f}_tn"] = mfma_leg(
-            lst, PEAK_FP4_TFLOPS,
-            "gemm_mx_256x256_e2m1_tn" if f == "e2m1" else f"gemm_mx_packed_256x256_{f}",
+            lst, PEAK_FP4_TFLOPS, f"gemm_mx_256x256_{f}_tn",
             {"sampled_ok": bool(p_ok), "worst_err_over_tol": round(p_worst, 5),
              "worst_err_over_16bit_tol": round(og.check(gotp, refp, boundp)[1], 5)},
-            f"tile_gemm_mx 8192x8192x8192, A {f} [M,K] and B {f} [N,K] packed rows, N(0,1) rounded "
-            f"to {f}, E8M0 scales per 32 K in 2^-10..2^10, fp32 D, beta=0")
+            f"tile_gemm_mx 8192x8192x8192, A {af_} [M,K] and B {bf_} [N,K] packed rows, N(0,1) rounded "
+            f"to the format, E8M0 scales per 32 K in 2^-10..2^10, fp32 D, beta=0"
+            + (" (packed kernel)" if af_ != bf_ else " (direct-load kernel)"))
     gi = synth.rng(79)
     fl_ok = True
     imgv = img.view(-1, 64, 8)

@@ -19,7 +19,8 @@ Workloads (seeds are part of the recipe):
   gemm8kf8 A e4m3 [8192,8192] N(0,1) (61), B e4m3 stored [N,K] N(0,1) (62), transB,
            beta=0, sample seed 63
   gemm8kf4 A e2m1 [8192,8192] N(0,1) (65), B e2m1 stored [N,K] N(0,1) (66), packed rows,
-           E8M0 scales 2^-10..2^10 (67), beta=0 (the e2m3 and e3m2 variants: seeds 68-70)
+           E8M0 scales 2^-10..2^10 (67), beta=0 (the e2m3 pair: seeds 68-70; A e2m1 with
+           B e2m3: 71-73)
 
 6- and 4-bit operands (e2m3, e3m2, e2m1) are stored K-contiguous as packed rows: code k of a
 row at bits [w·k, w·k + w) of the row's little-endian bit stream (w = 6 or 4).
