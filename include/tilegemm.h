@@ -235,9 +235,11 @@ int tile_gemm_fp8_plan(const void* A, const void* B, const float* C, const float
  *   operand's bits — with code k of a row at bits [w·k, w·k + w) of that row's little-endian bit
  *   stream (fp4: two codes per byte, the even one in the low nibble; fp6: four codes in every
  *   three bytes).  Any other orientation is TG_E_LAYOUT.  Shapes, scales, C, D, beta and
- *   alignment as above; each packed operand under 2 GiB.  e2m1 x e2m1 with K % 256 == 0 runs
- *   the direct-load kernel (256 K per 128-byte stage row; tile_gemm_mx_plan reports loader 1
- *   and block_k 256); every other packed pair and shape runs the packed kernel (128-K stages).
+ *   alignment as above; each packed operand under 2 GiB.  The direct-load kernel
+ *   (tile_gemm_mx_plan reports loader 1) runs e2m1 x e2m1 with K % 256 == 0 (block_k 256: 256 K
+ *   per 128-byte stage row) and every pair of 6-bit operands (block_k 128: 96 bytes of each
+ *   128-byte stage row); an e2m1 operand with a 6-bit one, or e2m1 x e2m1 with K % 256 != 0,
+ *   runs the packed kernel (loader 0, 128-K stages).
  * Returns TG_OK or a tg_status; asynchronous on `stream`.
  */
 int tile_gemm_mx(const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
