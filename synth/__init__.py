@@ -230,6 +230,12 @@ def pack_rows(codes, width):
     return np.packbits(bits.reshape(rows, K * width), axis=1, bitorder="little")
 
 
+def packed_random(nbytes, seed):
+    """nbytes uniformly random bytes: packed 6- or 4-bit rows in which every code is equally
+    likely (no code of these formats is a NaN or an infinity)."""
+    return rng(seed).integers(0, 256, size=nbytes, dtype=np.uint8)
+
+
 def gemm_mx_small_inputs(M, N, K, a_fmt, b_fmt, beta, seeds, dist="codes", scale_range=(117, 138)):
     """Packed A [M, K·wa/8], packed B [N, K·wb/8] (both K-contiguous), their codes, E8M0
     scales SA [M, K/32], SB [N, K/32] and C (float32 U[-1, 1]) or None.

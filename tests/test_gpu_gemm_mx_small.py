@@ -147,6 +147,36 @@ def test_sampled_8192(af, seed):
     assert guards and ok, worst
 
 
+# A packed operand just under 2 GiB on each direct-load path (ragged M, every code equally
+# likely, scales over 2^-10 .. 2^10), checked on 4096 sampled outputs
+@pytest.mark.parametrize("M,af,bf,beta", [(524272, "e2m1", "e2m1", 0.0), (349520, "e2m3", "e3m2", 1.0)])
+def test_direct_operand_just_under_2gib_sampled(M, af, bf, beta):
+    N, K = 256, 8192
+    wa, wb = synth.SMALL_W[af], synth.SMALL_W[bf]
+    abytes = M * K * wa // 8
+    assert abytes < 1 << 31 and abytes > (1 << 31) - (1 << 20)
+    pa, pb = synth.packed_random(abytes, 81), synth.packed_random(N * K * wb // 8, 82)
+    g = synth.rng(83)
+    sa = g.integers(117, 138, size=(M, K // 32)).astype(np.uint8)
+    sb = g.integers(117, 138, size=(N, K // 32)).astype(np.uint8)
+    c = synth.uniform(84, M * N).reshape(M, N) if beta else None
+    say(f"gemm_mx {af} x {bf} {M}x{N}x{K}: A of {abytes} bytes (direct-load kernel)")
+    A, B, SA, SB = up8(pa), up8(pb), up8(sa), up8(sb)
+    D = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    Cd = upload_f32(c) if beta else None
+    p = tg.tile_gemm_mx_plan(A, B, SA, SB, Cd, D, M, N, K, 0, 1, beta, FMT[af], FMT[bf])
+    assert p.loader == 1 and p.bounds_checked == 1
+    tg.tile_gemm_mx(A, B, SA, SB, Cd, D, M, N, K, 0, 1, beta, FMT[af], FMT[bf])
+    torch.cuda.synchronize()
+    rows, cols = synth.sample_points(M, N, 85, count=4096, tile=(256, 256))
+    rows[:8] = M - 1 - np.arange(8)   # the last rows: the far end of A
+    ref, bound = og.gemm_mx_ref_at(pa, pb, sa, sb, c, M, N, K, False, True, beta, af, bf, rows, cols)
+    got = D.cpu().numpy()[rows, cols]
+    ok, worst = og.check_fp8(got, ref, bound, pa, pb, M, N, K, False, True, af, bf, rows, cols,
+                             sa_bits=sa, sb_bits=sb)
+    assert ok, worst
+
+
 def test_one_hot_block_scales_reach_their_block():
     # A = 1.0 everywhere, B one-hot per column in one block, scales 2^(n mod 7) on that block of B:
     # each output is exactly the chosen B scale times the A scale of the block
