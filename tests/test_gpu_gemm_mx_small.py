@@ -177,6 +177,22 @@ def test_direct_operand_just_under_2gib_sampled(M, af, bf, beta):
     assert ok, worst
 
 
+@pytest.mark.parametrize("af,bf", [("e2m1", "e2m1"), ("e2m3", "e3m2"), ("e2m1", "e2m3")])
+def test_empty_and_k_zero(af, bf):
+    # M or N = 0: nothing is read or written; K = 0: D = beta·C (beta 1) or 0 (beta 0)
+    say(f"gemm_mx {af} x {bf}: M = 0, N = 0, K = 0")
+    tg.tile_gemm_mx(None, None, None, None, None, None, 0, 64, 128, 0, 1, 0.0, FMT[af], FMT[bf])
+    tg.tile_gemm_mx(None, None, None, None, None, None, 64, 0, 128, 0, 1, 1.0, FMT[af], FMT[bf])
+    c = synth.uniform(6, 48 * 32).reshape(48, 32)
+    for beta in (1.0, 0.0):
+        D = Guarded(48 * 32 * 4, fill=np.full((48, 32), np.nan, np.float32))
+        tg.tile_gemm_mx(None, None, None, None, upload_f32(c) if beta else None, D.ptr, 48, 32, 0, 0, 1,
+                        beta, FMT[af], FMT[bf])
+        torch.cuda.synchronize()
+        want = c if beta else np.zeros((48, 32), np.float32)
+        assert np.array_equal(D.host(np.float32).reshape(48, 32), want) and D.guards_intact()
+
+
 def test_one_hot_block_scales_reach_their_block():
     # A = 1.0 everywhere, B one-hot per column in one block, scales 2^(n mod 7) on that block of B:
     # each output is exactly the chosen B scale times the A scale of the block
