@@ -356,6 +356,26 @@ def main():
         torch.cuda.synchronize()
         return [ev[0].elapsed_time(ev[1]) / per_group for ev in evs]
 
+    def graphed(call, n=100, groups=5):
+        """Per-launch ms inside a HIP graph of `n` launches (captured on a side stream), replayed
+        `groups` times between events: the kernels without the per-call host cost."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(n):
+                    call()
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(groups)]
+        for ev in evs:
+            ev[0].record()
+            graph.replay()
+            ev[1].record()
+        torch.cuda.synchronize()
+        return [ev[0].elapsed_time(ev[1]) / n for ev in evs]
+
     # ---- 2. the other legs, back to back on the GPU, each into buffers of its own ------------
     t_gpu = time.perf_counter()
     print("bench: small configurations", file=sys.stderr, flush=True)
@@ -364,35 +384,44 @@ def main():
         Aa, Ba = up(a), up(b)
         Ca = torch.from_numpy(c).to(dev) if beta else None
         Da = torch.empty((16, 8), dtype=torch.float32, device=dev)
-        ms = batched(lambda: tg.tile_gemm(Aa, Ba, Ca, Da, 16, 8, 16, 0, 0, beta, tg.TG_F16),
-                     per_group=200)
+        atom = lambda: tg.tile_gemm(Aa, Ba, Ca, Da, 16, 8, 16, 0, 0, beta, tg.TG_F16)  # noqa: E731
+        ms = batched(atom, per_group=200)
+        gms = graphed(atom)
         small[f"atom_16x8x16_f16_beta{int(beta)}"] = {"us": round(float(np.median(ms)) * 1e3, 3),
-                                                        **_stats(ms)}
+                                                        **_stats(ms),
+                                                        "graph_us": round(float(np.median(gms)) * 1e3, 3)}
         small_out[beta] = Da
     s32 = torch.from_numpy(src32.view(np.int32)).to(dev)
     d32 = torch.empty_like(s32)
     o32 = dict(tile_rows=32, tile_cols=32, threads=64, lds_kind=tg.TG_ROW_MAJOR)
-    ms = batched(lambda: tg.tile_copy_ex(s32, d32, (32, 32), tg.TG_F32, None, None, o32), per_group=200)
-    small["copy_32x32_f32_wave64"] = {"us": round(float(np.median(ms)) * 1e3, 3), **_stats(ms)}
+    c32 = lambda: tg.tile_copy_ex(s32, d32, (32, 32), tg.TG_F32, None, None, o32)  # noqa: E731
+    ms, gms = batched(c32, per_group=200), graphed(c32)
+    small["copy_32x32_f32_wave64"] = {"us": round(float(np.median(ms)) * 1e3, 3), **_stats(ms),
+                                      "graph_us": round(float(np.median(gms)) * 1e3, 3)}
     s128 = up(src128)
     d128 = torch.empty_like(s128)
     x128 = torch.empty_like(s128)
     o128 = dict(tile_rows=128, tile_cols=64, threads=256, lds_kind=tg.TG_XOR_SWIZZLE)
-    ms = batched(lambda: tg.tile_copy_ex(s128, d128, (128, 64), tg.TG_F16, None, None, o128), per_group=200)
-    small["copy_128x64_f16_xor_256t"] = {"us": round(float(np.median(ms)) * 1e3, 3), **_stats(ms)}
+    c128 = lambda: tg.tile_copy_ex(s128, d128, (128, 64), tg.TG_F16, None, None, o128)  # noqa: E731
+    ms, gms = batched(c128, per_group=200), graphed(c128)
+    small["copy_128x64_f16_xor_256t"] = {"us": round(float(np.median(ms)) * 1e3, 3), **_stats(ms),
+                                         "graph_us": round(float(np.median(gms)) * 1e3, 3)}
     # the LDS image of the tile (a global destination in the XOR layout), checked later
     tg.tile_copy_ex(s128, x128, (128, 64), tg.TG_F16, None, (tg.TG_XOR_SWIZZLE, 0), o128)
     A3, B3, C3 = up(c3[0]), up(c3[1]), torch.from_numpy(c3[2]).to(dev)
     D3 = torch.empty((512, 512), dtype=torch.float32, device=dev)
-    ms = batched(lambda: tg.tile_gemm(A3, B3, C3, D3, 512, 512, 256, 0, 1, 1.0, tg.TG_BF16), per_group=100)
+    g3 = lambda: tg.tile_gemm(A3, B3, C3, D3, 512, 512, 256, 0, 1, 1.0, tg.TG_BF16)  # noqa: E731
+    ms, gms = batched(g3, per_group=100), graphed(g3)
     t3 = float(np.median(ms)) * 1e-3
+    tg3 = float(np.median(gms)) * 1e-3
     fl3, by3 = 2.0 * 512 * 512 * 256, 2 * 512 * 256 * 2 + 2 * 512 * 512 * 4
     t_roof = max(fl3 / (PEAK_MFMA_TFLOPS * 1e12), by3 / (PEAK_HBM_GBS * 1e9))
     small["gemm_512x512x256_bf16_transB_beta1"] = {
         "us": round(t3 * 1e6, 3), **_stats(ms), "TFLOP/s": round(fl3 / t3 / 1e12, 3),
+        "graph_us": round(tg3 * 1e6, 3), "graph_TFLOP/s": round(fl3 / tg3 / 1e12, 3),
         "roofline": {"bound": "hbm (the larger of the MFMA and HBM times)",
                      "time_at_roofline_us": round(t_roof * 1e6, 4), "frac": round(t_roof / t3, 4),
-                     "compulsory_bytes": by3}}
+                     "graph_frac": round(t_roof / tg3, 4), "compulsory_bytes": by3}}
 
     print("bench: fp16 transA beta=1 gemm", file=sys.stderr, flush=True)
     Ah, Bh = up(hin[0]), up(hin[1])
