@@ -18,9 +18,13 @@ The oracle is written from these pages (cited by title and section):
              矩阵描述符与调度算法" (pnsm.cn/news/1939927).
 
 Modules:
-  numerics  exact decoding of fp16 / bf16 / fp8 (e4m3, e5m2) / e8m0 bit patterns to float64
-  gemm      D = A·B (+C) in float64 (16-bit operands, and the fp8 operands of the
-            asynchronous GEMM's precision family), the acceptance tables, the error bound
+  numerics  exact decoding of fp16 / bf16 / fp8 (e4m3, e5m2) / e8m0 bit patterns, and of the
+            6- and 4-bit element types (e2m3, e3m2, e2m1) and their packed rows, to float64
+  gemm      D = A·B (+C) in float64 (16-bit operands, the fp8 operands of the asynchronous
+            GEMM's precision family, block-scaled fp8 and 6/4-bit operands), the acceptance
+            tables, the error bound and the fp8 comparison bar
+  fragment  the matrix instructions' register maps, register images, the register-level
+            product over them, and the atom selection rules
   layout    logical (row, col) -> element offset for row-major, column-major and
             the XOR-swizzled tile layout
   copy      element-by-element copy between two layouts (bit patterns)
@@ -31,4 +35,4 @@ Every function that has no pin of its own says "parity unpinned" in its
 docstring; at present every function is pinned by tests/test_oracle_*.py.
 """
 
-from . import numerics, gemm, layout, copy, planner  # noqa: F401
+from . import numerics, gemm, layout, copy, planner, fragment  # noqa: F401
