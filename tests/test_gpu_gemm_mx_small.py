@@ -109,6 +109,18 @@ def test_fp4_direct_in_place_and_codes():
     full_check(512, 768, 1536, "e2m1", "e2m1", 1.0, 53, c_is_d=True)
 
 
+# the packed kernel's pairs (an e2m1 operand with a 6-bit one; e2m1 x e2m1 with K % 256 != 0):
+# 128- and 256-wide blocks, whole and ragged, one to many 128-K stages, beta 0 and 1
+@pytest.mark.parametrize("M,N,K,af,bf,beta", [(16, 48, 128, "e2m1", "e3m2", 1.0),
+                                              (400, 272, 640, "e2m3", "e2m1", 0.0),
+                                              (1024, 1040, 1152, "e2m1", "e2m3", 1.0),
+                                              (4112, 4096, 384, "e3m2", "e2m1", 0.0),
+                                              (4096, 4352, 640, "e2m1", "e2m1", 1.0)])
+def test_packed_kernel_pairs(M, N, K, af, bf, beta):
+    say(f"gemm_mx packed kernel {M}x{N}x{K} {af} x {bf} beta={beta}")
+    full_check(M, N, K, af, bf, beta, M + N + K + 2, dist="normal", scale_range=(100, 154))
+
+
 @pytest.mark.parametrize("af", ["e2m1", "e2m3"])
 def test_normal_data_and_wide_scales(af):
     # N(0,1) rounded to the format, scales over 2^-60 .. 2^60
