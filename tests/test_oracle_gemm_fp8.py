@@ -204,8 +204,8 @@ def _fp8_codes_in(fmt, lo, hi):
 def test_fp8_bar_is_the_16bit_bar_within_six_binades(fa, fb):
     # An fp8 product carries at most 8 significant bits, so a product within 2^6 of its group's
     # largest lies on the group's 2^-13 grid: the allowance is exactly zero and the fp8 bar is
-    # the benchmark spec's 16-bit bar.  Operands drawn from [1, 2) and [2^-2, 2^1) keep every product in
-    # [2^-2, 2^2), inside six binades of any group maximum.
+    # the 16-bit bar (1e-4·sum|a·b| + 1e-6).  Operands drawn from [1, 2) and [2^-2, 2^1) keep
+    # every product in [2^-2, 2^2), inside six binades of any group maximum.
     rs = np.random.default_rng(8)
     M, N, K = 32, 48, 256
     ca, cb = _fp8_codes_in(fa, 1.0, 2.0), _fp8_codes_in(fb, 0.25, 2.0)

@@ -1,6 +1,6 @@
 """Build libtilegemm.so in-tree with hipcc for gfx950.
 
-    python -m tile_level_gemm_amd.build        # or __graft_entry__.build()
+    python -m tile_level_gemm_amd.build
 
 Objects go to tile_level_gemm_amd/_build/ (git-ignored); the library lands next to
 this file so that it travels with the source tree.
