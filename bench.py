@@ -264,7 +264,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the tile GEMM and tile copy "
-              "run on a single MI355X and this build has no multi-GPU path.", file=sys.stderr)
+              "run on a single MI355X and this library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
