@@ -5,15 +5,21 @@ synchronises, so a caller may run it on any stream or record it into a graph.  T
 check that results are the same bits on a side stream, and that a captured graph recomputes
 from the current contents of its inputs on every replay, with eager work in between."""
 
+import numpy as np
 import pytest
 import torch
 
+import synth
 import tile_level_gemm_amd as tg
 from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+
+
+def _up8(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(DEV)
 
 
 def _gemm_inputs(M, N, K, dtype, seed):
@@ -96,3 +102,51 @@ def test_graph_replays_recompute():
         assert torch.equal(D, want_alt if alt else want_d), rep
         assert torch.equal(D8, want_d8), rep
         assert torch.equal(dst, src), rep
+
+
+def test_graph_replays_block_scaled_and_atom_paths():
+    # one captured graph over the 6/4-bit kernels (e2m1 and 6-bit pairs on the direct-load
+    # kernel, an e2m1 x e2m3 pair on the packed kernel) and the register atom kernel; every
+    # replay, with eager work between them, must give the eager results
+    say("streams: graph of block-scaled e2m1 / e2m3 / mixed gemms + a 16x8x16 atom, replayed 3 times")
+    M, N, K = 512, 384, 1024
+    runs = []
+    for (af, bf, code_a, code_b, seed) in (("e2m1", "e2m1", tg.TG_FP4_E2M1, tg.TG_FP4_E2M1, 91),
+                                           ("e2m3", "e3m2", tg.TG_FP6_E2M3, tg.TG_FP6_E3M2, 94),
+                                           ("e2m1", "e2m3", tg.TG_FP4_E2M1, tg.TG_FP6_E2M3, 97)):
+        pa, pb, _, _, sa, sb, _ = synth.gemm_mx_small_inputs(M, N, K, af, bf, 0.0,
+                                                             (seed, seed + 1, seed + 2), dist="normal")
+        runs.append((_up8(pa), _up8(pb), _up8(sa), _up8(sb), torch.empty(M, N, device=DEV), code_a,
+                     code_b))
+    Aa = torch.randn(16, 16, device=DEV).to(torch.float16)
+    Ba = torch.randn(16, 8, device=DEV).to(torch.float16)
+    Da = torch.empty(16, 8, device=DEV)
+
+    def work():
+        for A, B, SA, SB, D, ca, cb in runs:
+            tg.tile_gemm_mx(A, B, SA, SB, None, D, M, N, K, 0, 1, 0.0, ca, cb)
+        tg.tile_gemm(Aa, Ba, None, Da, 16, 8, 16, 0, 0, 0.0, tg.TG_F16)
+
+    work()
+    torch.cuda.synchronize()
+    want = [r[4].clone() for r in runs] + [Da.clone()]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        for r in runs:
+            r[4].fill_(float("nan"))
+        Da.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [r[4] for r in runs] + [Da]
+        for g_, w_ in zip(got, want):
+            assert torch.equal(g_, w_), rep
