@@ -358,7 +358,16 @@ def main():
 
     def graphed(call, n=100, groups=5):
         """Per-launch ms inside a HIP graph of `n` launches (captured on a side stream), replayed
-        `groups` times between events: the kernels without the per-call host cost."""
+        `groups` times between events: the kernels without the per-call host cost.  None when
+        the capture fails (the figure is then reported as null; nothing else depends on it)."""
+        try:
+            return _graphed(call, n, groups)
+        except RuntimeError as e:
+            print(f"bench: graph timing skipped ({e})", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+            return None
+
+    def _graphed(call, n, groups):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         graph = torch.cuda.CUDAGraph()
@@ -376,6 +385,9 @@ def main():
         torch.cuda.synchronize()
         return [ev[0].elapsed_time(ev[1]) / n for ev in evs]
 
+    def _gus(gms):
+        return round(float(np.median(gms)) * 1e3, 3) if gms else None
+
     # ---- 2. the other legs, back to back on the GPU, each into buffers of its own ------------
     t_gpu = time.perf_counter()
     print("bench: small configurations", file=sys.stderr, flush=True)
@@ -389,7 +401,7 @@ def main():
         gms = graphed(atom)
         small[f"atom_16x8x16_f16_beta{int(beta)}"] = {"us": round(float(np.median(ms)) * 1e3, 3),
                                                         **_stats(ms),
-                                                        "graph_us": round(float(np.median(gms)) * 1e3, 3)}
+                                                        "graph_us": _gus(gms)}
         small_out[beta] = Da
     s32 = torch.from_numpy(src32.view(np.int32)).to(dev)
     d32 = torch.empty_like(s32)
@@ -397,7 +409,7 @@ def main():
     c32 = lambda: tg.tile_copy_ex(s32, d32, (32, 32), tg.TG_F32, None, None, o32)  # noqa: E731
     ms, gms = batched(c32, per_group=200), graphed(c32)
     small["copy_32x32_f32_wave64"] = {"us": round(float(np.median(ms)) * 1e3, 3), **_stats(ms),
-                                      "graph_us": round(float(np.median(gms)) * 1e3, 3)}
+                                      "graph_us": _gus(gms)}
     s128 = up(src128)
     d128 = torch.empty_like(s128)
     x128 = torch.empty_like(s128)
@@ -405,7 +417,7 @@ def main():
     c128 = lambda: tg.tile_copy_ex(s128, d128, (128, 64), tg.TG_F16, None, None, o128)  # noqa: E731
     ms, gms = batched(c128, per_group=200), graphed(c128)
     small["copy_128x64_f16_xor_256t"] = {"us": round(float(np.median(ms)) * 1e3, 3), **_stats(ms),
-                                         "graph_us": round(float(np.median(gms)) * 1e3, 3)}
+                                         "graph_us": _gus(gms)}
     # the LDS image of the tile (a global destination in the XOR layout), checked later
     tg.tile_copy_ex(s128, x128, (128, 64), tg.TG_F16, None, (tg.TG_XOR_SWIZZLE, 0), o128)
     A3, B3, C3 = up(c3[0]), up(c3[1]), torch.from_numpy(c3[2]).to(dev)
@@ -413,15 +425,16 @@ def main():
     g3 = lambda: tg.tile_gemm(A3, B3, C3, D3, 512, 512, 256, 0, 1, 1.0, tg.TG_BF16)  # noqa: E731
     ms, gms = batched(g3, per_group=100), graphed(g3)
     t3 = float(np.median(ms)) * 1e-3
-    tg3 = float(np.median(gms)) * 1e-3
+    tg3 = float(np.median(gms)) * 1e-3 if gms else None
     fl3, by3 = 2.0 * 512 * 512 * 256, 2 * 512 * 256 * 2 + 2 * 512 * 512 * 4
     t_roof = max(fl3 / (PEAK_MFMA_TFLOPS * 1e12), by3 / (PEAK_HBM_GBS * 1e9))
     small["gemm_512x512x256_bf16_transB_beta1"] = {
         "us": round(t3 * 1e6, 3), **_stats(ms), "TFLOP/s": round(fl3 / t3 / 1e12, 3),
-        "graph_us": round(tg3 * 1e6, 3), "graph_TFLOP/s": round(fl3 / tg3 / 1e12, 3),
+        "graph_us": round(tg3 * 1e6, 3) if tg3 else None,
+        "graph_TFLOP/s": round(fl3 / tg3 / 1e12, 3) if tg3 else None,
         "roofline": {"bound": "hbm (the larger of the MFMA and HBM times)",
                      "time_at_roofline_us": round(t_roof * 1e6, 4), "frac": round(t_roof / t3, 4),
-                     "graph_frac": round(t_roof / tg3, 4), "compulsory_bytes": by3}}
+                     "graph_frac": round(t_roof / tg3, 4) if tg3 else None, "compulsory_bytes": by3}}
 
     print("bench: fp16 transA beta=1 gemm", file=sys.stderr, flush=True)
     Ah, Bh = up(hin[0]), up(hin[1])
